@@ -1,0 +1,262 @@
+"""Seeded synthetic decode-attention workloads.
+
+This module only draws inputs: random queries, a paged KV cache stored as raw
+bf16 / e4m3 codes, block tables and sequence lengths.  It holds none of the
+attention arithmetic (no dequantisation, no softmax, no split planning), so
+both the HIP path and the fp64 oracle can consume the same arrays without
+sharing any of the method's code.
+
+The shapes follow the workloads the split-KV pages discuss:
+
+* few KV heads with a long KV history in single-token decode ("vLLM 0.30.0
+  FA4 SplitKV Bug: H100 Decode Can Be 48% Slower", sections "What SplitKV is
+  trying to do" and "Gemma 4 exposes the failure clearly");
+* MLA decode of one request at six speculative tokens ("Shipped: 484.5 tok/s
+  on one GB300 ...", table "What shipped");
+* bf16 queries over an FP8 KV cache in a paged, HND-layout cache ("Xqa
+  decode kernels", sections "Purpose" and "Test Plan").
+
+Cache layout (logical, "HND"): ``cache[page][kv_head][slot][d]``.  A sequence
+``b`` owns logical token ``j`` at ``cache[block_table[b][j // P]][hk][j % P]``.
+
+Poison conventions, so that a read of memory the method must not touch shows
+up in the output:
+
+* slots at or past ``L_b`` in the last page of a sequence hold NaN codes;
+* pages that no block table references hold NaN codes;
+* block-table entries past ``ceil(L_b / P)`` hold ``INT32_MAX``.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+
+INT32_MAX = 2**31 - 1
+BF16_NAN = 0x7FC0        # quiet NaN in bfloat16
+E4M3_NAN = 0x7F          # NaN in the OCP e4m3fn encoding (no infinities)
+E4M3_MAX = 448.0
+
+KV_BF16 = "bf16"
+KV_E4M3 = "e4m3"
+
+
+@dataclasses.dataclass
+class Case:
+    """One decode-attention problem, as raw codes plus metadata."""
+    name: str
+    B: int
+    T: int
+    Hq: int
+    Hkv: int
+    d_qk: int
+    d_v: int
+    page_size: int
+    kv_dtype: str                 # "bf16" or "e4m3"
+    mla: bool                     # one latent cache, V = K[..., :d_v]
+    causal: bool
+    scale: float                  # softmax scale sigma, an fp32 value
+    k_scale: float                # per-tensor dequant scale (1.0 for bf16)
+    v_scale: float
+    out_fp32: bool                # output dtype: fp32 if True, else bf16
+    seq_lens: np.ndarray          # [B] int32
+    block_table: np.ndarray       # [B, max_pages] int32
+    q: np.ndarray                 # [B, T, Hq, d_qk] uint16 (bf16 codes)
+    k_cache: np.ndarray           # [num_pages, Hkv, P, d_qk] uint16 or uint8 codes
+    v_cache: Optional[np.ndarray]  # [num_pages, Hkv, P, d_v] codes, None for MLA
+    seed: int
+
+    @property
+    def g(self) -> int:
+        return self.Hq // self.Hkv
+
+    @property
+    def num_pages(self) -> int:
+        return int(self.k_cache.shape[0])
+
+    def kv_bytes(self) -> int:
+        """Algorithmic KV bytes one decode step must read (each cached token once)."""
+        tok = int(np.sum(self.seq_lens.astype(np.int64)))
+        elem = 1 if self.kv_dtype == KV_E4M3 else 2
+        if self.mla:
+            return tok * self.d_qk * elem
+        return tok * self.Hkv * (self.d_qk + self.d_v) * elem
+
+
+# --------------------------------------------------------------------------
+# rounding of fp32 draws to storage codes (input preparation only)
+# --------------------------------------------------------------------------
+
+def _torch():
+    import torch  # local import: the generators are usable without a GPU
+    return torch
+
+
+def to_bf16_codes(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to bfloat16 (round-to-nearest-even) and return raw codes."""
+    torch = _torch()
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def to_e4m3_codes(x: np.ndarray) -> np.ndarray:
+    """Clamp to +-448 and round to OCP e4m3fn (RNE); return raw codes.
+
+    torch's CPU conversion does not saturate (500 becomes NaN), so the clamp
+    comes first.
+    """
+    torch = _torch()
+    t = torch.from_numpy(np.clip(np.ascontiguousarray(x, dtype=np.float32), -E4M3_MAX, E4M3_MAX))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+
+
+# --------------------------------------------------------------------------
+# page pools and block tables
+# --------------------------------------------------------------------------
+
+def _page_pool(rng, seq_lens, page_size, spare_frac=0.03, contiguous=False):
+    """Assign physical pages to sequences.
+
+    Returns (block_table, num_pages).  With ``contiguous`` every sequence owns
+    consecutive pages in order; otherwise the pool is a seeded permutation with
+    a few spare pages that no sequence references.
+    """
+    pages_per = [max(1, -(-int(L) // page_size)) for L in seq_lens]
+    used = sum(pages_per)
+    spare = 0 if contiguous else max(1, int(math.ceil(used * spare_frac)))
+    num_pages = used + spare
+    perm = np.arange(num_pages) if contiguous else rng.permutation(num_pages)
+    max_pages = max(pages_per)
+    bt = np.full((len(seq_lens), max_pages), INT32_MAX, dtype=np.int32)
+    off = 0
+    for b, n in enumerate(pages_per):
+        bt[b, :n] = perm[off:off + n]
+        off += n
+    return bt, num_pages
+
+
+def _fill_cache(rng, num_pages, H, P, D, std, dtype, bt, seq_lens, scale_out, chunk_pages=4096):
+    """Draw a paged cache; page tails and unreferenced pages hold NaN codes."""
+    if dtype == KV_BF16:
+        cache = np.empty((num_pages, H, P, D), dtype=np.uint16)
+    else:
+        cache = np.empty((num_pages, H, P, D), dtype=np.uint8)
+    amax = 0.0
+    draws = []
+    # first pass: draw in chunks (fp32), remember amax for the FP8 scale
+    for p0 in range(0, num_pages, chunk_pages):
+        p1 = min(num_pages, p0 + chunk_pages)
+        x = rng.standard_normal((p1 - p0, H, P, D), dtype=np.float32) * np.float32(std)
+        if dtype == KV_BF16:
+            cache[p0:p1] = to_bf16_codes(x)
+        else:
+            amax = max(amax, float(np.max(np.abs(x))))
+            draws.append((p0, p1, x))
+    if dtype == KV_E4M3:
+        s = scale_out if scale_out is not None else amax / E4M3_MAX
+        inv = np.float32(1.0) / np.float32(s)
+        for p0, p1, x in draws:
+            cache[p0:p1] = to_e4m3_codes(x * inv)
+        scale = float(np.float32(s))
+    else:
+        scale = 1.0
+    nan = BF16_NAN if dtype == KV_BF16 else E4M3_NAN
+    referenced = np.zeros(num_pages, dtype=bool)
+    for b, L in enumerate(seq_lens):
+        n = max(1, -(-int(L) // P))
+        pages = bt[b, :n]
+        referenced[pages] = True
+        tail = int(L) - (n - 1) * P          # valid slots in the last page
+        cache[pages[-1], :, tail:, :] = nan
+    cache[~referenced] = nan
+    return cache, scale
+
+
+# --------------------------------------------------------------------------
+# the workloads
+# --------------------------------------------------------------------------
+
+def log_uniform_lengths(rng, B, lo=1, hi=131072, forced=(1, 2, 15, 16, 17, 255, 131072)):
+    """Ragged lengths: floor(exp(u)), u ~ U[ln lo, ln hi], with forced edge entries first."""
+    u = rng.uniform(math.log(lo), math.log(hi), size=B)
+    L = np.floor(np.exp(u)).astype(np.int64)
+    L = np.clip(L, lo, hi)
+    for i, v in enumerate(forced[:B]):
+        L[i] = v
+    return L.astype(np.int32)
+
+
+def make_case(name: str, *, B: int, T: int, Hq: int, Hkv: int, d_qk: int, d_v: int,
+              seq_lens, page_size: int, kv_dtype: str = KV_BF16, mla: bool = False,
+              std: float = 1.0, q_std: Optional[float] = None, scale: Optional[float] = None,
+              out_fp32: bool = False, seed: int = 0, contiguous: bool = False,
+              fp8_scale: Optional[float] = None) -> Case:
+    """Generic generator; every workload below is one call of it."""
+    rng = np.random.default_rng(seed)
+    seq_lens = np.asarray(seq_lens, dtype=np.int32).reshape(B)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_qk)
+    scale = float(np.float32(scale))
+    q_std = std if q_std is None else q_std
+    bt, num_pages = _page_pool(rng, seq_lens, page_size, contiguous=contiguous)
+    qx = rng.standard_normal((B, T, Hq, d_qk), dtype=np.float32) * np.float32(q_std)
+    q = to_bf16_codes(qx)
+    if mla:
+        k_cache, k_scale = _fill_cache(rng, num_pages, 1, page_size, d_qk, std, kv_dtype, bt,
+                                       seq_lens, fp8_scale)
+        v_cache, v_scale = None, k_scale
+    else:
+        k_cache, k_scale = _fill_cache(rng, num_pages, Hkv, page_size, d_qk, std, kv_dtype, bt,
+                                       seq_lens, fp8_scale)
+        v_cache, v_scale = _fill_cache(rng, num_pages, Hkv, page_size, d_v, std, kv_dtype, bt,
+                                       seq_lens, fp8_scale)
+    return Case(name=name, B=B, T=T, Hq=Hq, Hkv=Hkv, d_qk=d_qk, d_v=d_v, page_size=page_size,
+                kv_dtype=kv_dtype, mla=mla, causal=T > 1, scale=scale, k_scale=k_scale,
+                v_scale=v_scale, out_fp32=out_fp32, seq_lens=seq_lens, block_table=bt, q=q,
+                k_cache=k_cache, v_cache=v_cache, seed=seed)
+
+
+def tiny_gqa(L: int = 256, seed: int = 1001) -> Case:
+    """Tiny GQA decode: B=1, T=1, Hq=8, Hkv=2, D=128, contiguous bf16, fp32 output."""
+    P = max(16, -(-L // 16) * 16)          # one page holds the whole sequence
+    return make_case("tiny-gqa", B=1, T=1, Hq=8, Hkv=2, d_qk=128, d_v=128, seq_lens=[L],
+                     page_size=P, out_fp32=True, seed=seed, contiguous=True)
+
+
+def few_kv_long(L: int = 5900, seed: int = 1002) -> Case:
+    """Few-KV-head long-context decode: B=1, T=1, Hq=16, Hkv=2, D=256, page 16, bf16."""
+    return make_case("few-kv-long", B=1, T=1, Hq=16, Hkv=2, d_qk=256, d_v=256, seq_lens=[L],
+                     page_size=16, seed=seed)
+
+
+def fp8_batched(B: int = 8, L: int = 32000, seed: int = 1003, fp8_scale=None) -> Case:
+    """Batched GQA with an e4m3 KV cache: Hq=32, Hkv=4, D=128, page 16, bf16 queries."""
+    return make_case("fp8-batched", B=B, T=1, Hq=32, Hkv=4, d_qk=128, d_v=128,
+                     seq_lens=[L] * B, page_size=16, kv_dtype=KV_E4M3, seed=seed,
+                     fp8_scale=fp8_scale)
+
+
+def mla_decode(L: int = 2048, seed: int = 1004, T: int = 6, Hq: int = 128) -> Case:
+    """MLA decode: 6 causal query tokens, 128 heads, one 576-wide latent head (V = first 512)."""
+    return make_case("mla", B=1, T=T, Hq=Hq, Hkv=1, d_qk=576, d_v=512, seq_lens=[L],
+                     page_size=64, mla=True, std=0.5, seed=seed)
+
+
+def ragged(B: int = 32, seed: int = 1005, hi: int = 131072, seq_lens=None) -> Case:
+    """Ragged batch: Hq=32, Hkv=8, D=128, bf16, log-uniform lengths in [1, hi], page 16."""
+    rng = np.random.default_rng(seed + 7919)
+    if seq_lens is None:
+        forced = tuple(min(v, hi) for v in (1, 2, 15, 16, 17, 255, 131072))
+        seq_lens = log_uniform_lengths(rng, B, hi=hi, forced=forced)
+    return make_case("ragged", B=B, T=1, Hq=32, Hkv=8, d_qk=128, d_v=128, seq_lens=seq_lens,
+                     page_size=16, seed=seed)
+
+
+# --------------------------------------------------------------------------
+# bf16 code helpers for the GPU side's upload (bit views only, no rounding)
+# --------------------------------------------------------------------------
+
+def random_queries(rng, shape, std=1.0) -> np.ndarray:
+    return to_bf16_codes(rng.standard_normal(shape, dtype=np.float32) * np.float32(std))

@@ -1,0 +1,78 @@
+"""Planted mistakes in the oracle must be caught by its pins.
+
+Each test swaps one oracle function for a plausibly wrong variant (on the CPU,
+in this process only) and checks that at least one pin then fails.
+"""
+import numpy as np
+import pytest
+
+import oracle.attention as A
+import oracle.codes as C
+import oracle.plan as P
+import tests.test_oracle_attention as TA
+import tests.test_oracle_codes as TC
+import tests.test_oracle_plan as TP
+
+
+def _fails(fn, *args):
+    with pytest.raises(AssertionError):
+        fn(*args)
+
+
+def test_wrong_e4m3_bias_is_caught(monkeypatch):
+    def bad(codes):
+        c = np.asarray(codes).astype(np.uint32)
+        sign = np.where((c >> 7) & 1, -1.0, 1.0)
+        e = ((c >> 3) & 0xF).astype(np.int64)
+        m = (c & 0x7).astype(np.float64)
+        out = np.where(e == 0, sign * np.ldexp(m / 8, -7), sign * np.ldexp(1 + m / 8, e - 8))
+        return np.where((e == 15) & (m == 7), np.nan, out)
+    monkeypatch.setattr(TC, "decode_e4m3", bad)
+    _fails(TC.test_e4m3_all_codes_match_torch)
+    _fails(TC.test_e4m3_spec_table)
+
+
+def test_wrong_head_grouping_is_caught(monkeypatch):
+    def bad_rows(case, hk):
+        return [(t, h) for t in range(case.T) for h in range(case.Hq) if h % case.Hkv == hk]
+    monkeypatch.setattr(A, "_rows_of_group", bad_rows)
+    _fails(TA.test_attend_vs_torch_sdpa_fp64)
+
+
+def test_dropped_scale_is_caught(monkeypatch):
+    orig = A.attend_rows
+    monkeypatch.setattr(A, "attend_rows", lambda q, K, V, sigma, lim: orig(q, K, V, 1.0, lim))
+    _fails(TA.test_golden_two_key)
+
+
+def test_off_by_one_causal_limit_is_caught(monkeypatch):
+    orig = A.attend_rows
+    monkeypatch.setattr(A, "attend_rows",
+                        lambda q, K, V, s, lim: orig(q, K, V, s, [x + 1 for x in lim]))
+    _fails(TA.test_attend_causal_vs_torch_sdpa_fp64)
+
+
+def test_unweighted_combine_is_caught(monkeypatch):
+    def bad(pm, pl, po, ns, off):
+        O, L = np.zeros((len(ns),) + pm.shape[1:] + (po.shape[-1],)), np.zeros((len(ns),) + pm.shape[1:])
+        for b in range(len(ns)):
+            sl = slice(off[b], off[b] + ns[b])
+            O[b] = po[sl].sum(0) / np.maximum(pl[sl].sum(0), 1e-300)[..., None]
+            L[b] = np.log(np.maximum(pl[sl].sum(0), 1e-300)) + pm[sl].max(0)
+        return O, L
+    monkeypatch.setattr(A, "combine", bad)
+    _fails(TA.test_split_emulation_equals_unsplit, 1, 3)
+
+
+def test_split_range_off_by_one_is_caught(monkeypatch):
+    def bad(L, n, i):
+        nblk = -(-L // 16)
+        return 16 * ((i * nblk) // n), min(L, 16 * (((i + 1) * nblk) // n) - 1)
+    monkeypatch.setattr(P, "split_range", bad)
+    _fails(TP.test_ranges_partition_and_are_nonempty)
+
+
+def test_ignored_request_is_caught(monkeypatch):
+    # the regression the pages describe: the stored default of one wins
+    monkeypatch.setattr(P, "clamp_request", lambda L, n, mx: 1)
+    _fails(TP.test_request_is_honoured_exactly)
