@@ -1,0 +1,236 @@
+/*
+ * splitkv.h -- C ABI of the MI355X (gfx950) split-KV decode-attention library.
+ *
+ * The operation: a few query tokens per sequence attend over a long, paged KV
+ * cache.  Each sequence's KV range is cut into num_splits ranges; every range
+ * yields a partial result (running max m, weight sum l, unnormalised output
+ * o) and a log-sum-exp combine merges the partials into the exact softmax
+ * output and its log-sum-exp.  Splitting exists to spread few-KV-head,
+ * long-context decode over many compute units ("vLLM 0.30.0 FA4 SplitKV Bug:
+ * H100 Decode Can Be 48% Slower", sections "What SplitKV is trying to do" and
+ * "Gemma 4 exposes the failure clearly"); extra splits never change the
+ * result, empty ones contribute zero weight (same page, "Why the result is
+ * still correct").
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked (host) are host memory; every other pointer is device
+ *     memory on the current HIP device.  The library never allocates device
+ *     memory and keeps no per-call state: the caller owns every buffer,
+ *     including the workspace (per-call buffer allocation inside attention
+ *     backends was flagged as a memory hazard in "Xqa decode kernels",
+ *     review comments).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Launches are asynchronous; device faults surface at the caller's next
+ *     synchronisation.
+ *   - Every call validates its arguments on the host and returns a status.
+ *     Nothing asserts or aborts across the ABI; splitkv_last_error() returns
+ *     a thread-local message for the last non-OK status.  Unsupported
+ *     devices and shapes fail cleanly with SPLITKV_ERR_UNSUPPORTED (an
+ *     unsupported-architecture path that crashed engine start-up is one of
+ *     the failures recorded in "Xqa decode kernels", commit timeline).
+ *   - Element strides are in elements of the tensor's own type; the last
+ *     (feature) dimension is always contiguous.  Queries need not be
+ *     contiguous otherwise ("Xqa decode kernels", timeline: a contiguity
+ *     assertion on the query crashed Hopper and was relaxed).
+ *
+ * Shapes and layouts:
+ *   q            bf16 [B][T][Hq][d_qk], strides q_stride_b/_t/_h.
+ *   k_cache      [num_pages][Hkv][page_size][d_qk] via strides
+ *                k_stride_page/_head/_tok (HND layout by default, any order
+ *                of the three outer dimensions through the strides).
+ *   v_cache      same with d_v; ignored for MLA, where V = K[..., :d_v].
+ *   block_table  int32 [B][bt_stride]; entry p of row b is the physical page
+ *                holding logical tokens [p*page_size, (p+1)*page_size).
+ *                Entries past ceil(L_b / page_size) are never read.
+ *   seq_lens     int32 [B]; L_b counts every cached token of sequence b,
+ *                including its own T query tokens.  Query token t sits at
+ *                position L_b - T + t and sees keys j <= L_b - T + t.
+ *   head map     query head h reads KV head h / (Hq / Hkv).
+ *   out          [B][T][Hq][d_v], bf16 or fp32 (out_dtype), contiguous.
+ *   lse          fp32 [B][T][Hq] natural-log log-sum-exp of the scaled
+ *                scores; may be NULL.
+ *   workspace    fp32; layout (S = total_slots, R = T*Hq):
+ *                  part_m [S][R]   max of scale*q.k over the split (natural
+ *                                  log units; -inf if the row sees nothing)
+ *                  part_l [S][R]   sum of exp(s - m)
+ *                  part_o [S][R][d_v]  sum of exp(s - m) * v (v dequantised)
+ *                part_o starts at the first 256-byte boundary after part_l;
+ *                splitkv_workspace_bytes() gives the total.
+ *   debug        optional int32 [S][Hkv][row_blocks][8] records
+ *                (b, i, hk, s, e, groups, xor_phys, sum_phys mod 2^31) over
+ *                the 16-token groups of the split's range; row_blocks =
+ *                ceil(g*T / rows_per_wg).  NULL disables it.
+ */
+#ifndef SPLITKV_H
+#define SPLITKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t splitkv_status;
+#define SPLITKV_OK 0
+#define SPLITKV_ERR_INVALID_ARG (-1)   /* null pointer, bad size, inconsistent shape */
+#define SPLITKV_ERR_UNSUPPORTED (-2)   /* device is not gfx950, or shape not built */
+#define SPLITKV_ERR_WORKSPACE (-3)     /* workspace smaller than splitkv_workspace_bytes() */
+#define SPLITKV_ERR_LAUNCH (-4)        /* a kernel launch returned an error */
+#define SPLITKV_ERR_DEVICE (-5)        /* a HIP runtime query failed */
+
+/* Split-range contract (see splitkv_plan). */
+#define SPLITKV_GRANULE 16             /* tokens; split ranges start on multiples of it */
+#define SPLITKV_AUTO_MIN_TOKENS 256    /* auto mode: fewest tokens per split */
+#define SPLITKV_AUTO_WG_PER_CU 2       /* auto mode: target workgroups per compute unit */
+#define SPLITKV_MAX_SPLITS_LIMIT 256   /* upper bound of max_splits */
+#define SPLITKV_ROWS_PER_WG_GQA 16     /* query rows (g*T) one GQA workgroup covers */
+#define SPLITKV_ROWS_PER_WG_MLA 64     /* query rows (T*Hq) one MLA workgroup covers */
+#define SPLITKV_DEBUG_INTS 8
+
+enum { SPLITKV_KV_BF16 = 0, SPLITKV_KV_E4M3 = 1 };
+enum { SPLITKV_KERNEL_GQA = 0, SPLITKV_KERNEL_MLA = 1 };
+enum { SPLITKV_OUT_BF16 = 0, SPLITKV_OUT_F32 = 1 };
+
+typedef struct {
+  int32_t B, T, Hq, Hkv;
+  int32_t kernel;            /* SPLITKV_KERNEL_GQA or SPLITKV_KERNEL_MLA (rows per workgroup) */
+  int32_t requested_splits;  /* > 0: honoured exactly when <= min(max_splits, nblk); 0: auto */
+  int32_t max_splits;        /* 1 .. SPLITKV_MAX_SPLITS_LIMIT */
+  int32_t num_cus;           /* > 0: compute units to plan for; 0: query the current device */
+} splitkv_plan_args;
+
+/*
+ * splitkv_plan -- host-only split planner.
+ *
+ * The runtime count decides the ranges: a request n > 0 yields exactly
+ * min(n, max_splits, nblk) non-empty splits, nblk = ceil(L / 16) (the
+ * regression in "vLLM 0.30.0 FA4 SplitKV Bug ...", section "The actual bug is
+ * one missing constructor argument", read a stored count of one and gave
+ * every other split an empty range).  n == 0 sizes splits for the machine:
+ * about SPLITKV_AUTO_WG_PER_CU * num_cus workgroups in total, at least
+ * SPLITKV_AUTO_MIN_TOKENS tokens per split, because the merge has a cost that
+ * can eat the gain of more splits ("Shipped: 484.5 tok/s on one GB300 ...",
+ * section "Why 8 splits lost").
+ *
+ * Split i of n covers [16*floor(i*nblk/n), min(L, 16*floor((i+1)*nblk/n))).
+ * L == 0 gives one empty split.
+ *
+ * Outputs (all host): num_splits[B]; slot_offset[B+1] (exclusive prefix
+ * sum); slot_seq[S] with slot_seq[slot_offset[b] + i] = b*256 + i, written
+ * only if slot_seq_host is not NULL and S <= slot_seq_capacity (else
+ * SPLITKV_ERR_INVALID_ARG); *total_slots = S.  B * max_splits always bounds S.
+ */
+splitkv_status splitkv_plan(const splitkv_plan_args* args, const int32_t* seq_lens_host,
+                            int32_t* num_splits_host, int32_t* slot_offset_host,
+                            int32_t* slot_seq_host, int32_t slot_seq_capacity,
+                            int32_t* total_slots);
+
+/* Token range [*s, *e) of split i of n for a sequence of L tokens (host; same formula as the kernels). */
+splitkv_status splitkv_split_range(int32_t L, int32_t n, int32_t i, int32_t* s, int32_t* e);
+
+/* Bytes of fp32 workspace the partials of S slots need. */
+size_t splitkv_workspace_bytes(int32_t total_slots, int32_t T, int32_t Hq, int32_t d_v);
+
+/* Arguments of the decode entry points. */
+typedef struct {
+  const void* q;                   /* bf16 */
+  int64_t q_stride_b, q_stride_t, q_stride_h;
+  const void* k_cache;             /* bf16 or e4m3 codes */
+  const void* v_cache;             /* same dtype; ignored (may be NULL) for MLA */
+  int64_t k_stride_page, k_stride_head, k_stride_tok;
+  int64_t v_stride_page, v_stride_head, v_stride_tok;
+  const int32_t* block_table;
+  int64_t bt_stride;
+  const int32_t* seq_lens;         /* [B] */
+  const int32_t* num_splits;       /* [B]   from splitkv_plan, on the device */
+  const int32_t* slot_offset;      /* [B+1] */
+  const int32_t* slot_seq;         /* [S] */
+  int32_t total_slots;             /* S, the host value splitkv_plan returned */
+  int32_t B, T, Hq, Hkv, d_qk, d_v, page_size, num_pages;
+  int32_t kv_dtype;                /* SPLITKV_KV_BF16 or SPLITKV_KV_E4M3 */
+  float scale;                     /* softmax scale applied to q.k */
+  float k_scale, v_scale;          /* dequant scales of an e4m3 cache (1 for bf16) */
+  float* workspace;
+  size_t workspace_bytes;
+  void* out;
+  int32_t out_dtype;               /* SPLITKV_OUT_BF16 or SPLITKV_OUT_F32 */
+  float* lse;                      /* may be NULL */
+  int32_t* debug;                  /* may be NULL */
+} splitkv_args;
+
+/*
+ * splitkv_decode_partial -- GQA partial kernel over a bf16 cache.
+ * One workgroup per (slot, KV head, block of 16 query rows) writes the
+ * partial (m, l, o) of its split ("vLLM 0.30.0 FA4 SplitKV Bug ...", section
+ * "What SplitKV is trying to do": each split computes a partial attention
+ * result).  Requires kv_dtype == BF16, d_qk == d_v in {128, 256},
+ * page_size % 16 == 0, 16-byte aligned q / caches / strides.
+ */
+splitkv_status splitkv_decode_partial(const splitkv_args* args, void* stream);
+
+/*
+ * splitkv_decode_partial_fp8 -- the same over an e4m3 cache with bf16
+ * queries ("Xqa decode kernels", section "Purpose": BF16/FP16 queries with an
+ * FP8 KV cache).  Codes widen exactly to bf16; k_scale multiplies the scores,
+ * v_scale the output.  The query is never quantised and takes no scale of its
+ * own (same page, timeline: no q_scale for model-dtype queries over an FP8
+ * cache).  Requires kv_dtype == E4M3, d_qk == d_v in {128, 256}.
+ */
+splitkv_status splitkv_decode_partial_fp8(const splitkv_args* args, void* stream);
+
+/*
+ * splitkv_mla_decode_partial -- MLA partial kernel: one latent KV head
+ * (Hkv == 1) of width d_qk == 576 serves as key, its first d_v == 512
+ * columns as value; one workgroup per (slot, block of 64 query rows in
+ * (t, h) order).  Causal within the T query tokens ("Shipped: 484.5 tok/s on
+ * one GB300 ...", table "What shipped": split-KV MLA decode of one request
+ * at six tokens).  Requires kv_dtype == BF16.
+ */
+splitkv_status splitkv_mla_decode_partial(const splitkv_args* args, void* stream);
+
+/*
+ * splitkv_combine -- log-sum-exp merge of the partials of every sequence into
+ * out and lse: M = max_i m_i, w_i = exp(m_i - M) (0 for an empty split),
+ * out = sum_i w_i o_i / sum_i w_i l_i, lse = M + ln(sum_i w_i l_i); a row
+ * with no visible key gives out = 0, lse = -inf ("vLLM 0.30.0 FA4 SplitKV
+ * Bug ...", section "Why the result is still correct": empty splits
+ * contribute zero weight).
+ */
+splitkv_status splitkv_combine(const splitkv_args* args, void* stream);
+
+/*
+ * splitkv_decode -- the whole decode step: the partial kernel that kv_dtype
+ * and `kernel` select, then the combine.  Sequences with a single split
+ * write out/lse directly from the partial kernel and are skipped by the
+ * combine; when every sequence has one split the combine is not launched.
+ * `kernel` is SPLITKV_KERNEL_GQA or SPLITKV_KERNEL_MLA.
+ */
+splitkv_status splitkv_decode(const splitkv_args* args, int32_t kernel, void* stream);
+
+/*
+ * splitkv_validate_block_table -- host-side check that every block-table
+ * entry a sequence reads (the first ceil(L_b / page_size)) lies in
+ * [0, num_pages).  All pointers are host memory.
+ */
+splitkv_status splitkv_validate_block_table(const int32_t* block_table_host,
+                                            const int32_t* seq_lens_host, int32_t B,
+                                            int64_t bt_stride, int32_t page_size,
+                                            int32_t num_pages);
+
+/*
+ * splitkv_e4m3_to_bf16 -- widen n e4m3 codes to bf16 codes on the device with
+ * the conversion the FP8 kernels use (exposed so that tests can check every
+ * code).
+ */
+splitkv_status splitkv_e4m3_to_bf16(const uint8_t* in, uint16_t* out, int64_t n, void* stream);
+
+const char* splitkv_last_error(void);   /* thread-local message of the last failure */
+const char* splitkv_version(void);      /* source revision the library was built from */
+size_t splitkv_args_size(void);         /* sizeof(splitkv_args), for binding checks */
+size_t splitkv_plan_args_size(void);    /* sizeof(splitkv_plan_args) */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPLITKV_H */

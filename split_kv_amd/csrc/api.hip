@@ -1,0 +1,301 @@
+// C ABI of the split-KV decode library: argument checks, the gfx950 gate and
+// dispatch to the kernels.  Every entry point returns a status and records a
+// message instead of asserting; the library allocates nothing.
+#include <cstring>
+#include <mutex>
+
+#include "device.h"
+#include "internal.h"
+
+#ifndef SPLITKV_REVISION
+#define SPLITKV_REVISION "unknown"
+#endif
+
+namespace splitkv {
+
+hipError_t launch_gqa_partial(const PartialParams& p, int D, bool fp8, hipStream_t stream);
+hipError_t launch_mla_partial(const PartialParams& p, hipStream_t stream);
+hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
+hipError_t launch_e4m3_to_bf16(const uint8_t* in, uint16_t* out, int64_t n, hipStream_t stream);
+
+namespace {
+
+struct DeviceInfo {
+  bool checked = false;
+  bool gfx950 = false;
+  int cus = 0;
+  char arch[64] = {0};
+};
+
+constexpr int kMaxDevices = 64;
+std::mutex g_dev_mu;
+DeviceInfo g_dev[kMaxDevices];
+
+// The kernels are written for gfx950 only; anything else is refused cleanly.
+splitkv_status check_device(int* cus) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(SPLITKV_ERR_DEVICE, "hipGetDevice failed");
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  DeviceInfo& d = g_dev[dev];
+  if (!d.checked) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+      return fail(SPLITKV_ERR_DEVICE, "hipGetDeviceProperties(%d) failed", dev);
+    strncpy(d.arch, prop.gcnArchName, sizeof(d.arch) - 1);
+    d.gfx950 = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    d.cus = prop.multiProcessorCount;
+    d.checked = true;
+  }
+  if (!d.gfx950)
+    return fail(SPLITKV_ERR_UNSUPPORTED, "device %d is %s; this library is built for gfx950 only",
+                dev, d.arch);
+  if (cus) *cus = d.cus;
+  return SPLITKV_OK;
+}
+
+bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+
+enum class Kind { GqaBf16, GqaFp8, Mla };
+
+struct Layout {
+  float* m;
+  float* l;
+  float* o;
+};
+
+Layout workspace_layout(const splitkv_args& a) {
+  const size_t rows = size_t(a.total_slots) * size_t(a.T) * size_t(a.Hq);
+  size_t ml = 2 * rows * sizeof(float);
+  ml = (ml + 255) / 256 * 256;
+  Layout w;
+  w.m = a.workspace;
+  w.l = a.workspace ? a.workspace + rows : nullptr;
+  w.o = a.workspace ? reinterpret_cast<float*>(reinterpret_cast<char*>(a.workspace) + ml) : nullptr;
+  return w;
+}
+
+splitkv_status check_common(const splitkv_args* a, const char* fn) {
+  if (!a) return fail(SPLITKV_ERR_INVALID_ARG, "%s: null args", fn);
+  if (!a->seq_lens || !a->num_splits || !a->slot_offset)
+    return fail(SPLITKV_ERR_INVALID_ARG, "%s: null plan pointer", fn);
+  if (a->B < 1 || a->T < 1 || a->Hq < 1 || a->Hkv < 1 || a->Hq % a->Hkv != 0)
+    return fail(SPLITKV_ERR_INVALID_ARG, "%s: bad shape B=%d T=%d Hq=%d Hkv=%d", fn, a->B, a->T,
+                a->Hq, a->Hkv);
+  if (a->total_slots < a->B)
+    return fail(SPLITKV_ERR_INVALID_ARG, "%s: total_slots=%d < B=%d", fn, a->total_slots, a->B);
+  if (a->out_dtype != SPLITKV_OUT_BF16 && a->out_dtype != SPLITKV_OUT_F32)
+    return fail(SPLITKV_ERR_INVALID_ARG, "%s: out_dtype=%d", fn, a->out_dtype);
+  if (a->lse && !aligned(a->lse, 4)) return fail(SPLITKV_ERR_INVALID_ARG, "%s: lse misaligned", fn);
+  return SPLITKV_OK;
+}
+
+splitkv_status check_partial(const splitkv_args* a, Kind kind, bool need_ws, const char* fn,
+                             int* row_blocks) {
+  splitkv_status st = check_common(a, fn);
+  if (st != SPLITKV_OK) return st;
+  if (!a->q || !a->k_cache || !a->block_table || !a->slot_seq)
+    return fail(SPLITKV_ERR_INVALID_ARG, "%s: null q, k_cache, block_table or slot_seq", fn);
+  if (kind != Kind::Mla && !a->v_cache) return fail(SPLITKV_ERR_INVALID_ARG, "%s: null v_cache", fn);
+  if (a->page_size < 16 || a->page_size % SPLITKV_GRANULE != 0)
+    return fail(SPLITKV_ERR_UNSUPPORTED, "%s: page_size=%d must be a positive multiple of 16", fn,
+                a->page_size);
+  if (a->num_pages < 1) return fail(SPLITKV_ERR_INVALID_ARG, "%s: num_pages=%d", fn, a->num_pages);
+  if (a->bt_stride < 1) return fail(SPLITKV_ERR_INVALID_ARG, "%s: bt_stride < 1", fn);
+  const int want_kv = kind == Kind::GqaFp8 ? SPLITKV_KV_E4M3 : SPLITKV_KV_BF16;
+  if (a->kv_dtype != want_kv)
+    return fail(SPLITKV_ERR_INVALID_ARG, "%s: kv_dtype=%d, this entry point takes %d", fn,
+                a->kv_dtype, want_kv);
+  if (kind == Kind::Mla) {
+    if (a->Hkv != 1 || a->d_qk != 576 || a->d_v != 512)
+      return fail(SPLITKV_ERR_UNSUPPORTED, "%s: MLA needs Hkv=1, d_qk=576, d_v=512 (got %d, %d, %d)",
+                  fn, a->Hkv, a->d_qk, a->d_v);
+  } else if (a->d_qk != a->d_v || (a->d_qk != 128 && a->d_qk != 256)) {
+    return fail(SPLITKV_ERR_UNSUPPORTED, "%s: head dims d_qk=%d d_v=%d; built for 128 and 256", fn,
+                a->d_qk, a->d_v);
+  }
+  if (!(a->scale > 0.f) || !(a->k_scale > 0.f) || !(a->v_scale > 0.f))
+    return fail(SPLITKV_ERR_INVALID_ARG, "%s: scales must be positive", fn);
+  // 16-byte vector loads of q rows and cache rows
+  const int64_t elem = kind == Kind::GqaFp8 ? 1 : 2;
+  if (!aligned(a->q, 16) || (a->q_stride_b * 2) % 16 || (a->q_stride_t * 2) % 16 ||
+      (a->q_stride_h * 2) % 16)
+    return fail(SPLITKV_ERR_UNSUPPORTED, "%s: q or its strides not 16-byte aligned", fn);
+  if (!aligned(a->k_cache, 16) || (a->k_stride_page * elem) % 16 ||
+      (a->k_stride_head * elem) % 16 || (a->k_stride_tok * elem) % 16)
+    return fail(SPLITKV_ERR_UNSUPPORTED, "%s: k_cache or its strides not 16-byte aligned", fn);
+  if (kind != Kind::Mla &&
+      (!aligned(a->v_cache, 16) || (a->v_stride_page * elem) % 16 ||
+       (a->v_stride_head * elem) % 16 || (a->v_stride_tok * elem) % 16))
+    return fail(SPLITKV_ERR_UNSUPPORTED, "%s: v_cache or its strides not 16-byte aligned", fn);
+  if (!a->out || !aligned(a->out, 16)) return fail(SPLITKV_ERR_INVALID_ARG, "%s: out null or misaligned", fn);
+  if (need_ws) {
+    const size_t need = splitkv_workspace_bytes(a->total_slots, a->T, a->Hq, a->d_v);
+    if (!a->workspace || !aligned(a->workspace, 16) || a->workspace_bytes < need)
+      return fail(SPLITKV_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu (16-byte aligned)", fn,
+                  a->workspace_bytes, need);
+  }
+  const int64_t rows = kind == Kind::Mla ? int64_t(a->T) * a->Hq : int64_t(a->Hq / a->Hkv) * a->T;
+  const int64_t rpw = kind == Kind::Mla ? SPLITKV_ROWS_PER_WG_MLA : SPLITKV_ROWS_PER_WG_GQA;
+  *row_blocks = int(ceil_div(rows, rpw));
+  const int64_t wgs = int64_t(a->total_slots) * a->Hkv * *row_blocks;
+  if (wgs > (int64_t(1) << 30)) return fail(SPLITKV_ERR_INVALID_ARG, "%s: grid too large", fn);
+  return SPLITKV_OK;
+}
+
+PartialParams make_partial_params(const splitkv_args& a, Kind kind, int row_blocks, bool direct) {
+  const int64_t elem = kind == Kind::GqaFp8 ? 1 : 2;
+  PartialParams p;
+  memset(&p, 0, sizeof(p));
+  p.q = static_cast<const uint16_t*>(a.q);
+  p.qsb = a.q_stride_b;
+  p.qst = a.q_stride_t;
+  p.qsh = a.q_stride_h;
+  p.k = static_cast<const uint8_t*>(a.k_cache);
+  p.v = kind == Kind::Mla ? p.k : static_cast<const uint8_t*>(a.v_cache);
+  p.ksp = a.k_stride_page * elem;
+  p.ksh = a.k_stride_head * elem;
+  p.kst = a.k_stride_tok * elem;
+  p.vsp = kind == Kind::Mla ? p.ksp : a.v_stride_page * elem;
+  p.vsh = kind == Kind::Mla ? p.ksh : a.v_stride_head * elem;
+  p.vst = kind == Kind::Mla ? p.kst : a.v_stride_tok * elem;
+  p.bt = a.block_table;
+  p.bt_stride = a.bt_stride;
+  p.seq_lens = a.seq_lens;
+  p.num_splits = a.num_splits;
+  p.slot_offset = a.slot_offset;
+  p.slot_seq = a.slot_seq;
+  p.T = a.T;
+  p.Hq = a.Hq;
+  p.Hkv = a.Hkv;
+  p.g = a.Hq / a.Hkv;
+  p.page_size = a.page_size;
+  p.rows = kind == Kind::Mla ? a.T * a.Hq : p.g * a.T;
+  p.row_blocks = row_blocks;
+  p.total_wg = a.total_slots * a.Hkv * row_blocks;
+  p.scale_log2 = a.scale * a.k_scale * kLog2e;
+  p.v_scale = a.v_scale;
+  const Layout w = workspace_layout(a);
+  p.part_m = w.m;
+  p.part_l = w.l;
+  p.part_o = w.o;
+  p.out = a.out;
+  p.out_f32 = a.out_dtype == SPLITKV_OUT_F32;
+  p.lse = a.lse;
+  p.debug = a.debug;
+  p.direct = direct ? 1 : 0;
+  return p;
+}
+
+splitkv_status run_partial(const splitkv_args* a, Kind kind, bool direct, void* stream,
+                           const char* fn) {
+  int row_blocks = 0;
+  // Direct mode only needs the workspace when some sequence has several splits.
+  const bool need_ws = !direct || (a && a->total_slots > a->B);
+  splitkv_status st = check_partial(a, kind, need_ws, fn, &row_blocks);
+  if (st != SPLITKV_OK) return st;
+  st = check_device(nullptr);
+  if (st != SPLITKV_OK) return st;
+  const PartialParams p = make_partial_params(*a, kind, row_blocks, direct);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t err = kind == Kind::Mla ? launch_mla_partial(p, s)
+                                           : launch_gqa_partial(p, a->d_qk, kind == Kind::GqaFp8, s);
+  if (err != hipSuccess) return fail(SPLITKV_ERR_LAUNCH, "%s: launch failed: %s", fn, hipGetErrorString(err));
+  return SPLITKV_OK;
+}
+
+splitkv_status run_combine(const splitkv_args* a, bool skip_single, void* stream, const char* fn) {
+  splitkv_status st = check_common(a, fn);
+  if (st != SPLITKV_OK) return st;
+  if (a->d_v != 128 && a->d_v != 256 && a->d_v != 512)
+    return fail(SPLITKV_ERR_UNSUPPORTED, "%s: d_v=%d; built for 128, 256, 512", fn, a->d_v);
+  if (!a->out || !aligned(a->out, 16)) return fail(SPLITKV_ERR_INVALID_ARG, "%s: out null or misaligned", fn);
+  const size_t need = splitkv_workspace_bytes(a->total_slots, a->T, a->Hq, a->d_v);
+  if (!a->workspace || !aligned(a->workspace, 16) || a->workspace_bytes < need)
+    return fail(SPLITKV_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, a->workspace_bytes,
+                need);
+  st = check_device(nullptr);
+  if (st != SPLITKV_OK) return st;
+  const Layout w = workspace_layout(*a);
+  CombineParams p;
+  p.num_splits = a->num_splits;
+  p.slot_offset = a->slot_offset;
+  p.part_m = w.m;
+  p.part_l = w.l;
+  p.part_o = w.o;
+  p.out = a->out;
+  p.out_f32 = a->out_dtype == SPLITKV_OUT_F32;
+  p.lse = a->lse;
+  p.B = a->B;
+  p.R = a->T * a->Hq;
+  p.d_v = a->d_v;
+  p.skip_single = skip_single ? 1 : 0;
+  const hipError_t err = launch_combine(p, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return fail(SPLITKV_ERR_LAUNCH, "%s: launch failed: %s", fn, hipGetErrorString(err));
+  return SPLITKV_OK;
+}
+
+}  // namespace
+}  // namespace splitkv
+
+using namespace splitkv;
+
+extern "C" {
+
+splitkv_status splitkv_plan(const splitkv_plan_args* args, const int32_t* seq_lens_host,
+                            int32_t* num_splits_host, int32_t* slot_offset_host,
+                            int32_t* slot_seq_host, int32_t slot_seq_capacity,
+                            int32_t* total_slots) {
+  if (!args) return fail(SPLITKV_ERR_INVALID_ARG, "splitkv_plan: null args");
+  int cus = args->num_cus;
+  if (cus == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return fail(SPLITKV_ERR_DEVICE, "splitkv_plan: cannot query the compute-unit count");
+  }
+  return plan_host(*args, cus, seq_lens_host, num_splits_host, slot_offset_host, slot_seq_host,
+                   slot_seq_capacity, total_slots);
+}
+
+splitkv_status splitkv_decode_partial(const splitkv_args* args, void* stream) {
+  return run_partial(args, Kind::GqaBf16, false, stream, "splitkv_decode_partial");
+}
+
+splitkv_status splitkv_decode_partial_fp8(const splitkv_args* args, void* stream) {
+  return run_partial(args, Kind::GqaFp8, false, stream, "splitkv_decode_partial_fp8");
+}
+
+splitkv_status splitkv_mla_decode_partial(const splitkv_args* args, void* stream) {
+  return run_partial(args, Kind::Mla, false, stream, "splitkv_mla_decode_partial");
+}
+
+splitkv_status splitkv_combine(const splitkv_args* args, void* stream) {
+  return run_combine(args, false, stream, "splitkv_combine");
+}
+
+splitkv_status splitkv_decode(const splitkv_args* args, int32_t kernel, void* stream) {
+  if (!args) return fail(SPLITKV_ERR_INVALID_ARG, "splitkv_decode: null args");
+  Kind kind;
+  if (kernel == SPLITKV_KERNEL_MLA) kind = Kind::Mla;
+  else if (kernel == SPLITKV_KERNEL_GQA) kind = args->kv_dtype == SPLITKV_KV_E4M3 ? Kind::GqaFp8 : Kind::GqaBf16;
+  else return fail(SPLITKV_ERR_INVALID_ARG, "splitkv_decode: unknown kernel %d", kernel);
+  splitkv_status st = run_partial(args, kind, true, stream, "splitkv_decode");
+  if (st != SPLITKV_OK || args->total_slots == args->B) return st;
+  return run_combine(args, true, stream, "splitkv_decode");
+}
+
+splitkv_status splitkv_e4m3_to_bf16(const uint8_t* in, uint16_t* out, int64_t n, void* stream) {
+  if (!in || !out || n < 0 || !aligned(in, 4) || !aligned(out, 2))
+    return fail(SPLITKV_ERR_INVALID_ARG, "splitkv_e4m3_to_bf16: bad arguments");
+  if (n == 0) return SPLITKV_OK;
+  splitkv_status st = check_device(nullptr);
+  if (st != SPLITKV_OK) return st;
+  const hipError_t err = launch_e4m3_to_bf16(in, out, n, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return fail(SPLITKV_ERR_LAUNCH, "splitkv_e4m3_to_bf16: %s", hipGetErrorString(err));
+  return SPLITKV_OK;
+}
+
+const char* splitkv_version(void) { return SPLITKV_REVISION; }
+
+}  // extern "C"

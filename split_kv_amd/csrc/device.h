@@ -1,0 +1,120 @@
+// Device-side helpers and the parameter block shared by the gfx950 kernels.
+//
+// Notation follows the split-KV pages: a decode step attends a few query
+// tokens over a long KV history; each split yields a partial (m, l, o) that a
+// combine merges ("vLLM 0.30.0 FA4 SplitKV Bug: H100 Decode Can Be 48%
+// Slower", section "What SplitKV is trying to do").
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace splitkv {
+
+typedef short bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Parameters of every partial kernel (plain values; built on the host).
+struct PartialParams {
+  const uint16_t* q;            // bf16 codes
+  int64_t qsb, qst, qsh;        // element strides
+  const uint8_t* k;             // cache base, as bytes
+  const uint8_t* v;
+  int64_t ksp, ksh, kst;        // byte strides
+  int64_t vsp, vsh, vst;
+  const int32_t* bt;
+  int64_t bt_stride;
+  const int32_t* seq_lens;
+  const int32_t* num_splits;
+  const int32_t* slot_offset;
+  const int32_t* slot_seq;
+  int32_t T, Hq, Hkv, g, page_size, rows, row_blocks, total_wg;
+  float scale_log2;             // scale * k_scale * log2(e)
+  float v_scale;
+  float* part_m;                // [S][T*Hq]
+  float* part_l;
+  float* part_o;                // [S][T*Hq][d_v]
+  void* out;
+  int32_t out_f32;
+  float* lse;
+  int32_t* debug;
+  int32_t direct;               // single-split sequences write out/lse directly
+};
+
+struct CombineParams {
+  const int32_t* num_splits;
+  const int32_t* slot_offset;
+  const float* part_m;
+  const float* part_l;
+  const float* part_o;
+  void* out;
+  int32_t out_f32;
+  float* lse;
+  int32_t B, R, d_v;            // R = T * Hq rows per sequence
+  int32_t skip_single;          // rows of single-split sequences were written by the partial kernel
+};
+
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Round an fp32 value to bfloat16 (round to nearest even; NaN stays NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// Widen four e4m3 codes (one dword) to four bf16 codes (two dwords).  Every
+// e4m3 value is a bf16 value, so the conversion is exact with scale 1.
+__device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t w) {
+  bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+  u32x2 r;
+  r.x = __builtin_bit_cast(uint32_t, lo);
+  r.y = __builtin_bit_cast(uint32_t, hi);
+  return r;
+}
+
+// Lane-exchange helpers within a 64-wide wavefront.
+__device__ __forceinline__ float xor_shfl(float v, int mask) {
+  return __shfl_xor(v, mask, 64);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+// Split i of n over L tokens, in 16-token granules: [s, e).
+__device__ __forceinline__ void split_bounds(int L, int n, int i, int* s, int* e) {
+  const int64_t nblk = (L + 15) >> 4;
+  *s = 16 * (int)((int64_t(i) * nblk) / n);
+  const int hi = 16 * (int)((int64_t(i + 1) * nblk) / n);
+  *e = hi < L ? hi : L;
+}
+
+template <typename T>
+__device__ __forceinline__ T uniform(T v) {
+  return __builtin_amdgcn_readfirstlane(v);
+}
+
+}  // namespace splitkv

@@ -1,0 +1,159 @@
+"""DecodeSession: plan + caller-owned buffers around the C ABI, for torch users.
+
+This is marshalling only.  It runs ``splitkv_plan`` on the host, copies the
+plan arrays to the device, allocates the workspace, output and log-sum-exp
+tensors with torch (the library itself never allocates), fills a
+``splitkv_args`` block from tensor addresses and strides, and calls the
+library's entry points on torch's current stream.  No arithmetic of the
+method happens here.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import (SPLITKV_KERNEL_GQA, SPLITKV_KERNEL_MLA, SPLITKV_KV_BF16, SPLITKV_KV_E4M3,
+               SPLITKV_OUT_BF16, SPLITKV_OUT_F32, SPLITKV_ROWS_PER_WG_GQA, SPLITKV_ROWS_PER_WG_MLA,
+               splitkv_args, splitkv_combine, splitkv_decode, splitkv_decode_partial,
+               splitkv_decode_partial_fp8, splitkv_mla_decode_partial, splitkv_plan,
+               splitkv_plan_args, splitkv_workspace_bytes)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+class DecodeSession:
+    """One decode-attention problem on the current HIP device.
+
+    q:           bf16 tensor [B, T, Hq, d_qk] (last dim contiguous, 16-byte aligned rows)
+    k_cache:     [num_pages, Hkv, P, d_qk] view (bf16, or uint8 / float8_e4m3fn codes);
+                 any strides with the feature dim contiguous
+    v_cache:     same with d_v (None for MLA, where V = K[..., :d_v])
+    block_table: int32 [B, max_pages] on the device
+    seq_lens:    host sequence lengths (numpy or list)
+    """
+
+    def __init__(self, *, q, k_cache, v_cache, block_table, seq_lens, scale: float,
+                 k_scale: float = 1.0, v_scale: float = 1.0, mla: bool = False,
+                 requested_splits: int = 0, max_splits: int = 64, num_cus: int = 0,
+                 out_fp32: bool = False, with_lse: bool = True, debug: bool = False):
+        torch = _torch()
+        self.torch = torch
+        dev = q.device
+        self.mla = bool(mla)
+        B, T, Hq, d_qk = q.shape
+        num_pages, Hkv, P, _ = k_cache.shape
+        d_v = 512 if mla else v_cache.shape[-1]
+        fp8 = k_cache.dtype in (torch.uint8, torch.float8_e4m3fn)
+        self.kv_dtype = SPLITKV_KV_E4M3 if fp8 else SPLITKV_KV_BF16
+        self.kernel = SPLITKV_KERNEL_MLA if mla else SPLITKV_KERNEL_GQA
+        self.shape = dict(B=B, T=T, Hq=Hq, Hkv=Hkv, d_qk=d_qk, d_v=d_v, P=P, num_pages=num_pages)
+        self.q, self.k_cache, self.v_cache = q, k_cache, v_cache
+        self.block_table = block_table
+        self.seq_lens_host = np.ascontiguousarray(seq_lens, dtype=np.int32)
+        self.seq_lens = torch.as_tensor(self.seq_lens_host, device=dev)
+        self.scale, self.k_scale, self.v_scale = float(scale), float(k_scale), float(v_scale)
+        self.out_fp32 = out_fp32
+        self.out = torch.empty((B, T, Hq, d_v), dtype=torch.float32 if out_fp32 else torch.bfloat16,
+                               device=dev)
+        self.lse = torch.empty((B, T, Hq), dtype=torch.float32, device=dev) if with_lse else None
+        self.want_debug = debug
+        self.num_cus = num_cus
+        self.max_splits = max_splits
+        self.replan(requested_splits)
+
+    # -- plan ---------------------------------------------------------------
+    def replan(self, requested_splits: int):
+        torch = self.torch
+        s = self.shape
+        pa = splitkv_plan_args(B=s["B"], T=s["T"], Hq=s["Hq"], Hkv=s["Hkv"], kernel=self.kernel,
+                               requested_splits=requested_splits, max_splits=self.max_splits,
+                               num_cus=self.num_cus)
+        ns, off, seq = splitkv_plan(pa, self.seq_lens_host)
+        self.requested_splits = requested_splits
+        self.num_splits_host, self.slot_offset_host, self.slot_seq_host = ns, off, seq
+        dev = self.q.device
+        self.num_splits = torch.as_tensor(ns, device=dev)
+        self.slot_offset = torch.as_tensor(off, device=dev)
+        self.slot_seq = torch.as_tensor(seq, device=dev)
+        self.total_slots = int(off[-1])
+        nbytes = splitkv_workspace_bytes(self.total_slots, s["T"], s["Hq"], s["d_v"])
+        self.workspace = torch.empty((nbytes + 3) // 4, dtype=torch.float32, device=dev)
+        if self.want_debug:
+            rows = s["T"] * s["Hq"] if self.mla else (s["Hq"] // s["Hkv"]) * s["T"]
+            rpw = SPLITKV_ROWS_PER_WG_MLA if self.mla else SPLITKV_ROWS_PER_WG_GQA
+            self.row_blocks = -(-rows // rpw)
+            self.debug = torch.full((self.total_slots, s["Hkv"], self.row_blocks, 8), -1,
+                                    dtype=torch.int32, device=dev)
+        else:
+            self.debug = None
+        self._build_args()
+
+    def _build_args(self):
+        s = self.shape
+        q, k, v = self.q, self.k_cache, self.v_cache
+        a = splitkv_args()
+        a.q = q.data_ptr()
+        a.q_stride_b, a.q_stride_t, a.q_stride_h = q.stride(0), q.stride(1), q.stride(2)
+        a.k_cache = k.data_ptr()
+        a.k_stride_page, a.k_stride_head, a.k_stride_tok = k.stride(0), k.stride(1), k.stride(2)
+        if v is not None:
+            a.v_cache = v.data_ptr()
+            a.v_stride_page, a.v_stride_head, a.v_stride_tok = v.stride(0), v.stride(1), v.stride(2)
+        a.block_table = self.block_table.data_ptr()
+        a.bt_stride = self.block_table.stride(0)
+        a.seq_lens = self.seq_lens.data_ptr()
+        a.num_splits = self.num_splits.data_ptr()
+        a.slot_offset = self.slot_offset.data_ptr()
+        a.slot_seq = self.slot_seq.data_ptr()
+        a.total_slots = self.total_slots
+        a.B, a.T, a.Hq, a.Hkv = s["B"], s["T"], s["Hq"], s["Hkv"]
+        a.d_qk, a.d_v, a.page_size, a.num_pages = s["d_qk"], s["d_v"], s["P"], s["num_pages"]
+        a.kv_dtype = self.kv_dtype
+        a.scale, a.k_scale, a.v_scale = self.scale, self.k_scale, self.v_scale
+        a.workspace = self.workspace.data_ptr()
+        a.workspace_bytes = self.workspace.numel() * 4
+        a.out = self.out.data_ptr()
+        a.out_dtype = SPLITKV_OUT_F32 if self.out_fp32 else SPLITKV_OUT_BF16
+        a.lse = self.lse.data_ptr() if self.lse is not None else None
+        a.debug = self.debug.data_ptr() if self.debug is not None else None
+        self.args = a
+
+    def set_block_table(self, block_table):
+        """Point later steps at another block table of the same shape (no re-plan)."""
+        self.block_table = block_table
+        self.args.block_table = block_table.data_ptr()
+        self.args.bt_stride = block_table.stride(0)
+
+    # -- steps ----------------------------------------------------------------
+    def _stream(self):
+        return self.torch.cuda.current_stream().cuda_stream
+
+    def decode(self):
+        """The whole decode step: partial kernel, then the combine where needed."""
+        splitkv_decode(self.args, self.kernel, self._stream())
+        return self.out, self.lse
+
+    def partial(self):
+        """Partial kernel only: writes (m, l, o) of every slot into the workspace."""
+        if self.mla:
+            splitkv_mla_decode_partial(self.args, self._stream())
+        elif self.kv_dtype == SPLITKV_KV_E4M3:
+            splitkv_decode_partial_fp8(self.args, self._stream())
+        else:
+            splitkv_decode_partial(self.args, self._stream())
+
+    def combine(self):
+        splitkv_combine(self.args, self._stream())
+        return self.out, self.lse
+
+    def partials(self):
+        """Views (part_m [S,T,Hq], part_l [S,T,Hq], part_o [S,T,Hq,d_v]) of the workspace."""
+        s = self.shape
+        S, T, Hq, dv = self.total_slots, s["T"], s["Hq"], s["d_v"]
+        rows = S * T * Hq
+        ml = -(-(2 * rows * 4) // 256) * 256 // 4
+        w = self.workspace
+        return (w[:rows].view(S, T, Hq), w[rows:2 * rows].view(S, T, Hq),
+                w[ml:ml + rows * dv].view(S, T, Hq, dv))

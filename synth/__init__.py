@@ -260,3 +260,42 @@ def ragged(B: int = 32, seed: int = 1005, hi: int = 131072, seq_lens=None) -> Ca
 
 def random_queries(rng, shape, std=1.0) -> np.ndarray:
     return to_bf16_codes(rng.standard_normal(shape, dtype=np.float32) * np.float32(std))
+
+
+# --------------------------------------------------------------------------
+# device upload (array conversion only)
+# --------------------------------------------------------------------------
+
+def to_torch(case: Case, device, layout: str = "HND", q_pad_heads: int = 0):
+    """Copy a case's arrays to ``device`` as torch tensors.
+
+    layout "HND" keeps [page][head][slot][d] contiguous; "NHD" stores
+    [page][slot][head][d] and returns the [page][head][slot][d] strided view.
+    ``q_pad_heads`` > 0 embeds q in a wider head dimension so that the query
+    tensor the kernels see is not contiguous.
+    """
+    torch = _torch()
+
+    def cache(arr):
+        if arr is None:
+            return None
+        dt = torch.int16 if arr.dtype == np.uint16 else torch.uint8
+        host = torch.from_numpy(arr.view(np.int16) if arr.dtype == np.uint16 else arr)
+        if layout == "NHD":
+            t = host.permute(0, 2, 1, 3).contiguous().to(device)
+            t = t.permute(0, 2, 1, 3)
+        else:
+            t = host.to(device)
+        assert t.dtype == dt
+        return t.view(torch.bfloat16) if dt == torch.int16 else t
+
+    q = torch.from_numpy(case.q.view(np.int16))
+    if q_pad_heads:
+        B, T, Hq, D = q.shape
+        big = torch.zeros((B, T, Hq + q_pad_heads, D), dtype=torch.int16)
+        big[:, :, :Hq] = q
+        qd = big.to(device)[:, :, :Hq]
+    else:
+        qd = q.to(device)
+    return dict(q=qd.view(torch.bfloat16), k_cache=cache(case.k_cache), v_cache=cache(case.v_cache),
+                block_table=torch.from_numpy(case.block_table).to(device))

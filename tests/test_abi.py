@@ -1,0 +1,182 @@
+"""CPU checks of the C ABI: the library loads, exports every declared symbol,
+its host planner matches the oracle's independent planner bit for bit, and
+bad arguments come back as status codes (no device is touched)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import split_kv_amd as sk
+from oracle import plan as oplan
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib():
+    try:
+        return sk.load()
+    except RuntimeError as e:
+        pytest.fail(f"library not built: {e}")
+
+
+def test_exports_every_declared_symbol():
+    lib = _lib()
+    header = open(os.path.join(ROOT, "include", "splitkv.h")).read()
+    declared = set(re.findall(r"\b(splitkv_[a-z0-9_]+)\s*\(", header))
+    assert declared, "no declarations parsed"
+    for name in sorted(declared):
+        assert hasattr(lib, name), f"{name} declared in splitkv.h but not exported"
+    assert declared == set(sk.EXPORTED)
+
+
+def test_struct_layouts_match():
+    lib = _lib()
+    assert lib.splitkv_args_size() == ctypes.sizeof(sk.splitkv_args)
+    assert lib.splitkv_plan_args_size() == ctypes.sizeof(sk.splitkv_plan_args)
+
+
+def test_constants_agree_with_oracle():
+    assert sk.SPLITKV_GRANULE == oplan.GRANULE
+    assert sk.SPLITKV_AUTO_MIN_TOKENS == oplan.AUTO_MIN_TOKENS
+    assert sk.SPLITKV_AUTO_WG_PER_CU == oplan.AUTO_WG_PER_CU
+    assert sk.SPLITKV_MAX_SPLITS_LIMIT == oplan.MAX_SPLITS_LIMIT
+    assert sk.SPLITKV_ROWS_PER_WG_GQA == oplan.ROWS_PER_WG_GQA
+    assert sk.SPLITKV_ROWS_PER_WG_MLA == oplan.ROWS_PER_WG_MLA
+    header = open(os.path.join(ROOT, "include", "splitkv.h")).read()
+    for name in ("GRANULE", "AUTO_MIN_TOKENS", "AUTO_WG_PER_CU", "MAX_SPLITS_LIMIT",
+                 "ROWS_PER_WG_GQA", "ROWS_PER_WG_MLA"):
+        m = re.search(rf"#define SPLITKV_{name} (\d+)", header)
+        assert int(m.group(1)) == getattr(sk, f"SPLITKV_{name}")
+
+
+def test_split_range_matches_oracle():
+    _lib()
+    for L in list(range(0, 700)) + [5900, 32000, 65536, 131072]:
+        nblk = max(1, -(-L // 16))
+        for n in (1, 2, 3, 5, 7, 16, 33, 64, 255):
+            if n > nblk:
+                continue
+            for i in range(n):
+                assert sk.splitkv_split_range(L, n, i) == oplan.split_range(L, n, i)
+
+
+def _plan(lens, T, Hq, Hkv, kernel, req, mx, cus):
+    pa = sk.splitkv_plan_args(B=len(lens), T=T, Hq=Hq, Hkv=Hkv, kernel=kernel, requested_splits=req,
+                              max_splits=mx, num_cus=cus)
+    return sk.splitkv_plan(pa, lens)
+
+
+@pytest.mark.parametrize("kernel", [sk.SPLITKV_KERNEL_GQA, sk.SPLITKV_KERNEL_MLA])
+def test_planner_bit_exact_against_oracle(kernel):
+    _lib()
+    rpw = oplan.ROWS_PER_WG_MLA if kernel == sk.SPLITKV_KERNEL_MLA else oplan.ROWS_PER_WG_GQA
+    rng = np.random.default_rng(0)
+    shapes = [(1, 16, 2), (1, 32, 4), (6, 128, 1), (1, 32, 8), (2, 8, 2)]
+    for L in list(range(0, 4097, 37)) + [5900, 32000, 65536, 131072]:
+        for (T, Hq, Hkv) in shapes:
+            for n in (0, 1, 2, 3, 8, 17, 64):
+                for mx in (1, 8, 64, 256):
+                    for cus in (1, 80, 256):
+                        got = _plan([L], T, Hq, Hkv, kernel, n, mx, cus)
+                        ref = oplan.make_plan([L], T=T, Hq=Hq, Hkv=Hkv, requested=n,
+                                              max_splits=mx, num_cus=cus, rows_per_wg=rpw)
+                        for a, b in zip(got, ref):
+                            assert np.array_equal(a, b), (L, T, Hq, Hkv, n, mx, cus)
+    # ragged batches as the ragged workload draws them
+    for seed in range(20):
+        import synth
+        lens = synth.log_uniform_lengths(np.random.default_rng(seed), 32)
+        for n in (0, 1, 4, 16, 64):
+            got = _plan(lens, 1, 32, 8, kernel, n, 64, 256)
+            ref = oplan.make_plan(lens, T=1, Hq=32, Hkv=8, requested=n, max_splits=64,
+                                  num_cus=256, rows_per_wg=rpw)
+            for a, b in zip(got, ref):
+                assert np.array_equal(a, b)
+
+
+def test_requested_count_is_honoured():
+    _lib()
+    for n in range(1, 65):
+        ns, off, seq = _plan([5900], 1, 16, 2, sk.SPLITKV_KERNEL_GQA, n, 64, 256)
+        assert ns[0] == n and off[-1] == n
+
+
+def test_plan_errors():
+    _lib()
+    with pytest.raises(sk.SplitKVError):
+        _plan([10], 1, 16, 3, 0, 1, 64, 256)            # Hq % Hkv != 0
+    with pytest.raises(sk.SplitKVError):
+        _plan([10], 1, 16, 2, 0, 1, 300, 256)           # max_splits above the limit
+    with pytest.raises(sk.SplitKVError):
+        _plan([-1], 1, 16, 2, 0, 1, 64, 256)            # negative length
+    with pytest.raises(sk.SplitKVError):
+        _plan([10], 1, 16, 2, 7, 1, 64, 256)            # unknown kernel
+
+
+def test_workspace_bytes():
+    _lib()
+    S, T, Hq, dv = 13, 2, 16, 256
+    rows = S * T * Hq
+    ml = -(-(2 * rows * 4) // 256) * 256
+    assert sk.splitkv_workspace_bytes(S, T, Hq, dv) == ml + rows * dv * 4
+
+
+def test_validate_block_table():
+    _lib()
+    bt = np.array([[3, 1, 2**31 - 1], [0, 2, 4]], dtype=np.int32)
+    sk.splitkv_validate_block_table(bt, [20, 40], 16, 5)
+    with pytest.raises(sk.SplitKVError):
+        sk.splitkv_validate_block_table(bt, [40, 40], 16, 5)    # reads the padding entry
+    with pytest.raises(sk.SplitKVError):
+        sk.splitkv_validate_block_table(bt, [20, 40], 16, 4)    # page 4 out of range
+
+
+def _args(**over):
+    a = sk.splitkv_args()
+    base = dict(q=0x1000, q_stride_b=16 * 128, q_stride_t=16 * 128, q_stride_h=128,
+                k_cache=0x2000, v_cache=0x3000, k_stride_page=2 * 16 * 128, k_stride_head=16 * 128,
+                k_stride_tok=128, v_stride_page=2 * 16 * 128, v_stride_head=16 * 128,
+                v_stride_tok=128, block_table=0x4000, bt_stride=4, seq_lens=0x5000,
+                num_splits=0x5100, slot_offset=0x5200, slot_seq=0x5300, total_slots=1, B=1, T=1,
+                Hq=16, Hkv=2, d_qk=128, d_v=128, page_size=16, num_pages=4, kv_dtype=0,
+                scale=0.1, k_scale=1.0, v_scale=1.0, workspace=0x6000, workspace_bytes=1 << 20,
+                out=0x7000, out_dtype=0, lse=0x8000, debug=None)
+    base.update(over)
+    for k, v in base.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), sk.SPLITKV_ERR_INVALID_ARG),
+    (dict(Hkv=3), sk.SPLITKV_ERR_INVALID_ARG),
+    (dict(d_qk=96, d_v=96), sk.SPLITKV_ERR_UNSUPPORTED),
+    (dict(page_size=24), sk.SPLITKV_ERR_UNSUPPORTED),
+    (dict(q=0x1008), sk.SPLITKV_ERR_UNSUPPORTED),
+    (dict(k_stride_tok=100), sk.SPLITKV_ERR_UNSUPPORTED),
+    (dict(workspace_bytes=16), sk.SPLITKV_ERR_WORKSPACE),
+    (dict(kv_dtype=1), sk.SPLITKV_ERR_INVALID_ARG),
+    (dict(total_slots=0), sk.SPLITKV_ERR_INVALID_ARG),
+    (dict(scale=0.0), sk.SPLITKV_ERR_INVALID_ARG),
+])
+def test_decode_argument_errors_without_device(over, code):
+    lib = _lib()
+    a = _args(**over)
+    st = lib.splitkv_decode_partial(ctypes.byref(a), None)
+    assert st == code, (st, sk.splitkv_last_error())
+    assert sk.splitkv_last_error()
+
+
+def test_mla_shape_errors_without_device():
+    lib = _lib()
+    a = _args(Hkv=1, d_qk=576, d_v=256, Hq=128, T=6)
+    assert lib.splitkv_mla_decode_partial(ctypes.byref(a), None) == sk.SPLITKV_ERR_UNSUPPORTED
+    a = _args(kv_dtype=1)
+    assert lib.splitkv_decode(ctypes.byref(a), 5, None) == sk.SPLITKV_ERR_INVALID_ARG
+
+
+def test_version_string():
+    _lib()
+    assert sk.splitkv_version()

@@ -1,0 +1,307 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Every workload of the split-KV pages' hot path is covered: tiny GQA (fp32
+out), few KV heads with long context swept over num_splits, batched GQA over
+an e4m3 cache, MLA with six causal tokens, and a ragged batch planned
+automatically.  Small sizes are compared element by element; full sizes are
+compared on sampled rows the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from oracle import plan as oplan
+from tests.gpu_helpers import (assert_close, log, session_for, to_np, tolerances)
+
+pytestmark = pytest.mark.gpu
+
+
+def _need_gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _check_full(case, sess, tag):
+    import torch
+    torch.cuda.synchronize()
+    O, L = oracle.attend(case)
+    atol, rtol = tolerances(case)
+    e1 = assert_close(to_np(sess.out), O, atol, rtol, f"{tag} out")
+    e2 = assert_close(to_np(sess.lse), L, atol, rtol, f"{tag} lse")
+    log(f"  {tag}: out max-abs {e1[0]:.2e} max-rel {e1[1]:.2e}; lse max-abs {e2[0]:.2e}")
+
+
+def _check_rows(case, sess, rows, tag):
+    import torch
+    torch.cuda.synchronize()
+    O, L = oracle.attend(case, select=rows)
+    out = to_np(sess.out)
+    lse = to_np(sess.lse)
+    got = np.stack([out[b, t, h] for (b, t, h) in rows])
+    gl = np.array([lse[b, t, h] for (b, t, h) in rows])
+    atol, rtol = tolerances(case)
+    e1 = assert_close(got, O, atol, rtol, f"{tag} out")
+    assert_close(gl, L, atol, rtol, f"{tag} lse")
+    log(f"  {tag}: {len(rows)} sampled rows, out max-abs {e1[0]:.2e}")
+
+
+def _check_debug(case, sess, Hkv, row_blocks):
+    rec = sess.debug.cpu().numpy()
+    ref = oplan.debug_records(case.seq_lens, case.block_table, case.page_size,
+                              sess.num_splits_host, sess.slot_offset_host, Hkv, row_blocks)
+    assert np.array_equal(rec, ref), "debug records differ from the oracle's integers"
+
+
+# ---------------------------------------------------------------------------
+
+def test_e4m3_widening_every_code_bit_exact():
+    _need_gpu()
+    import torch
+    import split_kv_amd as sk
+    codes = torch.arange(256, dtype=torch.uint8, device="cuda")
+    out = torch.empty(256, dtype=torch.int16, device="cuda")
+    log("e4m3 -> bf16 all 256 codes")
+    sk.splitkv_e4m3_to_bf16(codes.data_ptr(), out.data_ptr(), 256,
+                            torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    got = oracle.decode_bf16(out.cpu().numpy().view(np.uint16))
+    ref = oracle.decode_e4m3(np.arange(256, dtype=np.uint8))
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+    assert same.all(), np.nonzero(~same)
+
+
+@pytest.mark.parametrize("n", [1, 2, 4])
+@pytest.mark.parametrize("mode", ["decode", "partial+combine"])
+def test_tiny_gqa_fp32_out(n, mode):
+    _need_gpu()
+    case = synth.tiny_gqa()
+    log(f"tiny-gqa L=256 seed={case.seed} n={n} {mode}")
+    sess, _ = session_for(case, requested_splits=n)
+    assert sess.total_slots == n
+    if mode == "decode":
+        sess.decode()
+    else:
+        sess.partial()
+        sess.combine()
+    _check_full(case, sess, f"tiny n={n}")
+
+
+@pytest.mark.parametrize("L", [260, 5900])
+def test_few_kv_long_sweep(L):
+    _need_gpu()
+    import torch
+    case = synth.few_kv_long(L=L)
+    O, LSE = oracle.attend(case)
+    outs = {}
+    for n in [1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64]:
+        log(f"few-kv-long L={L} seed={case.seed} n={n}")
+        sess, _ = session_for(case, requested_splits=n, debug=True)
+        assert sess.total_slots == min(n, -(-L // 16))
+        sess.decode()
+        torch.cuda.synchronize()
+        e = assert_close(to_np(sess.out), O, 1e-2, 2e-2, f"L={L} n={n} out")
+        assert_close(to_np(sess.lse), LSE, 1e-2, 2e-2, f"L={L} n={n} lse")
+        _check_debug(case, sess, case.Hkv, 1)
+        rec = sess.debug.cpu().numpy()
+        assert (rec[..., 4] > rec[..., 3]).all(), "a requested split got an empty range"
+        outs[n] = to_np(sess.out)
+        log(f"  max-abs {e[0]:.2e}")
+    # independent of the split count
+    for n, o in outs.items():
+        assert_close(o, outs[1], 2e-2, 4e-2, f"n={n} vs n=1")
+
+
+def test_few_kv_partials_match_oracle_split_emulation():
+    _need_gpu()
+    import torch
+    case = synth.few_kv_long(L=997, seed=77)
+    sess, _ = session_for(case, requested_splits=7)
+    log("few-kv partials L=997 n=7")
+    sess.partial()
+    torch.cuda.synchronize()
+    pm, pl, po = oracle.split_partials(case, sess.num_splits_host, sess.slot_offset_host)
+    gm, gl, go = (to_np(x) for x in sess.partials())
+    assert_close(gm, pm, 1e-4, 1e-4, "part_m")
+    assert_close(gl, pl, 1e-3, 1e-2, "part_l")
+    assert_close(go, po, 1e-2, 2e-2, "part_o")
+
+
+def test_combine_alone_against_oracle_combine():
+    _need_gpu()
+    import torch
+    import split_kv_amd as sk
+    rng = np.random.default_rng(12)
+    case = synth.few_kv_long(L=700, seed=5)
+    sess, _ = session_for(case, requested_splits=9)
+    sess.out_fp32 = True
+    sess.out = torch.empty(sess.out.shape, dtype=torch.float32, device="cuda")
+    sess._build_args()
+    gm, gl, go = sess.partials()
+    S, T, Hq, dv = go.shape
+    m = rng.normal(0, 3, size=(S, T, Hq)).astype(np.float32)
+    m[rng.random(m.shape) < 0.3] = -np.inf              # empty splits
+    m[:, 0, 3] = -np.inf                                # a row that sees nothing
+    l = np.where(np.isinf(m), 0, rng.uniform(0.5, 20, size=m.shape)).astype(np.float32)
+    o = (rng.normal(size=(S, T, Hq, dv)) * l[..., None]).astype(np.float32)
+    o[np.isinf(m)] = 0
+    gm.copy_(torch.from_numpy(m))
+    gl.copy_(torch.from_numpy(l))
+    go.copy_(torch.from_numpy(o))
+    log("combine alone, random partials with -inf rows")
+    sess.combine()
+    torch.cuda.synchronize()
+    Oref, Lref = oracle.combine(m.astype(np.float64), l.astype(np.float64), o.astype(np.float64),
+                                sess.num_splits_host, sess.slot_offset_host)
+    assert_close(to_np(sess.out), Oref, 1e-6, 1e-5, "combine out")
+    assert_close(to_np(sess.lse), Lref, 1e-6, 1e-5, "combine lse")
+    assert (to_np(sess.out)[0, 0, 3] == 0).all() and np.isneginf(to_np(sess.lse)[0, 0, 3])
+
+
+def test_combine_of_one_split_is_identity():
+    _need_gpu()
+    import torch
+    case = synth.few_kv_long(L=300, seed=8)
+    sess, _ = session_for(case, requested_splits=1)
+    sess.out_fp32 = True
+    sess.out = torch.empty(sess.out.shape, dtype=torch.float32, device="cuda")
+    sess._build_args()
+    log("combine(n=1) identity")
+    sess.partial()
+    sess.combine()
+    torch.cuda.synchronize()
+    gm, gl, go = (to_np(x) for x in sess.partials())
+    want = go[0] / gl[0][..., None]
+    got = to_np(sess.out)[0]
+    assert np.allclose(got, want, rtol=3e-7, atol=1e-30)
+    assert np.allclose(to_np(sess.lse)[0], gm[0] + np.log(gl[0]), rtol=1e-6)
+
+
+@pytest.mark.parametrize("n", [1, 2, 8, 0])
+def test_fp8_small_full_compare(n):
+    _need_gpu()
+    case = synth.fp8_batched(B=3, L=3001, seed=31)
+    log(f"fp8 B=3 L=3001 n={n}")
+    sess, _ = session_for(case, requested_splits=n, debug=True)
+    sess.decode()
+    _check_full(case, sess, f"fp8 small n={n}")
+    _check_debug(case, sess, case.Hkv, 1)
+
+
+def test_fp8_clamped_scale():
+    _need_gpu()
+    case = synth.fp8_batched(B=2, L=1500, seed=32, fp8_scale=1 / 128)
+    log("fp8 clamp variant scale=1/128")
+    sess, _ = session_for(case, requested_splits=4)
+    sess.decode()
+    _check_full(case, sess, "fp8 clamp")
+
+
+@pytest.mark.parametrize("n", [1, 4, 8])
+def test_mla_small_full_compare(n):
+    _need_gpu()
+    case = synth.mla_decode(L=2048)
+    log(f"mla L=2048 n={n}")
+    sess, _ = session_for(case, requested_splits=n, debug=True)
+    sess.decode()
+    _check_full(case, sess, f"mla n={n}")
+    _check_debug(case, sess, 1, 12)
+
+
+def test_mla_short_causal_edge():
+    # L = 21: the last split holds keys only the later draft tokens see
+    _need_gpu()
+    case = synth.mla_decode(L=21, seed=9)
+    log("mla L=21 n=2 (empty causal rows)")
+    sess, _ = session_for(case, requested_splits=2)
+    sess.decode()
+    _check_full(case, sess, "mla L=21")
+
+
+@pytest.mark.parametrize("n", [0, 1, 16])
+def test_ragged_small_full_compare(n):
+    _need_gpu()
+    case = synth.ragged(B=32, hi=4096)
+    log(f"ragged B=32 hi=4096 seed={case.seed} n={n}")
+    sess, _ = session_for(case, requested_splits=n, debug=True)
+    sess.decode()
+    _check_full(case, sess, f"ragged n={n}")
+    _check_debug(case, sess, case.Hkv, 1)
+
+
+def test_layouts_and_noncontiguous_query():
+    _need_gpu()
+    case = synth.ragged(B=8, hi=2000, seed=41)
+    log("ragged NHD layout, padded q")
+    sess, _ = session_for(case, requested_splits=3, layout="NHD", q_pad_heads=5)
+    assert not sess.q.is_contiguous()
+    sess.decode()
+    _check_full(case, sess, "NHD + strided q")
+
+
+def test_page_permutation_and_repeat_bit_identical():
+    _need_gpu()
+    import torch
+    case = synth.few_kv_long(L=5900, seed=55)
+    sess, t = session_for(case, requested_splits=16)
+    sess.decode()
+    torch.cuda.synchronize()
+    out1, lse1 = sess.out.clone(), sess.lse.clone()
+    sess.decode()
+    torch.cuda.synchronize()
+    assert torch.equal(out1, sess.out) and torch.equal(lse1, sess.lse), "repeat run differs"
+    # move every page to another physical slot
+    rng = np.random.default_rng(99)
+    perm = rng.permutation(case.num_pages)
+    case2 = synth.few_kv_long(L=5900, seed=55)
+    case2.k_cache = np.empty_like(case.k_cache)
+    case2.v_cache = np.empty_like(case.v_cache)
+    case2.k_cache[perm] = case.k_cache
+    case2.v_cache[perm] = case.v_cache
+    bt = case.block_table.copy()
+    valid = bt != synth.INT32_MAX
+    bt[valid] = perm[bt[valid]]
+    case2.block_table = bt
+    log("page permutation invariance L=5900 n=16")
+    sess2, _ = session_for(case2, requested_splits=16)
+    sess2.decode()
+    torch.cuda.synchronize()
+    assert torch.equal(out1, sess2.out) and torch.equal(lse1, sess2.lse)
+
+
+# ---- full-size workloads, sampled rows -------------------------------------
+
+def test_fp8_full_size_sampled():
+    _need_gpu()
+    case = synth.fp8_batched()
+    log(f"fp8 full B=8 L=32000 auto plan")
+    sess, _ = session_for(case, requested_splits=0)
+    log(f"  plan: splits {sess.num_splits_host.tolist()}")
+    sess.decode()
+    rows = [(b, 0, h) for b in (0, 3, 7) for h in (0, 9, 31)]
+    _check_rows(case, sess, rows, "fp8 full")
+
+
+@pytest.mark.parametrize("n", [1, 4, 8])
+def test_mla_full_size_sampled(n):
+    _need_gpu()
+    case = synth.mla_decode(L=65536)
+    log(f"mla full L=65536 n={n}")
+    sess, _ = session_for(case, requested_splits=n)
+    sess.decode()
+    rows = [(0, t, h) for t in (0, 5) for h in (0, 77, 127)] + [(0, 3, 64)]
+    _check_rows(case, sess, rows, f"mla full n={n}")
+
+
+def test_ragged_full_size_sampled():
+    _need_gpu()
+    case = synth.ragged()
+    log(f"ragged full B=32 seed={case.seed}, sum L={int(case.seq_lens.sum())}")
+    sess, _ = session_for(case, requested_splits=0, debug=True)
+    log(f"  plan total slots {sess.total_slots}")
+    sess.decode()
+    _check_debug(case, sess, case.Hkv, 1)
+    bmax = int(np.argmax(case.seq_lens))
+    rows = [(b, 0, h) for b in (0, 2, 4, bmax) for h in (0, 13, 31)]
+    _check_rows(case, sess, rows, "ragged full")
