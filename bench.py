@@ -39,8 +39,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--L", type=int, default=5900)
-    ap.add_argument("--sweep", type=str, default="1,2,3,4,6,8,12,16,24,32,48,64",
-                    help="comma-separated num_splits to sweep ('' to skip)")
+    ap.add_argument("--sweep", type=str, default="1,2,3,4,6,8,12,16,24,32,48,64,96,128,192,256",
+                    help="comma-separated num_splits to sweep ('' to skip); the workload's own "
+                         "sweep is 1..64, larger counts are extra points")
     ap.add_argument("--only", type=int, default=None,
                     help="time one split count only (0 = auto); for profiler runs")
     ap.add_argument("--warm-cache", action="store_true", help="reuse one page pool copy")
@@ -146,7 +147,7 @@ def main():
     def session(n):
         t0 = time.perf_counter()
         s = DecodeSession(q=q, k_cache=k, v_cache=v, block_table=bts[0], seq_lens=case.seq_lens,
-                          scale=case.scale, requested_splits=n, max_splits=64)
+                          scale=case.scale, requested_splits=n, max_splits=256)
         return s, (time.perf_counter() - t0) * 1e6
 
     if args.only is not None:

@@ -117,13 +117,16 @@ typedef struct {
  * L == 0 gives one empty split.
  *
  * Outputs (all host): num_splits[B]; slot_offset[B+1] (exclusive prefix
- * sum); slot_seq[S] with slot_seq[slot_offset[b] + i] = b*256 + i, written
- * only if slot_seq_host is not NULL and S <= slot_seq_capacity (else
- * SPLITKV_ERR_INVALID_ARG); *total_slots = S.  B * max_splits always bounds S.
+ * sum); slot_info[S][4], the work record of slot s = slot_offset[b] + i:
+ *   { b, (num_splits[b] << 16) | i, start, end }
+ * so a workgroup learns its sequence, split and token range [start, end)
+ * with one load.  slot_info is written only if slot_info_host is not NULL and
+ * S <= slot_info_capacity (in slots; else SPLITKV_ERR_INVALID_ARG);
+ * *total_slots = S.  B * max_splits always bounds S.
  */
 splitkv_status splitkv_plan(const splitkv_plan_args* args, const int32_t* seq_lens_host,
                             int32_t* num_splits_host, int32_t* slot_offset_host,
-                            int32_t* slot_seq_host, int32_t slot_seq_capacity,
+                            int32_t* slot_info_host, int32_t slot_info_capacity,
                             int32_t* total_slots);
 
 /* Token range [*s, *e) of split i of n for a sequence of L tokens (host; same formula as the kernels). */
@@ -145,7 +148,7 @@ typedef struct {
   const int32_t* seq_lens;         /* [B] */
   const int32_t* num_splits;       /* [B]   from splitkv_plan, on the device */
   const int32_t* slot_offset;      /* [B+1] */
-  const int32_t* slot_seq;         /* [S] */
+  const int32_t* slot_info;        /* [S][4] */
   int32_t total_slots;             /* S, the host value splitkv_plan returned */
   int32_t B, T, Hq, Hkv, d_qk, d_v, page_size, num_pages;
   int32_t kv_dtype;                /* SPLITKV_KV_BF16 or SPLITKV_KV_E4M3 */

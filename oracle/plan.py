@@ -65,10 +65,10 @@ def clamp_request(L: int, n: int, max_splits: int) -> int:
 
 def make_plan(seq_lens, *, T: int, Hq: int, Hkv: int, requested: int, max_splits: int,
               num_cus: int, rows_per_wg: int):
-    """Return (num_splits[B], slot_offset[B+1], slot_seq[S]) as int32 arrays.
+    """Return (num_splits[B], slot_offset[B+1], slot_info[S, 4]) as int32 arrays.
 
-    ``slot_seq[s]`` packs the (sequence, split) pair that workgroup slot ``s``
-    serves as ``b * MAX_SPLITS_LIMIT + i``.
+    ``slot_info[s]`` is the work record of slot ``s`` (split ``i`` of sequence
+    ``b``): ``(b, (n_b << 16) | i, start, end)`` with [start, end) its range.
     """
     L = [int(x) for x in seq_lens]
     B = len(L)
@@ -84,12 +84,13 @@ def make_plan(seq_lens, *, T: int, Hq: int, Hkv: int, requested: int, max_splits
     off = [0]
     for n in ns:
         off.append(off[-1] + n)
-    seq = []
+    info = []
     for b, n in enumerate(ns):
         for i in range(n):
-            seq.append(b * MAX_SPLITS_LIMIT + i)
+            s, e = split_range(L[b], n, i)
+            info.append((b, (n << 16) | i, s, e))
     return (np.array(ns, dtype=np.int32), np.array(off, dtype=np.int32),
-            np.array(seq, dtype=np.int32))
+            np.array(info, dtype=np.int32).reshape(-1, 4))
 
 
 def debug_records(seq_lens, block_table, page_size, num_splits, slot_offset, Hkv, row_blocks):

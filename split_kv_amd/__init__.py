@@ -58,7 +58,7 @@ class splitkv_args(ctypes.Structure):
         ("k_stride_page", c_i64), ("k_stride_head", c_i64), ("k_stride_tok", c_i64),
         ("v_stride_page", c_i64), ("v_stride_head", c_i64), ("v_stride_tok", c_i64),
         ("block_table", c_vp), ("bt_stride", c_i64),
-        ("seq_lens", c_vp), ("num_splits", c_vp), ("slot_offset", c_vp), ("slot_seq", c_vp),
+        ("seq_lens", c_vp), ("num_splits", c_vp), ("slot_offset", c_vp), ("slot_info", c_vp),
         ("total_slots", c_i32),
         ("B", c_i32), ("T", c_i32), ("Hq", c_i32), ("Hkv", c_i32), ("d_qk", c_i32), ("d_v", c_i32),
         ("page_size", c_i32), ("num_pages", c_i32), ("kv_dtype", c_i32),
@@ -141,7 +141,7 @@ def splitkv_version() -> str:
 
 
 def splitkv_plan(args: splitkv_plan_args, seq_lens):
-    """Host planner -> (num_splits[B], slot_offset[B+1], slot_seq[S]) as int32 numpy arrays."""
+    """Host planner -> (num_splits[B], slot_offset[B+1], slot_info[S, 4]) as int32 numpy arrays."""
     lib = load()
     lens = _i32(seq_lens)
     B = int(args.B)
@@ -150,12 +150,12 @@ def splitkv_plan(args: splitkv_plan_args, seq_lens):
     ns = np.zeros(B, np.int32)
     off = np.zeros(B + 1, np.int32)
     cap = max(1, B * max(1, int(args.max_splits)))
-    seq = np.zeros(cap, np.int32)
+    info = np.zeros((cap, 4), np.int32)
     total = c_i32(0)
     st = lib.splitkv_plan(ctypes.byref(args), lens.ctypes.data, ns.ctypes.data, off.ctypes.data,
-                          seq.ctypes.data, cap, ctypes.byref(total))
+                          info.ctypes.data, cap, ctypes.byref(total))
     _check("splitkv_plan", st)
-    return ns, off, seq[:total.value].copy()
+    return ns, off, info[:total.value].copy()
 
 
 def splitkv_split_range(L: int, n: int, i: int):

@@ -46,9 +46,18 @@ def sources():
                   if f.endswith(".hip") or f.endswith(".cpp"))
 
 
+# Per-source code-generation options.  The grouped-query kernel rescales its
+# MFMA accumulators with vector ALU code; keeping them in VGPRs (instead of the
+# accumulation registers) avoids copying them across on every group.
+PER_FILE = {
+    "gqa.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
+}
+
+
 def _compile(src: str, rev: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, f'-DSPLITKV_REVISION="{rev}"', "-c", src, "-o", obj]
+    extra = PER_FILE.get(os.path.basename(src), [])
+    cmd = [HIPCC, *FLAGS, *extra, f'-DSPLITKV_REVISION="{rev}"', "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -94,8 +94,9 @@ splitkv_status check_partial(const splitkv_args* a, Kind kind, bool need_ws, con
                              int* row_blocks) {
   splitkv_status st = check_common(a, fn);
   if (st != SPLITKV_OK) return st;
-  if (!a->q || !a->k_cache || !a->block_table || !a->slot_seq)
-    return fail(SPLITKV_ERR_INVALID_ARG, "%s: null q, k_cache, block_table or slot_seq", fn);
+  if (!a->q || !a->k_cache || !a->block_table || !a->slot_info)
+    return fail(SPLITKV_ERR_INVALID_ARG, "%s: null q, k_cache, block_table or slot_info", fn);
+  if (!aligned(a->slot_info, 16)) return fail(SPLITKV_ERR_INVALID_ARG, "%s: slot_info misaligned", fn);
   if (kind != Kind::Mla && !a->v_cache) return fail(SPLITKV_ERR_INVALID_ARG, "%s: null v_cache", fn);
   if (a->page_size < 16 || a->page_size % SPLITKV_GRANULE != 0)
     return fail(SPLITKV_ERR_UNSUPPORTED, "%s: page_size=%d must be a positive multiple of 16", fn,
@@ -164,7 +165,7 @@ PartialParams make_partial_params(const splitkv_args& a, Kind kind, int row_bloc
   p.seq_lens = a.seq_lens;
   p.num_splits = a.num_splits;
   p.slot_offset = a.slot_offset;
-  p.slot_seq = a.slot_seq;
+  p.slot_info = a.slot_info;
   p.T = a.T;
   p.Hq = a.Hq;
   p.Hkv = a.Hkv;
@@ -173,6 +174,7 @@ PartialParams make_partial_params(const splitkv_args& a, Kind kind, int row_bloc
   p.rows = kind == Kind::Mla ? a.T * a.Hq : p.g * a.T;
   p.row_blocks = row_blocks;
   p.total_wg = a.total_slots * a.Hkv * row_blocks;
+  p.page_shift = (a.page_size & (a.page_size - 1)) == 0 ? __builtin_ctz(unsigned(a.page_size)) : -1;
   p.scale_log2 = a.scale * a.k_scale * kLog2e;
   p.v_scale = a.v_scale;
   const Layout w = workspace_layout(a);
@@ -244,7 +246,7 @@ extern "C" {
 
 splitkv_status splitkv_plan(const splitkv_plan_args* args, const int32_t* seq_lens_host,
                             int32_t* num_splits_host, int32_t* slot_offset_host,
-                            int32_t* slot_seq_host, int32_t slot_seq_capacity,
+                            int32_t* slot_info_host, int32_t slot_info_capacity,
                             int32_t* total_slots) {
   if (!args) return fail(SPLITKV_ERR_INVALID_ARG, "splitkv_plan: null args");
   int cus = args->num_cus;
@@ -254,8 +256,8 @@ splitkv_status splitkv_plan(const splitkv_plan_args* args, const int32_t* seq_le
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return fail(SPLITKV_ERR_DEVICE, "splitkv_plan: cannot query the compute-unit count");
   }
-  return plan_host(*args, cus, seq_lens_host, num_splits_host, slot_offset_host, slot_seq_host,
-                   slot_seq_capacity, total_slots);
+  return plan_host(*args, cus, seq_lens_host, num_splits_host, slot_offset_host, slot_info_host,
+                   slot_info_capacity, total_slots);
 }
 
 splitkv_status splitkv_decode_partial(const splitkv_args* args, void* stream) {

@@ -9,75 +9,99 @@
 // the split count ("Shipped: 484.5 tok/s on one GB300 ...", section "Why 8
 // splits lost"): it reads S * rows * (d_v + 2) * 4 bytes of partials.
 //
-// One wave per output row (b, t, h); lanes span the d_v features so every
-// partial row is one coalesced read.
+// A row's d_v features are split over workgroups of 64 features each, and a
+// workgroup's 256 threads are 16 float4 columns x 16 groups over splits, so
+// that at decode sizes every load of the row is in flight at once (the kernel
+// is latency-bound): each thread loads m, l and one float4 of o for each of
+// its splits, eight at a time, merges them against its own running max, and
+// the groups are merged through LDS (the same rescaling as across splits).
 #include "device.h"
 
 namespace splitkv {
 
-template <int DV>
-__global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
-  constexpr int VEC = DV / 64;          // features per lane: 2, 4 or 8
-  const int lane = threadIdx.x & 63;
-  const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (row >= int64_t(p.B) * p.R) return;
+constexpr int kCombineCols = 16;                // float4 columns per workgroup (64 features)
+constexpr int kCombineGroups = 256 / kCombineCols;
+
+__global__ __launch_bounds__(256) void combine_kernel(CombineParams p, int dsplit) {
+  constexpr int CH = kCombineCols, G = kCombineGroups, U = 8;
+  __shared__ float red_m[G][CH], red_l[G][CH];
+  __shared__ f32x4 red_o[G][CH];
+
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x / dsplit;
+  const int part = blockIdx.x % dsplit;
   const int b = int(row / p.R);
   const int64_t rix = row % p.R;
   const int n = p.num_splits[b];
   if (p.skip_single && n == 1) return;
   const int64_t base = p.slot_offset[b];
+  const int c = tid % CH, g = tid / CH;
+  const int DV = p.d_v;
 
-  float M = -INFINITY;
-  for (int i = lane; i < n; i += 64) M = fmaxf(M, p.part_m[(base + i) * p.R + rix]);
-  M = wave_max(M);
-  float lam = 0.f;
-  for (int i = lane; i < n; i += 64) {
-    const float mi = p.part_m[(base + i) * p.R + rix];
-    if (mi != -INFINITY) lam += expf(mi - M) * p.part_l[(base + i) * p.R + rix];
-  }
-  lam = wave_sum(lam);
-
-  float acc[VEC];
+  float M = -INFINITY, lam = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const float* po = p.part_o + rix * DV + 64 * part + 4 * c;
+  const int64_t step = int64_t(p.R) * DV;
+  for (int i0 = g; i0 < n; i0 += U * G) {
+    float mi[U], li[U];
+    f32x4 oi[U];
 #pragma unroll
-  for (int k = 0; k < VEC; ++k) acc[k] = 0.f;
-  if (M != -INFINITY) {
-    for (int i = 0; i < n; ++i) {
-      const float mi = p.part_m[(base + i) * p.R + rix];
-      if (mi == -INFINITY) continue;
-      const float w = expf(mi - M);
-      const float* src = p.part_o + ((base + i) * p.R + rix) * DV + lane * VEC;
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * G;
+      const int64_t sl = base + (i < n ? i : i0);   // past the end: reread a valid slot, weight 0
+      mi[u] = p.part_m[sl * p.R + rix];
+      li[u] = p.part_l[sl * p.R + rix];
+      oi[u] = *reinterpret_cast<const f32x4*>(po + sl * step);
+      if (i >= n) mi[u] = -INFINITY;
+    }
 #pragma unroll
-      for (int k = 0; k < VEC; k += 2) {
-        const float2 v = *reinterpret_cast<const float2*>(src + k);
-        acc[k] += w * v.x;
-        acc[k + 1] += w * v.y;
-      }
+    for (int u = 0; u < U; ++u) {
+      if (mi[u] == -INFINITY) continue;                  // empty split: zero weight
+      const float Mn = fmaxf(M, mi[u]);
+      const float a = M == -INFINITY ? 0.f : expf(M - Mn);
+      const float w = expf(mi[u] - Mn);
+      lam = lam * a + w * li[u];
+      acc = acc * a + w * oi[u];
+      M = Mn;
     }
   }
-  const bool ok = M != -INFINITY && lam > 0.f;
-  const float inv = ok ? 1.f / lam : 0.f;
-  const int64_t o = row * DV + lane * VEC;
-  if (p.out_f32) {
-    float* dst = static_cast<float*>(p.out) + o;
+  red_m[g][c] = M;
+  red_l[g][c] = lam;
+  red_o[g][c] = acc;
+  __syncthreads();
+  if (g == 0) {
+    float Mt = red_m[0][c];
 #pragma unroll
-    for (int k = 0; k < VEC; ++k) dst[k] = acc[k] * inv;
-  } else {
-    uint32_t* dst = reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(p.out) + o);
+    for (int k = 1; k < G; ++k) Mt = fmaxf(Mt, red_m[k][c]);
+    float lt = 0.f;
+    f32x4 ot = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 0; k < VEC; k += 2) dst[k / 2] = pack_bf16x2(acc[k] * inv, acc[k + 1] * inv);
+    for (int k = 0; k < G; ++k) {
+      const float mk = red_m[k][c];
+      if (mk == -INFINITY) continue;
+      const float w = expf(mk - Mt);
+      lt += w * red_l[k][c];
+      ot += w * red_o[k][c];
+    }
+    const bool ok = Mt != -INFINITY && lt > 0.f;
+    ot *= ok ? 1.f / lt : 0.f;
+    const int64_t o = row * DV + 64 * part + 4 * c;
+    if (p.out_f32) {
+      *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + o) = ot;
+    } else {
+      u32x2 pk = {pack_bf16x2(ot[0], ot[1]), pack_bf16x2(ot[2], ot[3])};
+      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + o) = pk;
+    }
+    if (p.lse && part == 0 && c == 0) p.lse[row] = ok ? Mt + logf(lt) : -INFINITY;
   }
-  if (p.lse && lane == 0) p.lse[row] = ok ? M + logf(lam) : -INFINITY;
 }
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
-  const int64_t rows = int64_t(p.B) * p.R;
-  const dim3 grid(unsigned((rows + 3) / 4)), block(256);
-  switch (p.d_v) {
-    case 128: hipLaunchKernelGGL(combine_kernel<128>, grid, block, 0, stream, p); break;
-    case 256: hipLaunchKernelGGL(combine_kernel<256>, grid, block, 0, stream, p); break;
-    case 512: hipLaunchKernelGGL(combine_kernel<512>, grid, block, 0, stream, p); break;
-    default: return hipErrorInvalidValue;
-  }
+  if (p.d_v % 64 != 0) return hipErrorInvalidValue;
+  const int dsplit = p.d_v / 64;
+  const int64_t wgs = int64_t(p.B) * p.R * dsplit;
+  const dim3 grid(static_cast<unsigned>(wgs)), block(256);
+  hipLaunchKernelGGL(combine_kernel, grid, block, 0, stream, p, dsplit);
   return hipGetLastError();
 }
 

@@ -9,6 +9,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "splitkv.h"
+
 namespace splitkv {
 
 typedef short bf16x8 __attribute__((ext_vector_type(8)));
@@ -33,8 +35,9 @@ struct PartialParams {
   const int32_t* seq_lens;
   const int32_t* num_splits;
   const int32_t* slot_offset;
-  const int32_t* slot_seq;
+  const int32_t* slot_info;     // [S][4]: b, (n << 16) | split, start, end
   int32_t T, Hq, Hkv, g, page_size, rows, row_blocks, total_wg;
+  int32_t page_shift;           // log2(page_size) when it is a power of two, else -1
   float scale_log2;             // scale * k_scale * log2(e)
   float v_scale;
   float* part_m;                // [S][T*Hq]
@@ -60,8 +63,14 @@ struct CombineParams {
   int32_t skip_single;          // rows of single-split sequences were written by the partial kernel
 };
 
+typedef short bf16x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma16x16x16(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
 // Round an fp32 value to bfloat16 (round to nearest even; NaN stays NaN).
@@ -92,6 +101,26 @@ __device__ __forceinline__ float xor_shfl(float v, int mask) {
   return __shfl_xor(v, mask, 64);
 }
 
+// Max over the four lanes {l, l^16, l^32, l^48} (one MFMA output column),
+// with the gfx950 lane-swap instructions instead of an LDS round trip.
+__device__ __forceinline__ float column_max4(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float column_sum4(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// 2^x with the hardware instruction (no denormal range reduction; the
+// arguments here are <= 8 and tiny results may flush to zero).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
@@ -104,12 +133,22 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Split i of n over L tokens, in 16-token granules: [s, e).
-__device__ __forceinline__ void split_bounds(int L, int n, int i, int* s, int* e) {
-  const int64_t nblk = (L + 15) >> 4;
-  *s = 16 * (int)((int64_t(i) * nblk) / n);
-  const int hi = 16 * (int)((int64_t(i + 1) * nblk) / n);
-  *e = hi < L ? hi : L;
+// Work record of one slot, read through the scalar cache in one load.
+struct SlotWork {
+  int b, split, nsplit, s, e;
+};
+
+typedef const __attribute__((address_space(4))) int32_t cint32;
+
+__device__ __forceinline__ SlotWork load_slot(const int32_t* slot_info, int slot) {
+  cint32* r = (cint32*)slot_info + 4 * slot;
+  SlotWork w;
+  w.b = r[0];
+  w.split = r[1] & 0xffff;
+  w.nsplit = r[1] >> 16;
+  w.s = r[2];
+  w.e = r[3];
+  return w;
 }
 
 template <typename T>

@@ -26,7 +26,7 @@ inline void split_range(int64_t L, int64_t n, int64_t i, int64_t* s, int64_t* e)
 
 // Pure host planner (no device queries).
 splitkv_status plan_host(const splitkv_plan_args& a, int32_t num_cus, const int32_t* seq_lens,
-                         int32_t* num_splits, int32_t* slot_offset, int32_t* slot_seq,
-                         int32_t slot_seq_capacity, int32_t* total_slots);
+                         int32_t* num_splits, int32_t* slot_offset, int32_t* slot_info,
+                         int32_t slot_info_capacity, int32_t* total_slots);
 
 }  // namespace splitkv

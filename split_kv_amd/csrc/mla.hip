@@ -64,12 +64,9 @@ __global__ __launch_bounds__(256) void mla_partial_kernel(PartialParams p, int p
   const int wave = uniform(tid >> 6);
   const int n16 = lane & 15, qg = lane >> 4;
 
-  const int packed = p.slot_seq[slot];
-  const int b = packed >> 8, split = packed & 255;
-  const int L = p.seq_lens[b];
-  const int nsplit = p.num_splits[b];
-  int s, e;
-  split_bounds(L, nsplit, split, &s, &e);
+  const SlotWork work = load_slot(p.slot_info, slot);
+  const int b = work.b, split = work.split, nsplit = work.nsplit, s = work.s, e = work.e;
+  const int L = ((cint32*)p.seq_lens)[b];
 
   const int row = rb * 64 + wave * 16 + n16;   // row = t * Hq + h
   const bool row_ok = row < p.rows;

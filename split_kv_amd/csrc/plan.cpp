@@ -38,8 +38,8 @@ static int32_t clamp_request(int64_t L, int64_t n, int64_t max_splits) {
 }
 
 splitkv_status plan_host(const splitkv_plan_args& a, int32_t num_cus, const int32_t* seq_lens,
-                         int32_t* num_splits, int32_t* slot_offset, int32_t* slot_seq,
-                         int32_t slot_seq_capacity, int32_t* total_slots) {
+                         int32_t* num_splits, int32_t* slot_offset, int32_t* slot_info,
+                         int32_t slot_info_capacity, int32_t* total_slots) {
   if (!seq_lens || !num_splits || !slot_offset || !total_slots)
     return fail(SPLITKV_ERR_INVALID_ARG, "splitkv_plan: null output or seq_lens pointer");
   if (a.B < 1 || a.T < 1 || a.Hq < 1 || a.Hkv < 1 || a.Hq % a.Hkv != 0)
@@ -81,14 +81,21 @@ splitkv_status plan_host(const splitkv_plan_args& a, int32_t num_cus, const int3
     slot_offset[b + 1] = static_cast<int32_t>(off);
   }
   *total_slots = static_cast<int32_t>(off);
-  if (slot_seq) {
-    if (off > slot_seq_capacity)
+  if (slot_info) {
+    if (off > slot_info_capacity)
       return fail(SPLITKV_ERR_INVALID_ARG,
-                  "splitkv_plan: slot_seq capacity %d < %lld slots", slot_seq_capacity,
+                  "splitkv_plan: slot_info capacity %d < %lld slots", slot_info_capacity,
                   static_cast<long long>(off));
     for (int32_t b = 0; b < a.B; ++b)
-      for (int32_t i = 0; i < num_splits[b]; ++i)
-        slot_seq[slot_offset[b] + i] = b * SPLITKV_MAX_SPLITS_LIMIT + i;
+      for (int32_t i = 0; i < num_splits[b]; ++i) {
+        int64_t s, e;
+        split_range(seq_lens[b], num_splits[b], i, &s, &e);
+        int32_t* r = slot_info + 4 * int64_t(slot_offset[b] + i);
+        r[0] = b;
+        r[1] = (num_splits[b] << 16) | i;
+        r[2] = static_cast<int32_t>(s);
+        r[3] = static_cast<int32_t>(e);
+      }
   }
   return SPLITKV_OK;
 }

@@ -70,13 +70,13 @@ class DecodeSession:
         pa = splitkv_plan_args(B=s["B"], T=s["T"], Hq=s["Hq"], Hkv=s["Hkv"], kernel=self.kernel,
                                requested_splits=requested_splits, max_splits=self.max_splits,
                                num_cus=self.num_cus)
-        ns, off, seq = splitkv_plan(pa, self.seq_lens_host)
+        ns, off, info = splitkv_plan(pa, self.seq_lens_host)
         self.requested_splits = requested_splits
-        self.num_splits_host, self.slot_offset_host, self.slot_seq_host = ns, off, seq
+        self.num_splits_host, self.slot_offset_host, self.slot_info_host = ns, off, info
         dev = self.q.device
         self.num_splits = torch.as_tensor(ns, device=dev)
         self.slot_offset = torch.as_tensor(off, device=dev)
-        self.slot_seq = torch.as_tensor(seq, device=dev)
+        self.slot_info = torch.as_tensor(info, device=dev)
         self.total_slots = int(off[-1])
         nbytes = splitkv_workspace_bytes(self.total_slots, s["T"], s["Hq"], s["d_v"])
         self.workspace = torch.empty((nbytes + 3) // 4, dtype=torch.float32, device=dev)
@@ -106,7 +106,7 @@ class DecodeSession:
         a.seq_lens = self.seq_lens.data_ptr()
         a.num_splits = self.num_splits.data_ptr()
         a.slot_offset = self.slot_offset.data_ptr()
-        a.slot_seq = self.slot_seq.data_ptr()
+        a.slot_info = self.slot_info.data_ptr()
         a.total_slots = self.total_slots
         a.B, a.T, a.Hq, a.Hkv = s["B"], s["T"], s["Hq"], s["Hkv"]
         a.d_qk, a.d_v, a.page_size, a.num_pages = s["d_qk"], s["d_v"], s["P"], s["num_pages"]

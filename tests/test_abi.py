@@ -139,7 +139,7 @@ def _args(**over):
                 k_cache=0x2000, v_cache=0x3000, k_stride_page=2 * 16 * 128, k_stride_head=16 * 128,
                 k_stride_tok=128, v_stride_page=2 * 16 * 128, v_stride_head=16 * 128,
                 v_stride_tok=128, block_table=0x4000, bt_stride=4, seq_lens=0x5000,
-                num_splits=0x5100, slot_offset=0x5200, slot_seq=0x5300, total_slots=1, B=1, T=1,
+                num_splits=0x5100, slot_offset=0x5200, slot_info=0x5300, total_slots=1, B=1, T=1,
                 Hq=16, Hkv=2, d_qk=128, d_v=128, page_size=16, num_pages=4, kv_dtype=0,
                 scale=0.1, k_scale=1.0, v_scale=1.0, workspace=0x6000, workspace_bytes=1 << 20,
                 out=0x7000, out_dtype=0, lse=0x8000, debug=None)

@@ -49,11 +49,12 @@ def test_request_is_honoured_exactly():
     for L in (17, 260, 5900):
         nblk = -(-L // 16)
         for n in range(1, 65):
-            ns, off, seq = P.make_plan([L], T=1, Hq=16, Hkv=2, requested=n, max_splits=64,
-                                       num_cus=256, rows_per_wg=16)
+            ns, off, info = P.make_plan([L], T=1, Hq=16, Hkv=2, requested=n, max_splits=64,
+                                        num_cus=256, rows_per_wg=16)
             assert ns[0] == min(n, nblk)
             assert off.tolist() == [0, ns[0]]
-            assert seq.tolist() == list(range(ns[0]))
+            assert [r[1] & 0xffff for r in info] == list(range(ns[0]))
+            assert all(r[3] > r[2] for r in info)
 
 
 def test_clamps():
@@ -74,12 +75,14 @@ def test_auto_plan_targets_two_wg_per_cu():
     ns, _, _ = P.make_plan([100, 300, 600], T=1, Hq=8, Hkv=2, requested=0, max_splits=64,
                            num_cus=256, rows_per_wg=16)
     assert ns.tolist() == [1, 2, 3]               # chunk = AUTO_MIN_TOKENS = 256
-    # slot_seq packs (b, i)
-    ns, off, seq = P.make_plan([40, 5000], T=1, Hq=8, Hkv=2, requested=3, max_splits=64,
-                               num_cus=256, rows_per_wg=16)
+    # slot_info holds (b, n << 16 | i, start, end)
+    ns, off, info = P.make_plan([40, 5000], T=1, Hq=8, Hkv=2, requested=3, max_splits=64,
+                                num_cus=256, rows_per_wg=16)
     assert ns.tolist() == [3, 3] and off.tolist() == [0, 3, 6]
-    assert [(s // P.MAX_SPLITS_LIMIT, s % P.MAX_SPLITS_LIMIT) for s in seq] == \
-        [(0, 0), (0, 1), (0, 2), (1, 0), (1, 1), (1, 2)]
+    assert [(r[0], r[1] >> 16, r[1] & 0xffff) for r in info] == \
+        [(0, 3, 0), (0, 3, 1), (0, 3, 2), (1, 3, 0), (1, 3, 1), (1, 3, 2)]
+    assert [tuple(r[2:]) for r in info] == [(0, 16), (16, 32), (32, 40),
+                                            (0, 1664), (1664, 3328), (3328, 5000)]
 
 
 def test_debug_records_brute_force():
