@@ -30,7 +30,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 METRIC = "decode-attention µs/step and KV GB/s (% of HBM peak) vs num_splits"
+
+
+def parse_defaults():
+    return {"sweep": "1,2,3,4,6,8,12,16,24,32,48,64,96,128,192,256"}
 
 
 def parse():
@@ -38,7 +43,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--L", type=int, default=5900)
+    ap.add_argument("--workload", default="few-kv-long",
+                    choices=["few-kv-long", "fp8-batched", "mla", "ragged", "tiny-gqa"],
+                    help="few-kv-long is the headline; the others are extra measurements")
+    ap.add_argument("--L", type=int, default=None, help="sequence length (few-kv-long, mla)")
     ap.add_argument("--sweep", type=str, default="1,2,3,4,6,8,12,16,24,32,48,64,96,128,192,256",
                     help="comma-separated num_splits to sweep ('' to skip); the workload's own "
                          "sweep is 1..64, larger counts are extra points")
@@ -50,16 +58,44 @@ def parse():
     return ap.parse_args()
 
 
+def make_workload(name, L):
+    import synth
+    if name == "few-kv-long":
+        return synth.few_kv_long(L=L or 5900, seed=1002)
+    if name == "fp8-batched":
+        return synth.fp8_batched()
+    if name == "mla":
+        return synth.mla_decode(L=L or 65536)
+    if name == "ragged":
+        return synth.ragged()
+    return synth.tiny_gqa()
+
+
+def describe(case, name):
+    if name == "few-kv-long":
+        return (f"few-KV-head long-context decode: B=1 T=1 Hq=16 Hkv=2 D=256 L={int(case.seq_lens[0])} "
+                f"bf16 paged (P=16, permuted)")
+    if name == "fp8-batched":
+        return "batched GQA decode, e4m3 KV: B=8 T=1 Hq=32 Hkv=4 D=128 L=32000 P=16, bf16 Q"
+    if name == "mla":
+        return f"MLA decode: B=1 T=6 Hq=128 latent 576/512 L={int(case.seq_lens[0])} P=64 bf16"
+    if name == "ragged":
+        return f"ragged GQA decode: B=32 Hq=32 Hkv=8 D=128 bf16 P=16, sum L={int(case.seq_lens.sum())}"
+    return "tiny GQA decode: B=1 T=1 Hq=8 Hkv=2 D=128 L=256 contiguous bf16, fp32 out"
+
+
 def cold_copies(case, device, warm):
     """Replicate the page pool R times (>= 1 GiB total) with per-copy block tables."""
     import numpy as np
     import torch
     import synth
     t = synth.to_torch(case, device)
-    pool = case.k_cache.nbytes + case.v_cache.nbytes
+    pool = case.k_cache.nbytes + (case.v_cache.nbytes if case.v_cache is not None else 0)
     R = 1 if warm else max(1, math.ceil((1 << 30) / pool))
     k = t["k_cache"].repeat(R, 1, 1, 1) if R > 1 else t["k_cache"]
-    v = t["v_cache"].repeat(R, 1, 1, 1) if R > 1 else t["v_cache"]
+    v = t["v_cache"]
+    if v is not None and R > 1:
+        v = v.repeat(R, 1, 1, 1)
     bt = case.block_table
     valid = bt != synth.INT32_MAX
     tables = []
@@ -179,18 +215,23 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
-    case = synth.few_kv_long(L=args.L, seed=1002)
+    case = make_workload(args.workload, args.L)
+    headline = args.workload == "few-kv-long"
     q, k, v, bts, R = cold_copies(case, dev, args.warm_cache)
     kv_bytes = case.kv_bytes()
 
     def session(n):
         t0 = time.perf_counter()
         s = DecodeSession(q=q, k_cache=k, v_cache=v, block_table=bts[0], seq_lens=case.seq_lens,
-                          scale=case.scale, requested_splits=n, max_splits=256)
+                          scale=case.scale, k_scale=case.k_scale, v_scale=case.v_scale,
+                          mla=case.mla, requested_splits=n, max_splits=256,
+                          out_fp32=case.out_fp32)
         return s, (time.perf_counter() - t0) * 1e6
 
     if args.only is not None:
         counts = [args.only]
+    elif not headline and args.sweep == parse_defaults()["sweep"]:
+        counts = [0, 1, 4, 8, 16]
     else:
         counts = [0] + [int(x) for x in args.sweep.split(",") if x.strip()]
     sweep = []
@@ -199,7 +240,8 @@ def main():
         sess, plan_us = session(n)
         eager_us = time_steps(sess, bts, R, args.steps, args.warmup, stream)
         us = time_steps_graph(sess, bts, R, args.steps, args.warmup)
-        rec = {"num_splits_requested": n, "num_splits": int(sess.num_splits_host[0]),
+        rec = {"num_splits_requested": n, "num_splits": int(sess.num_splits_host.max()),
+               "total_slots": sess.total_slots,
                "us_per_step": round(us, 3), "kv_GBps": round(kv_bytes / us / 1e3, 1),
                "pct_hbm_peak": round(100 * kv_bytes / us / 1e3 / HBM_PEAK_GBS, 2),
                "eager_us_per_step": round(eager_us, 3),
@@ -213,7 +255,18 @@ def main():
 
     us = head["us_per_step"]
     part_us = head["partial_kernel_us"]
-    achieved = kv_bytes / part_us / 1e3
+    if case.mla:
+        flops = 2 * case.T * case.Hq * (case.d_qk + case.d_v) * int(case.seq_lens.sum())
+        roof = {"bound": "mfma", "kernel": "mla_partial_kernel",
+                "achieved": round(flops / part_us / 1e6, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(flops / part_us / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": None, "kernel_us": part_us, "flops_per_launch": flops}
+    else:
+        kname = ("gqa_partial_kernel<%d,%s>" % (case.d_qk, "e4m3" if case.kv_dtype == "e4m3" else "bf16"))
+        achieved = kv_bytes / part_us / 1e3
+        roof = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel_us": part_us, "bytes_per_launch": kv_bytes}
     line = {
         "metric": METRIC,
         "value": head["kv_GBps"],
@@ -230,21 +283,19 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "e4m3-kv/bf16" if case.kv_dtype == "e4m3" else "bf16",
         "data": "synthetic",
-        "config": {"workload": f"few-KV-head long-context decode: B=1 T=1 Hq=16 Hkv=2 D=256 "
-                               f"L={args.L} bf16 paged (P=16, permuted), "
+        "config": {"workload": f"{describe(case, args.workload)}, "
                                f"{'warm' if args.warm_cache else 'cold'} cache ({R} pool copies)",
                    "num_splits": head["num_splits"],
                    "num_splits_requested": head["num_splits_requested"],
                    "kv_bytes_per_step": kv_bytes,
                    "plan_host_us": head["plan_host_us"]},
         "sweep": sweep,
-        "roofline": {"bound": "hbm", "kernel": "gqa_partial_kernel<256,bf16>",
-                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel_us": part_us},
+        "roofline": roof,
     }
+    if not headline:
+        line["note"] = "extra measurement; the bench line is the few-kv-long workload"
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -82,7 +82,8 @@ typedef int32_t splitkv_status;
 /* Split-range contract (see splitkv_plan). */
 #define SPLITKV_GRANULE 16             /* tokens; split ranges start on multiples of it */
 #define SPLITKV_AUTO_MIN_TOKENS 256    /* auto mode: fewest tokens per split */
-#define SPLITKV_AUTO_WG_PER_CU 2       /* auto mode: target workgroups per compute unit */
+#define SPLITKV_AUTO_WG_PER_CU 2       /* auto mode: target GQA workgroups per compute unit */
+#define SPLITKV_AUTO_WG_PER_CU_MLA 1   /* auto mode: target MLA workgroups per compute unit */
 #define SPLITKV_MAX_SPLITS_LIMIT 256   /* upper bound of max_splits */
 #define SPLITKV_ROWS_PER_WG_GQA 16     /* query rows (g*T) one GQA workgroup covers */
 #define SPLITKV_ROWS_PER_WG_MLA 64     /* query rows (T*Hq) one MLA workgroup covers */
@@ -108,10 +109,13 @@ typedef struct {
  * regression in "vLLM 0.30.0 FA4 SplitKV Bug ...", section "The actual bug is
  * one missing constructor argument", read a stored count of one and gave
  * every other split an empty range).  n == 0 sizes splits for the machine:
- * about SPLITKV_AUTO_WG_PER_CU * num_cus workgroups in total, at least
+ * at most R = SPLITKV_AUTO_WG_PER_CU * num_cus workgroups in total
+ * (SPLITKV_AUTO_WG_PER_CU_MLA for the MLA kernel), at least
  * SPLITKV_AUTO_MIN_TOKENS tokens per split, because the merge has a cost that
  * can eat the gain of more splits ("Shipped: 484.5 tok/s on one GB300 ...",
- * section "Why 8 splits lost").
+ * section "Why 8 splits lost"): with units = Hkv * ceil(g*T / rows_per_wg)
+ * workgroups per split, chunk = max(MIN, ceil(sum_b L_b * units / R)) and
+ * n_b = clamp(floor(L_b / chunk), 1, min(max_splits, nblk_b)).
  *
  * Split i of n covers [16*floor(i*nblk/n), min(L, 16*floor((i+1)*nblk/n))).
  * L == 0 gives one empty split.

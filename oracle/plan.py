@@ -21,10 +21,13 @@ two are compared bit for bit.
 * Granule G = 16 tokens; nblk(L) = ceil(L / G).
 * A request n > 0 is honoured exactly whenever n <= min(max_splits, nblk):
   n_eff = clamp(n, 1, min(max_splits, max(nblk, 1))).
-* Auto mode (n == 0): R = AUTO_WG_PER_CU * num_cus target workgroups,
+* Auto mode (n == 0): R = AUTO_WG_PER_CU * num_cus target workgroups
+  (AUTO_WG_PER_CU_MLA for the MLA kernel, whose workgroup fills a CU),
   units = Hkv * ceil(g*T / rows_per_wg) workgroups per split of a sequence,
   chunk = max(AUTO_MIN_TOKENS, ceil(sum_b L_b * units / R)),
-  n_b = clamp(ceil(L_b / chunk), 1, min(max_splits, max(nblk_b, 1))).
+  n_b = clamp(floor(L_b / chunk), 1, min(max_splits, max(nblk_b, 1))) -- floor,
+  so the total never exceeds R workgroups (a second partial round of
+  workgroups would double the step time).
 * Split i of n covers [G*floor(i*nblk/n), min(L, G*floor((i+1)*nblk/n))).
   Because n <= nblk every range holds at least one token, the ranges are
   disjoint and contiguous and their union is [0, L).  L == 0 gives one empty
@@ -37,6 +40,7 @@ import numpy as np
 GRANULE = 16
 AUTO_MIN_TOKENS = 256
 AUTO_WG_PER_CU = 2
+AUTO_WG_PER_CU_MLA = 1
 MAX_SPLITS_LIMIT = 256
 ROWS_PER_WG_GQA = 16
 ROWS_PER_WG_MLA = 64
@@ -78,9 +82,10 @@ def make_plan(seq_lens, *, T: int, Hq: int, Hkv: int, requested: int, max_splits
         g = Hq // Hkv
         units = Hkv * _ceil_div(g * T, rows_per_wg)
         work = sum(L) * units
-        target = AUTO_WG_PER_CU * num_cus
+        per_cu = AUTO_WG_PER_CU_MLA if rows_per_wg == ROWS_PER_WG_MLA else AUTO_WG_PER_CU
+        target = per_cu * num_cus
         chunk = max(AUTO_MIN_TOKENS, _ceil_div(work, target))
-        ns = [clamp_request(Lb, _ceil_div(Lb, chunk), max_splits) for Lb in L]
+        ns = [clamp_request(Lb, Lb // chunk, max_splits) for Lb in L]
     off = [0]
     for n in ns:
         off.append(off[-1] + n)

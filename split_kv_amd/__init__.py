@@ -31,6 +31,7 @@ SPLITKV_ERR_DEVICE = -5
 SPLITKV_GRANULE = 16
 SPLITKV_AUTO_MIN_TOKENS = 256
 SPLITKV_AUTO_WG_PER_CU = 2
+SPLITKV_AUTO_WG_PER_CU_MLA = 1
 SPLITKV_MAX_SPLITS_LIMIT = 256
 SPLITKV_ROWS_PER_WG_GQA = 16
 SPLITKV_ROWS_PER_WG_MLA = 64

@@ -29,7 +29,7 @@ constexpr int kMlaDv = 512;
 constexpr int kTile = 32;
 constexpr int kRowBytes = kMlaDqk * 2 + 16;      // LDS row pitch, padded
 constexpr int kChunks = kMlaDqk * 2 / 16;        // 72 16-byte chunks per row
-constexpr int kPerThread = kTile * kChunks / 256; // 9
+constexpr int kPerThread = kTile * kChunks / 256; // 9 chunks per thread per tile
 
 __device__ __forceinline__ void transpose8x8_m(const u32x4 (&w)[8], bf16x8 (&op)[8]) {
 #pragma unroll
@@ -86,24 +86,32 @@ __global__ __launch_bounds__(256) void mla_partial_kernel(PartialParams p, int p
   f32x4 oacc[32];
 #pragma unroll
   for (int c = 0; c < 32; ++c) oacc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  // m_ref: reference max of the exponentials (moves only when a row max grows
+  // by more than kRescaleMargin, so the accumulators are rarely touched by
+  // vector ALU code); m_true: the row's true running max.
+  constexpr float kRescaleMargin = 8.f;
+  float m_ref = -INFINITY, m_true = -INFINITY, l_run = 0.f;
 
   const int P = p.page_size;
+  const int psh = p.page_shift;
   const int32_t* bt_row = p.bt + b * p.bt_stride;
+  cint32* cbt = (cint32*)bt_row;
 
-  // Tile fetch into registers: chunk c = tid + 256k covers token c / 72.
+  // Tile fetch into registers: thread (token tid / 8, lane-in-row tid % 8)
+  // copies 16-byte chunks j, j+8, ..., j+64 of its token's 1152-byte row, so a
+  // thread needs one page lookup per tile.
+  const int ftok = tid >> 3, fj = tid & 7;
   auto fetch = [&](int tile, u32x4 (&regs)[kPerThread]) {
+    const int gt = tile + ftok;
+    if (gt < e) {
+      const int64_t pg = bt_row[psh >= 0 ? gt >> psh : gt / P];
+      const int sl = psh >= 0 ? gt & (P - 1) : gt % P;
+      const uint8_t* src = p.k + pg * p.ksp + int64_t(sl) * p.kst + 16 * fj;
 #pragma unroll
-    for (int k = 0; k < kPerThread; ++k) {
-      const int c = tid + 256 * k;
-      const int tok = c / kChunks, ch = c % kChunks;
-      const int gt = tile + tok;
-      if (gt < e) {
-        const int64_t pg = bt_row[gt / P];
-        regs[k] = *reinterpret_cast<const u32x4*>(p.k + pg * p.ksp + (gt % P) * p.kst + 16 * ch);
-      } else {
-        regs[k] = u32x4{0u, 0u, 0u, 0u};      // past the range: zeros, never NaN
-      }
+      for (int k = 0; k < kPerThread; ++k) regs[k] = *reinterpret_cast<const u32x4*>(src + 128 * k);
+    } else {
+#pragma unroll
+      for (int k = 0; k < kPerThread; ++k) regs[k] = u32x4{0u, 0u, 0u, 0u};   // past the range: zeros
     }
   };
 
@@ -114,31 +122,34 @@ __global__ __launch_bounds__(256) void mla_partial_kernel(PartialParams p, int p
   for (int tile = s; tile < e; tile += kTile) {
     __syncthreads();                           // previous tile fully consumed
 #pragma unroll
-    for (int k = 0; k < kPerThread; ++k) {
-      const int c = tid + 256 * k;
-      *reinterpret_cast<u32x4*>(smk + (c / kChunks) * kRowBytes + 16 * (c % kChunks)) = regs[k];
-    }
+    for (int k = 0; k < kPerThread; ++k)
+      *reinterpret_cast<u32x4*>(smk + ftok * kRowBytes + 16 * (fj + 8 * k)) = regs[k];
     __syncthreads();
     if (tile + kTile < e) fetch(tile + kTile, regs);
 
     const bool has1 = tile + 16 < e;
     {
-      const int pg0 = bt_row[tile / P];
-      const int pg1 = has1 ? bt_row[(tile + 16) / P] : 0;
+      const int pg0 = cbt[psh >= 0 ? tile >> psh : tile / P];
+      const int pg1 = has1 ? cbt[psh >= 0 ? (tile + 16) >> psh : (tile + 16) / P] : 0;
       dbg_groups += has1 ? 2 : 1;
       dbg_xor ^= pg0 ^ pg1;
       dbg_sum += uint32_t(pg0) + uint32_t(pg1);
     }
 
-    // ---- S^T = K Q^T for the two 16-token groups
+    // ---- S^T = K Q^T for the two 16-token groups (two accumulation chains each)
     f32x4 sc0 = {0.f, 0.f, 0.f, 0.f}, sc1 = {0.f, 0.f, 0.f, 0.f};
+    f32x4 sc0b = {0.f, 0.f, 0.f, 0.f}, sc1b = {0.f, 0.f, 0.f, 0.f};
     const uint8_t* k0 = smk + n16 * kRowBytes + 16 * qg;
     const uint8_t* k1 = k0 + 16 * kRowBytes;
 #pragma unroll
-    for (int it = 0; it < kMlaDqk / 32; ++it) {
+    for (int it = 0; it < kMlaDqk / 32; it += 2) {
       sc0 = mfma16x16x32(*reinterpret_cast<const bf16x8*>(k0 + 64 * it), qop[it], sc0);
       sc1 = mfma16x16x32(*reinterpret_cast<const bf16x8*>(k1 + 64 * it), qop[it], sc1);
+      sc0b = mfma16x16x32(*reinterpret_cast<const bf16x8*>(k0 + 64 * (it + 1)), qop[it + 1], sc0b);
+      sc1b = mfma16x16x32(*reinterpret_cast<const bf16x8*>(k1 + 64 * (it + 1)), qop[it + 1], sc1b);
     }
+    sc0 += sc0b;
+    sc1 += sc1b;
     float sv[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -149,19 +160,22 @@ __global__ __launch_bounds__(256) void mla_partial_kernel(PartialParams p, int p
     float mx = sv[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
-    mx = fmaxf(mx, xor_shfl(mx, 16));
-    mx = fmaxf(mx, xor_shfl(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
-    float pv[8], psum = 0.f;
+    mx = column_max4(mx);
+    m_true = fmaxf(m_true, mx);
+    const bool bump = mx > m_ref + kRescaleMargin;
+    if (__any(bump)) {
+      const float m_new = bump ? mx : m_ref;
+      const float alpha = fast_exp2(m_ref - m_new);   // 0 on the first visible tile
+      l_run *= alpha;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      pv[i] = exp2f(sv[i] - m_use);
-      psum += pv[i];
+      for (int c = 0; c < 32; ++c) oacc[c] *= alpha;
+      m_ref = m_new;
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
+    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+    float pv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pv[i] = fast_exp2(sv[i] - m_use);
+    l_run += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
     u32x4 pw = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
                 pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])};
     const bf16x8 pop = __builtin_bit_cast(bf16x8, pw);
@@ -178,13 +192,19 @@ __global__ __launch_bounds__(256) void mla_partial_kernel(PartialParams p, int p
       bf16x8 vop[8];
       transpose8x8_m(vw, vop);
 #pragma unroll
-      for (int e8 = 0; e8 < 8; ++e8)
-        oacc[c * 8 + e8] = mfma16x16x32(vop[e8], pop, oacc[c * 8 + e8] * alpha);
+      for (int e8 = 0; e8 < 8; ++e8) oacc[c * 8 + e8] = mfma16x16x32(vop[e8], pop, oacc[c * 8 + e8]);
     }
   }
 
-  l_run += xor_shfl(l_run, 16);
-  l_run += xor_shfl(l_run, 32);
+  // bring (l, o) from the reference max to the true max of the row
+  {
+    const float f = (m_ref == -INFINITY) ? 0.f : fast_exp2(m_ref - m_true);
+    l_run *= f;
+#pragma unroll
+    for (int c = 0; c < 32; ++c) oacc[c] *= f;
+  }
+  const float m_run = m_true;
+  l_run = column_sum4(l_run);
   const bool direct = p.direct && nsplit == 1;
   if (row_ok) {
     const int64_t R = int64_t(p.T) * p.Hq;

@@ -66,7 +66,10 @@ splitkv_status plan_host(const splitkv_plan_args& a, int32_t num_cus, const int3
         a.kernel == SPLITKV_KERNEL_MLA ? SPLITKV_ROWS_PER_WG_MLA : SPLITKV_ROWS_PER_WG_GQA;
     const int64_t g = a.Hq / a.Hkv;
     const int64_t units = int64_t(a.Hkv) * ceil_div(g * a.T, rows_per_wg);
-    const int64_t target = int64_t(SPLITKV_AUTO_WG_PER_CU) * num_cus;
+    // an MLA workgroup fills a compute unit; grouped-query workgroups fit two
+    const int64_t per_cu =
+        a.kernel == SPLITKV_KERNEL_MLA ? SPLITKV_AUTO_WG_PER_CU_MLA : SPLITKV_AUTO_WG_PER_CU;
+    const int64_t target = per_cu * num_cus;
     chunk = ceil_div(sum_len * units, target);
     if (chunk < SPLITKV_AUTO_MIN_TOKENS) chunk = SPLITKV_AUTO_MIN_TOKENS;
   }
@@ -74,7 +77,8 @@ splitkv_status plan_host(const splitkv_plan_args& a, int32_t num_cus, const int3
   slot_offset[0] = 0;
   for (int32_t b = 0; b < a.B; ++b) {
     const int64_t L = seq_lens[b];
-    const int64_t want = a.requested_splits > 0 ? a.requested_splits : ceil_div(L, chunk);
+    // auto: floor, so the plan never asks for more than the target workgroups
+    const int64_t want = a.requested_splits > 0 ? a.requested_splits : L / chunk;
     num_splits[b] = clamp_request(L, want, a.max_splits);
     off += num_splits[b];
     if (off > INT32_MAX) return fail(SPLITKV_ERR_INVALID_ARG, "splitkv_plan: too many slots");

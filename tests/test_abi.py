@@ -41,11 +41,12 @@ def test_constants_agree_with_oracle():
     assert sk.SPLITKV_GRANULE == oplan.GRANULE
     assert sk.SPLITKV_AUTO_MIN_TOKENS == oplan.AUTO_MIN_TOKENS
     assert sk.SPLITKV_AUTO_WG_PER_CU == oplan.AUTO_WG_PER_CU
+    assert sk.SPLITKV_AUTO_WG_PER_CU_MLA == oplan.AUTO_WG_PER_CU_MLA
     assert sk.SPLITKV_MAX_SPLITS_LIMIT == oplan.MAX_SPLITS_LIMIT
     assert sk.SPLITKV_ROWS_PER_WG_GQA == oplan.ROWS_PER_WG_GQA
     assert sk.SPLITKV_ROWS_PER_WG_MLA == oplan.ROWS_PER_WG_MLA
     header = open(os.path.join(ROOT, "include", "splitkv.h")).read()
-    for name in ("GRANULE", "AUTO_MIN_TOKENS", "AUTO_WG_PER_CU", "MAX_SPLITS_LIMIT",
+    for name in ("GRANULE", "AUTO_MIN_TOKENS", "AUTO_WG_PER_CU", "AUTO_WG_PER_CU_MLA", "MAX_SPLITS_LIMIT",
                  "ROWS_PER_WG_GQA", "ROWS_PER_WG_MLA"):
         m = re.search(rf"#define SPLITKV_{name} (\d+)", header)
         assert int(m.group(1)) == getattr(sk, f"SPLITKV_{name}")

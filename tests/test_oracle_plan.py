@@ -66,6 +66,22 @@ def test_clamps():
     assert P.split_range(0, 1, 0) == (0, 0)
 
 
+def test_auto_plan_never_exceeds_target():
+    # the floor keeps sum_b n_b * units <= target workgroups
+    import numpy as np
+    rng = np.random.default_rng(3)
+    for _ in range(200):
+        B = int(rng.integers(1, 40))
+        lens = rng.integers(0, 200000, size=B).tolist()
+        for (T, Hq, Hkv, rpw) in [(1, 32, 8, 16), (6, 128, 1, 64), (1, 16, 2, 16)]:
+            ns, off, _ = P.make_plan(lens, T=T, Hq=Hq, Hkv=Hkv, requested=0, max_splits=256,
+                                     num_cus=256, rows_per_wg=rpw)
+            units = Hkv * -(-(Hq // Hkv) * T // rpw)
+            per_cu = P.AUTO_WG_PER_CU_MLA if rpw == 64 else P.AUTO_WG_PER_CU
+            over = [n for n, Lb in zip(ns, lens) if n > 1]
+            assert sum(over) * units <= per_cu * 256 or not over
+
+
 def test_auto_plan_targets_two_wg_per_cu():
     # 8 x 32000 tokens, 4 KV heads, g=8 rows -> 32 units per split; 512 target WGs
     ns, off, seq = P.make_plan([32000] * 8, T=1, Hq=32, Hkv=4, requested=0, max_splits=256,
@@ -74,7 +90,7 @@ def test_auto_plan_targets_two_wg_per_cu():
     # minimum chunk: short sequences get one split
     ns, _, _ = P.make_plan([100, 300, 600], T=1, Hq=8, Hkv=2, requested=0, max_splits=64,
                            num_cus=256, rows_per_wg=16)
-    assert ns.tolist() == [1, 2, 3]               # chunk = AUTO_MIN_TOKENS = 256
+    assert ns.tolist() == [1, 1, 2]               # chunk = AUTO_MIN_TOKENS = 256, floor
     # slot_info holds (b, n << 16 | i, start, end)
     ns, off, info = P.make_plan([40, 5000], T=1, Hq=8, Hkv=2, requested=3, max_splits=64,
                                 num_cus=256, rows_per_wg=16)
