@@ -120,7 +120,7 @@ __global__ __launch_bounds__(256) void gqa_partial_kernel(PartialParams p) {
   constexpr int QROW = D + 8;           // bf16 elements per LDS query row (padded)
   constexpr float kRescaleMargin = 8.f; // base-2 growth of a row max before O is rescaled
   __shared__ float sm_o[4][16][LDS_STRIDE];
-  __shared__ float sm_m[4][16], sm_l[4][16];
+  __shared__ float sm_m[4][16], sm_r[4][16], sm_l[4][16];
   __shared__ int sm_dbg[4][3];
   __shared__ __attribute__((aligned(16))) uint16_t sm_q[Q_IN_LDS ? 16 : 1][QROW];
 
@@ -139,9 +139,7 @@ __global__ __launch_bounds__(256) void gqa_partial_kernel(PartialParams p) {
 
   // This lane's query row (column of the S^T tile).
   const int row = rb * 16 + n16;
-  const bool row_ok = row < p.rows;
-  const int t = row_ok ? row / p.g : 0;
-  const int h = hk * p.g + (row_ok ? row % p.g : 0);
+  const int t = row < p.rows ? row / p.g : 0;
   // Causal limit: with one query token every key of the range is visible, so
   // only multi-token decode reads the sequence length.
   int limit = 0x7fffffff;
@@ -156,22 +154,18 @@ __global__ __launch_bounds__(256) void gqa_partial_kernel(PartialParams p) {
     for (int k = 0; k < QCH; ++k) {
       const int c = threadIdx.x + 256 * k;
       const int r = c / (D / 8), d8 = c % (D / 8);
-      const int gr = rb * 16 + r;
-      qstage[k] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      if (gr < p.rows) {
-        const int tt = gr / p.g, hh = hk * p.g + gr % p.g;
-        qstage[k] = *reinterpret_cast<const bf16x8*>(p.q + b * p.qsb + tt * p.qst + hh * p.qsh + 8 * d8);
-      }
+      // Rows past the last query row load row rows-1 and are zeroed when
+      // staged: an unconditional load keeps the completion count exact.
+      const int gr = min(rb * 16 + r, p.rows - 1);
+      const int tt = gr / p.g, hh = hk * p.g + gr % p.g;
+      qstage[k] = *reinterpret_cast<const bf16x8*>(p.q + b * p.qsb + tt * p.qst + hh * p.qsh + 8 * d8);
     }
   } else {
-    const uint16_t* qrow = p.q + b * p.qsb + t * p.qst + h * p.qsh;
+    const int rc = min(row, p.rows - 1);
+    const uint16_t* qrow = p.q + b * p.qsb + (rc / p.g) * p.qst + (hk * p.g + rc % p.g) * p.qsh;
 #pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      if (row_ok)
-        qop[it] = *reinterpret_cast<const bf16x8*>(qrow + q_chunk_d0<FP8>(it, qg));
-      else
-        qop[it] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
-    }
+    for (int it = 0; it < NIT; ++it)
+      qop[it] = *reinterpret_cast<const bf16x8*>(qrow + q_chunk_d0<FP8>(it, qg));
   }
 
   const int P = p.page_size;
@@ -306,45 +300,57 @@ __global__ __launch_bounds__(256) void gqa_partial_kernel(PartialParams p) {
     dbg_sum += uint32_t(pg);
   };
 
-  // Software pipeline, distance one: group j+1 is in flight while group j is
-  // computed.  Prefetches are unconditional (clamped to the last group, whose
-  // lines they then re-read from cache) and the loop has a single exit at its
-  // end, so no control-flow path reaches the loop head with loads the compiler
-  // cannot account for -- otherwise it waits for every load at the top of each
-  // iteration.  sched_barrier keeps the scheduler from hoisting compute (and
-  // its waits) above the prefetch.  The first group's loads are issued before
-  // the query is staged, so the two latencies overlap.
+  // Software pipeline over two register sets: groups j and j+1 are in
+  // flight before group j is computed, and each set is refilled (group j+2,
+  // j+3) as soon as its group has been consumed, so a wave always has one or
+  // two groups of loads outstanding.  Prefetches are unconditional (clamped
+  // to the last group, whose lines they then re-read from cache) and the loop
+  // has a single exit at its end, so no control-flow path reaches the loop
+  // head with loads the compiler cannot account for -- otherwise it waits for
+  // every load at the top of each iteration.  sched_barrier keeps the
+  // scheduler from hoisting compute (and its waits) above a prefetch.  The
+  // first two groups are issued before the query is staged, so the query
+  // and block-table latencies overlap them.  A wave without groups issues
+  // the same loads from page 0 (which always exists) and never uses them:
+  // the loads stay unconditional, so the wait for the query stays exact.
   GroupRegs<D, FP8> ra, rb2;
-  int pg_cur = 0, pg_nxt = 0;
+  int pg_cur = 0, pg_nxt = 0, pg_a = 0, pg_b = 0;   // pages of groups j, j+1, j+2, j+3
   if (ngw > 0) {
     pg_cur = page_of(0);
-    load(0, pg_cur, ra);
     pg_nxt = page_of(min(1, ngw - 1));
+  }
+  load(0, pg_cur, ra);
+  load(min(1, max(ngw - 1, 0)), pg_nxt, rb2);
+  if (ngw > 0) {
+    pg_a = page_of(min(2, ngw - 1));
+    pg_b = page_of(min(3, ngw - 1));
   }
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (Q_IN_LDS) {
 #pragma unroll
     for (int k = 0; k < QCH; ++k) {
       const int c = threadIdx.x + 256 * k;
-      *reinterpret_cast<bf16x8*>(&sm_q[c / (D / 8)][8 * (c % (D / 8))]) = qstage[k];
+      const int r = c / (D / 8);
+      const bf16x8 zero = {0, 0, 0, 0, 0, 0, 0, 0};
+      *reinterpret_cast<bf16x8*>(&sm_q[r][8 * (c % (D / 8))]) = rb * 16 + r < p.rows ? qstage[k] : zero;
     }
     __syncthreads();
   }
   for (int j = 0; j < ngw; j += 2) {
-    load(min(j + 1, ngw - 1), pg_nxt, rb2);
-    const int pg_a = page_of(min(j + 2, ngw - 1));
-    __builtin_amdgcn_sched_barrier(0);
     visit(pg_cur);
     compute(j, ra);
     load(min(j + 2, ngw - 1), pg_a, ra);
-    const int pg_b = page_of(min(j + 3, ngw - 1));
+    pg_cur = pg_a;
+    pg_a = page_of(min(j + 4, ngw - 1));
     __builtin_amdgcn_sched_barrier(0);
     if (j + 1 < ngw) {
       visit(pg_nxt);
       compute(j + 1, rb2);
     }
-    pg_cur = pg_a;
+    load(min(j + 3, ngw - 1), pg_b, rb2);
     pg_nxt = pg_b;
+    pg_b = page_of(min(j + 5, ngw - 1));
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // ---- per-wave row totals; then merge the four waves through LDS
@@ -362,21 +368,9 @@ __global__ __launch_bounds__(256) void gqa_partial_kernel(PartialParams p) {
       }
   if (qg == 0) {
     sm_m[wave][n16] = m_true;
-    sm_l[wave][n16] = m_ref;        // reference max, parked here until the merge
+    sm_r[wave][n16] = m_ref;
+    sm_l[wave][n16] = l_run;
   }
-  __syncthreads();
-  // per-wave scale so every wave's (l, o) refer to the wave's true max
-  float mref_w[4], mtrue_w[4];
-  {
-    const int r = threadIdx.x >> 4;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      mtrue_w[w] = sm_m[w][r];
-      mref_w[w] = sm_l[w][r];
-    }
-  }
-  __syncthreads();
-  if (qg == 0) sm_l[wave][n16] = l_run;
   if (lane == 0) {
     sm_dbg[wave][0] = dbg_groups;
     sm_dbg[wave][1] = dbg_xor;
@@ -390,13 +384,16 @@ __global__ __launch_bounds__(256) void gqa_partial_kernel(PartialParams p) {
     const int part = threadIdx.x & 15;    // D/16 features each
     const int grow = rb * 16 + r;
     if (grow < p.rows) {
-      float M = mtrue_w[0];
+      // each wave's (l, o) is relative to its reference max; bring all four
+      // to the block's true max
+      float M = sm_m[0][r];
 #pragma unroll
-      for (int w = 1; w < 4; ++w) M = fmaxf(M, mtrue_w[w]);
+      for (int w = 1; w < 4; ++w) M = fmaxf(M, sm_m[w][r]);
       float wgt[4], Lsum = 0.f;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        wgt[w] = mref_w[w] == -INFINITY ? 0.f : exp2f(mref_w[w] - M);
+        const float mr = sm_r[w][r];
+        wgt[w] = mr == -INFINITY ? 0.f : exp2f(mr - M);
         Lsum += wgt[w] * sm_l[w][r];
       }
       const int tt = grow / p.g, hh = hk * p.g + grow % p.g;
