@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--warm-cache", action="store_true", help="reuse one page pool copy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device copy, the known-size reference that "
+                         "scales the FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
 
 
@@ -163,26 +166,27 @@ def time_steps_graph(sess, bts, R, steps, warmup, check=True):
 
 
 def time_partial_kernel(sess, bts, R, steps, stream):
-    """Average duration of the partial kernel alone.
+    """Average duration of the dominant kernel, the partial kernel.
 
-    `steps` partial launches (launch i reads page-pool copy i mod R) are
-    captured in one HIP graph on `stream` and replayed once untimed, then once
-    between two events recorded on that same stream; the result is the
-    replay time divided by `steps`.  Back-to-back graph nodes leave only the
-    dispatch gap between kernels, so this tracks the kernel-trace duration.
+    `steps` launches (launch i reads page-pool copy i mod R) are captured in
+    one HIP graph on `stream` and replayed once untimed, then once between two
+    events recorded on that same stream; the result is the replay time divided
+    by `steps`.  Back-to-back graph nodes leave only the dispatch gap between
+    kernels, so this tracks the kernel-trace duration.
     """
     import torch
+    launch = sess.partial
     with torch.cuda.stream(stream):
         for i in range(3):
             sess.set_block_table(bts[i % R])
-            sess.partial()
+            launch()
     torch.cuda.synchronize()
     cap = torch.cuda.Stream()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=cap):
         for i in range(steps):
             sess.set_block_table(bts[i % R])
-            sess.partial()
+            launch()
     with torch.cuda.stream(cap):
         g.replay()
         torch.cuda.synchronize()
@@ -193,6 +197,37 @@ def time_partial_kernel(sess, bts, R, steps, stream):
     torch.cuda.synchronize()
     del g
     return start.elapsed_time(end) * 1e3 / steps
+
+
+COUNTERS = os.path.join(ROOT, "profiles", "gqa_partial_fewkv_L5900_counters.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "split_kv_amd", "csrc", f) for f in ("gqa.hip", "device.h")]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the headline partial kernel from the committed
+    FETCH_SIZE / WRITE_SIZE counter runs, each scaled by what the same counter
+    reads for a plain copy of known size; None when the kernel source has
+    changed since the counters were taken (or they are missing)."""
+    import hashlib
+    try:
+        vals = {}
+        for line in open(COUNTERS):
+            if ":" in line and not line.startswith(("#", " ", "|")):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+        h = hashlib.sha256()
+        for f in KERNEL_SOURCES:
+            h.update(open(f, "rb").read())
+        if h.hexdigest()[:16] != vals["kernel_source_sha256_16"]:
+            return None, "kernel changed since the counters were taken"
+        copy = float(vals["copy_bytes"])
+        fetch = float(vals["fetch_kib_per_dispatch"]) * copy / (1024 * float(vals["copy_fetch_kib"]))
+        write = float(vals["write_kib_per_dispatch"]) * copy / (1024 * float(vals["copy_write_kib"]))
+        return int(round((fetch + write) * 1024)), {
+            "fetch_bytes": int(round(fetch * 1024)), "write_bytes": int(round(write * 1024)),
+            "source": os.path.relpath(COUNTERS, ROOT)}
+    except (OSError, KeyError, ValueError) as e:
+        return None, f"counters unavailable: {e}"
 
 
 def cpu_baseline(case, seconds):
@@ -218,8 +253,27 @@ def cpu_baseline(case, seconds):
                       f"{per_step * 1e6:.0f} us per step"}
 
 
+def copy_calibration():
+    """A plain device-to-device copy of 256 MiB, repeated 5 times.
+
+    Under rocprofv3 --pmc FETCH_SIZE (or WRITE_SIZE) the copy kernel's counter
+    divided by 256 MiB is the factor that turns the counter into HBM bytes.
+    """
+    import torch
+    n = 256 << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
+
+
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "multi-GPU sharding is described in DESIGN.md, not run.", file=sys.stderr)
@@ -286,6 +340,11 @@ def main():
         roof = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                 "kernel_us": part_us, "bytes_per_launch": kv_bytes}
+        # counters were taken for the headline workload at the auto plan
+        if headline and head["num_splits_requested"] == 0 and not args.warm_cache and args.L is None:
+            traffic, detail = measured_traffic()
+            roof["traffic"] = traffic
+            roof["traffic_detail"] = detail
     line = {
         "metric": METRIC,
         "value": head["kv_GBps"],
@@ -308,6 +367,7 @@ def main():
                                f"{'warm' if args.warm_cache else 'cold'} cache ({R} pool copies)",
                    "num_splits": head["num_splits"],
                    "num_splits_requested": head["num_splits_requested"],
+                   "step": "partial kernel, then combine kernel (skipped when every sequence has one split)",
                    "kv_bytes_per_step": kv_bytes,
                    "plan_host_us": head["plan_host_us"]},
         "sweep": sweep,

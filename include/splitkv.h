@@ -81,7 +81,7 @@ typedef int32_t splitkv_status;
 
 /* Split-range contract (see splitkv_plan). */
 #define SPLITKV_GRANULE 16             /* tokens; split ranges start on multiples of it */
-#define SPLITKV_AUTO_MIN_TOKENS 256    /* auto mode: fewest tokens per split */
+#define SPLITKV_AUTO_MIN_TOKENS 96     /* auto mode: fewest tokens per split */
 #define SPLITKV_AUTO_WG_PER_CU 2       /* auto mode: target GQA workgroups per compute unit */
 #define SPLITKV_AUTO_WG_PER_CU_MLA 1   /* auto mode: target MLA workgroups per compute unit */
 #define SPLITKV_MAX_SPLITS_LIMIT 256   /* upper bound of max_splits */

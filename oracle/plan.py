@@ -38,7 +38,7 @@ import numpy as np
 # Constants of the contract (the library publishes its own copies; a test
 # checks that the two agree).
 GRANULE = 16
-AUTO_MIN_TOKENS = 256
+AUTO_MIN_TOKENS = 96
 AUTO_WG_PER_CU = 2
 AUTO_WG_PER_CU_MLA = 1
 MAX_SPLITS_LIMIT = 256

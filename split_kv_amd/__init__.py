@@ -29,7 +29,7 @@ SPLITKV_ERR_LAUNCH = -4
 SPLITKV_ERR_DEVICE = -5
 
 SPLITKV_GRANULE = 16
-SPLITKV_AUTO_MIN_TOKENS = 256
+SPLITKV_AUTO_MIN_TOKENS = 96
 SPLITKV_AUTO_WG_PER_CU = 2
 SPLITKV_AUTO_WG_PER_CU_MLA = 1
 SPLITKV_MAX_SPLITS_LIMIT = 256

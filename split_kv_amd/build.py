@@ -48,9 +48,13 @@ def sources():
 
 # Per-source code-generation options.  The grouped-query kernel rescales its
 # MFMA accumulators with vector ALU code; keeping them in VGPRs (instead of the
-# accumulation registers) avoids copying them across on every group.
+# accumulation registers) avoids copying them across on every group.  The
+# grouped-query and combine kernels take their first fourteen argument dwords
+# preloaded into scalar registers at wave launch, so their first memory access
+# does not wait for an argument load.
 PER_FILE = {
-    "gqa.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
+    "gqa.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true", "-mllvm", "-amdgpu-kernarg-preload-count=14"],
+    "combine.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=14"],
 }
 
 

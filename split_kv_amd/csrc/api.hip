@@ -141,6 +141,23 @@ splitkv_status check_partial(const splitkv_args* a, Kind kind, bool need_ws, con
   *row_blocks = int(ceil_div(rows, rpw));
   const int64_t wgs = int64_t(a->total_slots) * a->Hkv * *row_blocks;
   if (wgs > (int64_t(1) << 30)) return fail(SPLITKV_ERR_INVALID_ARG, "%s: grid too large", fn);
+  if (kind != Kind::Mla) {
+    // the grouped-query kernels take 32-bit strides and a packed launch geometry
+    const int64_t st[] = {a->q_stride_b, a->q_stride_t, a->q_stride_h, a->k_stride_page * elem,
+                          a->k_stride_head * elem, a->k_stride_tok * elem, a->v_stride_page * elem,
+                          a->v_stride_head * elem, a->v_stride_tok * elem, a->bt_stride};
+    for (int64_t x : st)
+      if (x < 0 || x > INT32_MAX)
+        return fail(SPLITKV_ERR_UNSUPPORTED, "%s: a stride of %lld does not fit 31 bits", fn,
+                    static_cast<long long>(x));
+    // buffer offsets inside one 16-token group are 32-bit
+    if (16 * (a->k_stride_tok * elem) + a->d_qk * elem > INT32_MAX ||
+        16 * (a->v_stride_tok * elem) + a->d_v * elem > INT32_MAX)
+      return fail(SPLITKV_ERR_UNSUPPORTED, "%s: token strides too large", fn);
+    if (a->Hkv > 0xffff || *row_blocks > 0xff)
+      return fail(SPLITKV_ERR_UNSUPPORTED, "%s: Hkv=%d or %d row blocks too large", fn, a->Hkv,
+                  *row_blocks);
+  }
   return SPLITKV_OK;
 }
 

@@ -9,14 +9,20 @@
 // range with four independent load streams and writes one partial.
 //
 // Decode attention is memory-bound here (per token 2*g*(d_qk+d_v) FLOPs
-// against (d_qk+d_v)*elem bytes), and at decode sizes mostly memory-latency
-// bound, so the kernel is organised around keeping loads in flight:
+// against (d_qk+d_v)*elem bytes), and at decode sizes mostly bound by memory
+// latency: a workgroup's critical path is a chain of dependent loads
+// (split record -> block table -> K/V).  The kernel keeps that chain short:
+//   * the first argument dwords (cache, table, query and plan pointers, the
+//     table stride and the launch geometry) are preloaded into scalar
+//     registers at wave launch, so the split record is the first memory
+//     access;
 //   * block-table entries come through the scalar cache, one group ahead, so
 //     waiting for them never waits for K/V vector loads;
 //   * every K/V load is a uniform base plus a loop-invariant lane offset;
-//   * the next group's K and V are loaded into a second register set while
-//     the current group is computed (software pipelining, distance one), in a
-//     loop shaped so the compiler's load-completion waits stay exact.
+//   * two groups of K and V are in flight per wave while one is computed
+//     (software pipelining over two register sets), in a loop shaped so the
+//     compiler's load-completion waits stay exact;
+//   * the query goes straight to registers in MFMA operand layout.
 // Per 16-token group, all in registers:
 //   * K rows go straight from HBM into the MFMA A-operand layout (lane = token,
 //     16 bytes of the feature dimension per load); e4m3 codes widen exactly to
@@ -39,6 +45,25 @@ namespace splitkv {
 
 namespace {
 
+// Arguments read after the preloaded ones (they are not on the first load's
+// critical path).
+struct GqaRest {
+  int32_t qsb, qst, qsh;          // query element strides
+  int32_t ksp, ksh, kst;          // key byte strides: page, head, token
+  int32_t vsp, vsh, vst;          // value byte strides
+  int32_t T, Hq, g, page_size, rows, R;   // R = T * Hq output rows per sequence
+  float scale_log2;               // scale * k_scale * log2(e)
+  float v_scale;
+  const int32_t* seq_lens;
+  float* part_m;
+  float* part_l;
+  float* part_o;
+  void* out;
+  float* lse;
+  int32_t* debug;
+  int32_t out_f32, direct;
+};
+
 template <bool FP8>
 __device__ __forceinline__ int q_chunk_d0(int it, int qg) {
   // Feature offset of the 8 elements lane-group qg holds in k-iteration it.
@@ -59,16 +84,25 @@ __device__ __forceinline__ void widen_k_fp8(bf16x8 (&kop)[D / 32]) {
   }
 }
 
+// Buffer resource over the bytes of one 16-token group.  A group past the
+// end of the range gets a resource of zero bytes: its loads are still issued
+// (so the load-completion counts stay static) but return zeros without a
+// memory access.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t group_rsrc(const uint8_t* base, bool valid) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, valid ? 0x7fffffff : 0,
+                                           0x00020000);
+}
+
 // 8 consecutive V features of one token: 4 dwords of bf16 pairs (bf16 cache)
 // or 2 dwords of e4m3 codes (FP8 cache, widened later).
 template <bool FP8>
-__device__ __forceinline__ u32x4 load_v8(const uint8_t* p) {
+__device__ __forceinline__ u32x4 load_v8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   if constexpr (!FP8) {
-    return *reinterpret_cast<const u32x4*>(p);
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
   } else {
-    const u32x2 w = *reinterpret_cast<const u32x2*>(p);
-    u32x4 r = {w.x, w.y, 0u, 0u};
-    return r;
+    const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+    u32x4 v = {w.x, w.y, 0u, 0u};
+    return v;
   }
 }
 
@@ -108,85 +142,77 @@ struct GroupRegs {
   u32x4 v[D / 128][4];
 };
 
+
 }  // namespace
 
+// Launch geometry packed into one preloaded dword: Hkv (bits 0-15), row
+// blocks (16-23), log2(page size) + 1 (24-31; 0 when not a power of two).
 template <int D, bool FP8>
-__global__ __launch_bounds__(256) void gqa_partial_kernel(PartialParams p) {
+__global__ __launch_bounds__(256) void gqa_partial_kernel(
+    const int32_t* bt, const int32_t* slot_info, const uint16_t* q, const uint8_t* kc,
+    const uint8_t* vc, int32_t bt_stride, int32_t geom, GqaRest a) {
   constexpr int NIT = D / 32;           // QK k-iterations
   constexpr int NC = D / 128;           // V feature chunks of 128 per lane-row
   constexpr int ELEM = FP8 ? 1 : 2;
   constexpr int LDS_STRIDE = D + 4;     // floats; padding against bank conflicts
-  constexpr bool Q_IN_LDS = D >= 256;   // frees 32 VGPRs for the wide head dim
-  constexpr int QROW = D + 8;           // bf16 elements per LDS query row (padded)
   constexpr float kRescaleMargin = 8.f; // base-2 growth of a row max before O is rescaled
   __shared__ float sm_o[4][16][LDS_STRIDE];
   __shared__ float sm_m[4][16], sm_r[4][16], sm_l[4][16];
   __shared__ int sm_dbg[4][3];
-  __shared__ __attribute__((aligned(16))) uint16_t sm_q[Q_IN_LDS ? 16 : 1][QROW];
 
   const int lane = threadIdx.x & 63;
   const int wave = uniform(int(threadIdx.x >> 6));
   const int n16 = lane & 15, qg = lane >> 4;
 
+  const int Hkv = geom & 0xffff;
+  const int RB = (geom >> 16) & 0xff;
+  const int psh = (geom >> 24) - 1;
   int wg = blockIdx.x;
-  const int rb = wg % p.row_blocks;
-  wg /= p.row_blocks;
-  const int hk = wg % p.Hkv;
-  const int slot = wg / p.Hkv;
+  const int rb = RB == 1 ? 0 : wg % RB;
+  wg = RB == 1 ? wg : wg / RB;
+  const int hk = wg % Hkv;
+  const int slot = wg / Hkv;
   // One scalar load gives the slot's sequence, split and token range.
-  const SlotWork work = load_slot(p.slot_info, slot);
+  const SlotWork work = load_slot(slot_info, slot);
   const int b = work.b, split = work.split, nsplit = work.nsplit, s = work.s, e = work.e;
 
-  // This lane's query row (column of the S^T tile).
-  const int row = rb * 16 + n16;
-  const int t = row < p.rows ? row / p.g : 0;
-  // Causal limit: with one query token every key of the range is visible, so
-  // only multi-token decode reads the sequence length.
-  int limit = 0x7fffffff;
-  if (p.T > 1) limit = ((cint32*)p.seq_lens)[b] - p.T + t;
-
-  // Query operand: issued now, consumed after the first K/V loads are in flight.
-  bf16x8 qop[Q_IN_LDS ? 1 : NIT];
-  constexpr int QCH = Q_IN_LDS ? (16 * (D / 8)) / 256 : 1;   // 16-byte chunks per thread
-  bf16x8 qstage[QCH];
-  if constexpr (Q_IN_LDS) {
-#pragma unroll
-    for (int k = 0; k < QCH; ++k) {
-      const int c = threadIdx.x + 256 * k;
-      const int r = c / (D / 8), d8 = c % (D / 8);
-      // Rows past the last query row load row rows-1 and are zeroed when
-      // staged: an unconditional load keeps the completion count exact.
-      const int gr = min(rb * 16 + r, p.rows - 1);
-      const int tt = gr / p.g, hh = hk * p.g + gr % p.g;
-      qstage[k] = *reinterpret_cast<const bf16x8*>(p.q + b * p.qsb + tt * p.qst + hh * p.qsh + 8 * d8);
-    }
-  } else {
-    const int rc = min(row, p.rows - 1);
-    const uint16_t* qrow = p.q + b * p.qsb + (rc / p.g) * p.qst + (hk * p.g + rc % p.g) * p.qsh;
-#pragma unroll
-    for (int it = 0; it < NIT; ++it)
-      qop[it] = *reinterpret_cast<const bf16x8*>(qrow + q_chunk_d0<FP8>(it, qg));
-  }
-
-  const int P = p.page_size;
-  const int32_t* bt_row = p.bt + b * p.bt_stride;
-  const uint8_t* kbase = p.k + hk * p.ksh;
-  const uint8_t* vbase = p.v + hk * p.vsh;
-
+  const int P = a.page_size;
+  const int32_t* bt_row = bt + b * bt_stride;
   // groups of the range: wave w takes groups w, w+4, w+8, ...
   const int ngroups = (e - s + 15) >> 4;
   const int ngw = ngroups > wave ? (ngroups - wave + 3) >> 2 : 0;
 
   // Block-table reads go through the scalar cache (constant address space:
   // the table is read-only while the kernel runs), so their completion
-  // counter is not the one the in-flight K/V vector loads use.  Each group's
-  // page is fetched one group ahead.
+  // counter is not the one the in-flight K/V vector loads use.
   cint32* cbt = (cint32*)bt_row;
-  const int psh = p.page_shift;
   auto page_of = [&](int j) -> int {
     const int tok = s + 16 * (wave + 4 * j);
     return cbt[psh >= 0 ? tok >> psh : tok / P];
   };
+  int pg_cur = 0, pg_nxt = 0, pg_a = 0, pg_b = 0;   // pages of groups j, j+1, j+2, j+3
+  if (ngw > 0) pg_cur = page_of(0);
+  if (ngw > 1) pg_nxt = page_of(1);
+
+  // This lane's query row (column of the S^T tile).  Rows past the last query
+  // row read row rows-1: their columns are computed and never stored.
+  const int row = rb * 16 + n16;
+  const int rc = min(row, a.rows - 1);
+  const int t = rc / a.g;
+  // Causal limit: with one query token every key of the range is visible, so
+  // only multi-token decode reads the sequence length.
+  int limit = 0x7fffffff;
+  if (a.T > 1) limit = ((cint32*)a.seq_lens)[b] - a.T + t;
+  bf16x8 qop[NIT];
+  {
+    const uint16_t* qrow = q + int64_t(b) * a.qsb + t * a.qst + (hk * a.g + rc % a.g) * a.qsh;
+#pragma unroll
+    for (int it = 0; it < NIT; ++it)
+      qop[it] = *reinterpret_cast<const bf16x8*>(qrow + q_chunk_d0<FP8>(it, qg));
+  }
+
+  const uint8_t* kbase = kc + int64_t(hk) * a.ksh;
+  const uint8_t* vbase = vc + int64_t(hk) * a.vsh;
 
   f32x4 oacc[NC * 8];
 #pragma unroll
@@ -200,30 +226,32 @@ __global__ __launch_bounds__(256) void gqa_partial_kernel(PartialParams p) {
   // Per-lane byte offsets inside a 16-token group are loop-invariant; each
   // load is a uniform (scalar) base plus one of them, so the loop needs no
   // per-iteration vector address arithmetic.
-  const uint32_t koff = uint32_t(n16 * p.kst) + 16u * qg;
+  const uint32_t koff = uint32_t(n16 * a.kst) + 16u * qg;
   uint32_t voff[4];
 #pragma unroll
-  for (int jt = 0; jt < 4; ++jt) voff[jt] = uint32_t((4 * qg + jt) * p.vst) + uint32_t(ELEM * 8 * n16);
+  for (int jt = 0; jt < 4; ++jt) voff[jt] = uint32_t((4 * qg + jt) * a.vst) + uint32_t(ELEM * 8 * n16);
 
+  // Group j of this wave (j < ngw loads; later j only keep the counts static).
   auto load = [&](int j, int64_t pg, GroupRegs<D, FP8>& r) {
+    const bool valid = j < ngw;
     const int tok = s + 16 * (wave + 4 * j);
     const int sl = psh >= 0 ? tok & (P - 1) : tok % P;
-    const uint8_t* kb = kbase + pg * p.ksp + int64_t(sl) * p.kst;
-    const uint8_t* vb = vbase + pg * p.vsp + int64_t(sl) * p.vst;
+    const auto rk = group_rsrc(kbase + pg * a.ksp + int64_t(sl) * a.kst, valid);
+    const auto rv = group_rsrc(vbase + pg * a.vsp + int64_t(sl) * a.vst, valid);
     if constexpr (!FP8) {
 #pragma unroll
       for (int it = 0; it < NIT; ++it)
-        r.k[it] = *reinterpret_cast<const bf16x8*>(kb + koff + 64 * it);
+        r.k[it] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, koff + 64 * it, 0, 0));
     } else {
 #pragma unroll
       for (int kk = 0; kk < D / 64; ++kk)
-        r.k[2 * kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kb + koff + 64 * kk));
+        r.k[2 * kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, koff + 64 * kk, 0, 0));
     }
 #pragma unroll
     for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
       for (int c = 0; c < NC; ++c)
-        r.v[c][jt] = load_v8<FP8>(vb + voff[jt] + ELEM * 128 * c);
+        r.v[c][jt] = load_v8<FP8>(rv, voff[jt] + ELEM * 128 * c);
   };
 
   auto compute = [&](int j, GroupRegs<D, FP8>& r) {
@@ -233,22 +261,17 @@ __global__ __launch_bounds__(256) void gqa_partial_kernel(PartialParams p) {
     f32x4 sca = {0.f, 0.f, 0.f, 0.f}, scb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
-      bf16x8 qv;
-      if constexpr (Q_IN_LDS)
-        qv = *reinterpret_cast<const bf16x8*>(&sm_q[n16][q_chunk_d0<FP8>(it, qg)]);
-      else
-        qv = qop[it];
       if (it & 1)
-        scb = mfma16x16x32(r.k[it], qv, scb);
+        scb = mfma16x16x32(r.k[it], qop[it], scb);
       else
-        sca = mfma16x16x32(r.k[it], qv, sca);
+        sca = mfma16x16x32(r.k[it], qop[it], sca);
     }
     const f32x4 sc = sca + scb;
     float sv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int tk = g0 + 4 * qg + i;
-      sv[i] = (tk < e && tk <= limit) ? sc[i] * p.scale_log2 : -INFINITY;
+      sv[i] = (tk < e && tk <= limit) ? sc[i] * a.scale_log2 : -INFINITY;
     }
     const float mx = column_max4(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
     m_true = fmaxf(m_true, mx);
@@ -303,54 +326,48 @@ __global__ __launch_bounds__(256) void gqa_partial_kernel(PartialParams p) {
   // Software pipeline over two register sets: groups j and j+1 are in
   // flight before group j is computed, and each set is refilled (group j+2,
   // j+3) as soon as its group has been consumed, so a wave always has one or
-  // two groups of loads outstanding.  Prefetches are unconditional (clamped
-  // to the last group, whose lines they then re-read from cache) and the loop
-  // has a single exit at its end, so no control-flow path reaches the loop
-  // head with loads the compiler cannot account for -- otherwise it waits for
-  // every load at the top of each iteration.  sched_barrier keeps the
-  // scheduler from hoisting compute (and its waits) above a prefetch.  The
-  // first two groups are issued before the query is staged, so the query
-  // and block-table latencies overlap them.  A wave without groups issues
-  // the same loads from page 0 (which always exists) and never uses them:
-  // the loads stay unconditional, so the wait for the query stays exact.
+  // two groups of loads outstanding.  Inside the steady-state loop every load
+  // is unconditional (the loop runs only while groups j+2 and j+3 exist), so
+  // the compiler's load-completion waits stay exact; the first two groups are
+  // issued unconditionally too (through an empty buffer range when the wave
+  // has fewer groups, which costs no memory traffic).  The at most three
+  // groups after the loop need at most one more load, issued in the tail, so
+  // no load is left in flight when the wave reaches the merge.
+  // sched_barrier keeps the scheduler from hoisting compute (and its waits)
+  // above a prefetch.
   GroupRegs<D, FP8> ra, rb2;
-  int pg_cur = 0, pg_nxt = 0, pg_a = 0, pg_b = 0;   // pages of groups j, j+1, j+2, j+3
-  if (ngw > 0) {
-    pg_cur = page_of(0);
-    pg_nxt = page_of(min(1, ngw - 1));
-  }
   load(0, pg_cur, ra);
-  load(min(1, max(ngw - 1, 0)), pg_nxt, rb2);
-  if (ngw > 0) {
-    pg_a = page_of(min(2, ngw - 1));
-    pg_b = page_of(min(3, ngw - 1));
-  }
+  load(1, pg_nxt, rb2);
+  if (ngw > 2) pg_a = page_of(2);
+  if (ngw > 3) pg_b = page_of(3);
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (Q_IN_LDS) {
-#pragma unroll
-    for (int k = 0; k < QCH; ++k) {
-      const int c = threadIdx.x + 256 * k;
-      const int r = c / (D / 8);
-      const bf16x8 zero = {0, 0, 0, 0, 0, 0, 0, 0};
-      *reinterpret_cast<bf16x8*>(&sm_q[r][8 * (c % (D / 8))]) = rb * 16 + r < p.rows ? qstage[k] : zero;
-    }
-    __syncthreads();
-  }
-  for (int j = 0; j < ngw; j += 2) {
+  int j = 0;
+  for (; j + 3 < ngw; j += 2) {
     visit(pg_cur);
     compute(j, ra);
-    load(min(j + 2, ngw - 1), pg_a, ra);
+    load(j + 2, pg_a, ra);
     pg_cur = pg_a;
-    pg_a = page_of(min(j + 4, ngw - 1));
     __builtin_amdgcn_sched_barrier(0);
-    if (j + 1 < ngw) {
-      visit(pg_nxt);
-      compute(j + 1, rb2);
-    }
-    load(min(j + 3, ngw - 1), pg_b, rb2);
+    visit(pg_nxt);
+    compute(j + 1, rb2);
+    load(j + 3, pg_b, rb2);
     pg_nxt = pg_b;
-    pg_b = page_of(min(j + 5, ngw - 1));
+    if (j + 4 < ngw) pg_a = page_of(j + 4);
+    if (j + 5 < ngw) pg_b = page_of(j + 5);
     __builtin_amdgcn_sched_barrier(0);
+  }
+  if (j < ngw) {
+    visit(pg_cur);
+    compute(j, ra);
+    if (j + 2 < ngw) load(j + 2, pg_a, ra);
+  }
+  if (j + 1 < ngw) {
+    visit(pg_nxt);
+    compute(j + 1, rb2);
+  }
+  if (j + 2 < ngw) {
+    visit(pg_a);
+    compute(j + 2, ra);
   }
 
   // ---- per-wave row totals; then merge the four waves through LDS
@@ -378,65 +395,67 @@ __global__ __launch_bounds__(256) void gqa_partial_kernel(PartialParams p) {
   }
   __syncthreads();
 
-  const bool direct = p.direct && nsplit == 1;
+  const bool direct = a.direct && nsplit == 1;
+  const int64_t R = a.R;
   {
-    const int r = threadIdx.x >> 4;       // row within the block
-    const int part = threadIdx.x & 15;    // D/16 features each
-    const int grow = rb * 16 + r;
-    if (grow < p.rows) {
-      // each wave's (l, o) is relative to its reference max; bring all four
-      // to the block's true max
-      float M = sm_m[0][r];
+    // Wave w merges rows w, w+4, w+8, w+12 of the block (those that are real
+    // query rows): the per-row values are wave-uniform, so they are computed
+    // once per row in scalar registers, and each lane merges one float4 of
+    // features from the four waves' LDS copies.
+    constexpr int F4 = D / 4;
+    const int nrow = min(16, a.rows - rb * 16);
 #pragma unroll
-      for (int w = 1; w < 4; ++w) M = fmaxf(M, sm_m[w][r]);
+    for (int k = 0; k < 4; ++k) {
+      const int r = wave + 4 * k;
+      if (r >= nrow) break;
+      // each wave's (l, o) is relative to its reference max; bring all four
+      // to the block's true max (reference maxima never exceed the true one)
+      const float M = fmaxf(fmaxf(sm_m[0][r], sm_m[1][r]), fmaxf(sm_m[2][r], sm_m[3][r]));
       float wgt[4], Lsum = 0.f;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         const float mr = sm_r[w][r];
-        wgt[w] = mr == -INFINITY ? 0.f : exp2f(mr - M);
+        wgt[w] = mr == -INFINITY ? 0.f : fast_exp2(mr - M);
         Lsum += wgt[w] * sm_l[w][r];
       }
-      const int tt = grow / p.g, hh = hk * p.g + grow % p.g;
-      const int64_t R = int64_t(p.T) * p.Hq;
-      const int64_t rix = int64_t(tt) * p.Hq + hh;
-      float mul = p.v_scale;
-      if (direct) mul = Lsum > 0.f ? p.v_scale / Lsum : 0.f;
-      constexpr int PER = D / 16;
+      const int grow = rb * 16 + r;
+      const int tt = grow / a.g, hh = hk * a.g + grow - (grow / a.g) * a.g;
+      const int64_t rix = int64_t(tt) * a.Hq + hh;
+      const bool empty = M == -INFINITY;
+      const float mul = direct ? (Lsum > 0.f ? a.v_scale / Lsum : 0.f) : a.v_scale;
+      const int64_t obase = ((direct ? int64_t(b) : int64_t(slot)) * R + rix) * D;
 #pragma unroll
-      for (int k4 = 0; k4 < PER / 4; ++k4) {
-        const int d = part * PER + 4 * k4;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int f0 = 0; f0 < F4; f0 += 64) {
+        const int f = f0 + lane;
+        if (F4 % 64 != 0 && f >= F4) break;
+        f32x4 acc = wgt[0] * *reinterpret_cast<const f32x4*>(&sm_o[0][r][4 * f]);
 #pragma unroll
-        for (int w = 0; w < 4; ++w)
-          acc += wgt[w] * *reinterpret_cast<const f32x4*>(&sm_o[w][r][d]);
+        for (int w = 1; w < 4; ++w) acc += wgt[w] * *reinterpret_cast<const f32x4*>(&sm_o[w][r][4 * f]);
         acc *= mul;
+        const int64_t o = obase + 4 * f;
         if (direct) {
-          const int64_t o = (int64_t(b) * R + rix) * D + d;
-          if (p.out_f32) {
-            *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + o) = acc;
+          if (a.out_f32) {
+            *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + o) = acc;
           } else {
             u32x2 pk = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
-            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + o) = pk;
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + o) = pk;
           }
         } else {
-          const int64_t o = (int64_t(slot) * R + rix) * D + d;
-          *reinterpret_cast<f32x4*>(p.part_o + o) = acc;
+          *reinterpret_cast<f32x4*>(a.part_o + o) = acc;
         }
       }
-      if (part == 0) {
-        const bool empty = M == -INFINITY;
+      if (lane == 0) {
         if (direct) {
-          if (p.lse)
-            p.lse[int64_t(b) * R + rix] =
-                (empty || !(Lsum > 0.f)) ? -INFINITY : (M + log2f(Lsum)) * kLn2;
+          if (a.lse)
+            a.lse[int64_t(b) * R + rix] = (empty || !(Lsum > 0.f)) ? -INFINITY : (M + log2f(Lsum)) * kLn2;
         } else {
-          p.part_m[int64_t(slot) * R + rix] = empty ? -INFINITY : M * kLn2;
-          p.part_l[int64_t(slot) * R + rix] = Lsum;
+          a.part_m[int64_t(slot) * R + rix] = empty ? -INFINITY : M * kLn2;
+          a.part_l[int64_t(slot) * R + rix] = Lsum;
         }
       }
     }
   }
-  if (p.debug && threadIdx.x == 0) {
+  if (a.debug && threadIdx.x == 0) {
     int groups = 0, x = 0;
     uint32_t sum = 0;
     for (int w = 0; w < 4; ++w) {
@@ -444,7 +463,7 @@ __global__ __launch_bounds__(256) void gqa_partial_kernel(PartialParams p) {
       x ^= sm_dbg[w][1];
       sum += uint32_t(sm_dbg[w][2]);
     }
-    int32_t* rec = p.debug + ((int64_t(slot) * p.Hkv + hk) * p.row_blocks + rb) * 8;
+    int32_t* rec = a.debug + ((int64_t(slot) * Hkv + hk) * RB + rb) * 8;
     rec[0] = b;
     rec[1] = split;
     rec[2] = hk;
@@ -458,12 +477,45 @@ __global__ __launch_bounds__(256) void gqa_partial_kernel(PartialParams p) {
 
 // Host launcher: grid = slots x KV heads x row blocks, 256 threads.
 hipError_t launch_gqa_partial(const PartialParams& p, int D, bool fp8, hipStream_t stream) {
+  GqaRest a;
+  a.qsb = int32_t(p.qsb);
+  a.qst = int32_t(p.qst);
+  a.qsh = int32_t(p.qsh);
+  a.ksp = int32_t(p.ksp);
+  a.ksh = int32_t(p.ksh);
+  a.kst = int32_t(p.kst);
+  a.vsp = int32_t(p.vsp);
+  a.vsh = int32_t(p.vsh);
+  a.vst = int32_t(p.vst);
+  a.T = p.T;
+  a.Hq = p.Hq;
+  a.g = p.g;
+  a.page_size = p.page_size;
+  a.rows = p.rows;
+  a.R = p.T * p.Hq;
+  a.scale_log2 = p.scale_log2;
+  a.v_scale = p.v_scale;
+  a.seq_lens = p.seq_lens;
+  a.part_m = p.part_m;
+  a.part_l = p.part_l;
+  a.part_o = p.part_o;
+  a.out = p.out;
+  a.lse = p.lse;
+  a.debug = p.debug;
+  a.out_f32 = p.out_f32;
+  a.direct = p.direct;
+  const int32_t geom = (p.Hkv & 0xffff) | ((p.row_blocks & 0xff) << 16) | ((p.page_shift + 1) << 24);
+  const int32_t bt_stride = int32_t(p.bt_stride);
   const dim3 grid(p.total_wg), block(256);
-  if (D == 128 && !fp8) hipLaunchKernelGGL((gqa_partial_kernel<128, false>), grid, block, 0, stream, p);
-  else if (D == 256 && !fp8) hipLaunchKernelGGL((gqa_partial_kernel<256, false>), grid, block, 0, stream, p);
-  else if (D == 128 && fp8) hipLaunchKernelGGL((gqa_partial_kernel<128, true>), grid, block, 0, stream, p);
-  else if (D == 256 && fp8) hipLaunchKernelGGL((gqa_partial_kernel<256, true>), grid, block, 0, stream, p);
+#define SPLITKV_LAUNCH(DD, F8)                                                                     \
+  hipLaunchKernelGGL((gqa_partial_kernel<DD, F8>), grid, block, 0, stream, p.bt, p.slot_info, p.q, \
+                     p.k, p.v, bt_stride, geom, a)
+  if (D == 128 && !fp8) SPLITKV_LAUNCH(128, false);
+  else if (D == 256 && !fp8) SPLITKV_LAUNCH(256, false);
+  else if (D == 128 && fp8) SPLITKV_LAUNCH(128, true);
+  else if (D == 256 && fp8) SPLITKV_LAUNCH(256, true);
   else return hipErrorInvalidValue;
+#undef SPLITKV_LAUNCH
   return hipGetLastError();
 }
 

@@ -88,9 +88,9 @@ def test_auto_plan_targets_two_wg_per_cu():
                                num_cus=256, rows_per_wg=16)
     assert ns.tolist() == [16] * 8                # chunk = ceil(8*32000*4/512) = 2000
     # minimum chunk: short sequences get one split
-    ns, _, _ = P.make_plan([100, 300, 600], T=1, Hq=8, Hkv=2, requested=0, max_splits=64,
+    ns, _, _ = P.make_plan([90, 300, 600], T=1, Hq=8, Hkv=2, requested=0, max_splits=64,
                            num_cus=256, rows_per_wg=16)
-    assert ns.tolist() == [1, 1, 2]               # chunk = AUTO_MIN_TOKENS = 256, floor
+    assert ns.tolist() == [1, 3, 6]               # chunk = AUTO_MIN_TOKENS = 96, floor
     # slot_info holds (b, n << 16 | i, start, end)
     ns, off, info = P.make_plan([40, 5000], T=1, Hq=8, Hkv=2, requested=3, max_splits=64,
                                 num_cus=256, rows_per_wg=16)
