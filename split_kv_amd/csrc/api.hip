@@ -111,6 +111,11 @@ splitkv_status check_partial(const splitkv_args* a, Kind kind, bool need_ws, con
     if (a->Hkv != 1 || a->d_qk != 576 || a->d_v != 512)
       return fail(SPLITKV_ERR_UNSUPPORTED, "%s: MLA needs Hkv=1, d_qk=576, d_v=512 (got %d, %d, %d)",
                   fn, a->Hkv, a->d_qk, a->d_v);
+    if ((a->page_size & (a->page_size - 1)) != 0)
+      return fail(SPLITKV_ERR_UNSUPPORTED, "%s: MLA needs a power-of-two page size (got %d)", fn,
+                  a->page_size);
+    if (a->k_stride_page * 2 > INT32_MAX || a->k_stride_tok * 2 > INT32_MAX)
+      return fail(SPLITKV_ERR_UNSUPPORTED, "%s: MLA cache strides must fit 31 bits", fn);
   } else if (a->d_qk != a->d_v || (a->d_qk != 128 && a->d_qk != 256)) {
     return fail(SPLITKV_ERR_UNSUPPORTED, "%s: head dims d_qk=%d d_v=%d; built for 128 and 256", fn,
                 a->d_qk, a->d_v);
