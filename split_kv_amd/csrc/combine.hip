@@ -22,38 +22,42 @@ namespace splitkv {
 constexpr int kCombineCols = 16;                // float4 columns per workgroup (64 features)
 constexpr int kCombineGroups = 256 / kCombineCols;
 
-// Arguments read after the preloaded ones.
-struct CombineRest {
-  void* out;
-  float* lse;
-  int32_t out_f32, d_v, skip_single;
-};
-
-// The first argument dwords (partial and plan pointers, the row geometry) are
-// preloaded into scalar registers at wave launch, so the plan read is the
-// first memory access.
-__global__ __launch_bounds__(256) void combine_kernel(const float* part_m, const float* part_l,
-                                                      const float* part_o, const int32_t* num_splits,
-                                                      const int32_t* slot_offset, int32_t R,
-                                                      int32_t dsplit, CombineRest p) {
+// All fourteen argument dwords (workspace, plan, output and log-sum-exp
+// pointers, the row geometry and flags) are preloaded into scalar registers
+// at wave launch, so the two plan reads of the row's sequence are the first
+// memory accesses, issued together, and the stores need no argument load.
+// part_l and part_o follow part_m in the workspace: part_l at SR floats
+// (SR = total_slots * rows per sequence), part_o at the next 256-byte
+// boundary after 2 * SR floats.  The merge runs in base 2 on the hardware
+// exponential (every argument is <= 0: a difference from the running max).
+// flags: d_v (bits 0-15) | skip rows of single-split sequences (bit 16) |
+// fp32 output (bit 17).
+__global__ __launch_bounds__(256) void combine_kernel(const float* part_m, const int32_t* num_splits,
+                                                      const int32_t* slot_offset, void* out,
+                                                      float* lse, int32_t R, int32_t dsplit,
+                                                      int32_t flags, int32_t SR) {
   constexpr int CH = kCombineCols, G = kCombineGroups, U = 8;
   __shared__ float red_m[G][CH], red_l[G][CH];
   __shared__ f32x4 red_o[G][CH];
 
   const int tid = threadIdx.x;
-  const int64_t row = blockIdx.x / dsplit;
-  const int part = blockIdx.x % dsplit;
-  const int b = int(row / R);
-  const int64_t rix = row % R;
+  const int row = int(blockIdx.x) / dsplit;
+  const int part = int(blockIdx.x) - row * dsplit;
+  const int b = row / R;
+  const int rix = row - b * R;
   const int n = ((cint32*)num_splits)[b];
-  const int64_t base = ((cint32*)slot_offset)[b];
-  if (p.skip_single && n == 1) return;
+  const int base = ((cint32*)slot_offset)[b];
+  asm volatile("" :: "s"(n), "s"(base));   // both reads in flight before either is used
+  if ((flags & (1 << 16)) && n == 1) return;
+  const int DV = flags & 0xffff;
   const int c = tid % CH, g = tid / CH;
-  const int DV = p.d_v;
+  const float* part_l = part_m + SR;
+  const float* part_o = part_m + (int64_t(2) * SR * 4 + 255) / 256 * 64;
 
-  float M = -INFINITY, lam = 0.f;
+  // running state in base 2: M2 = max of m_i * log2(e)
+  float M2 = -INFINITY, lam = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  const float* po = part_o + rix * DV + 64 * part + 4 * c;
+  const float* po = part_o + int64_t(rix) * DV + 64 * part + 4 * c;
   const int64_t step = int64_t(R) * DV;
   for (int i0 = g; i0 < n; i0 += U * G) {
     float mi[U], li[U];
@@ -70,15 +74,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* part_m, const
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (mi[u] == -INFINITY) continue;                  // empty split: zero weight
-      const float Mn = fmaxf(M, mi[u]);
-      const float a = M == -INFINITY ? 0.f : expf(M - Mn);
-      const float w = expf(mi[u] - Mn);
+      const float m2 = mi[u] * kLog2e;
+      const float Mn = fmaxf(M2, m2);
+      const float a = fast_exp2(M2 - Mn);                 // 0 while M2 is -inf
+      const float w = fast_exp2(m2 - Mn);
       lam = lam * a + w * li[u];
       acc = acc * a + w * oi[u];
-      M = Mn;
+      M2 = Mn;
     }
   }
-  red_m[g][c] = M;
+  red_m[g][c] = M2;
   red_l[g][c] = lam;
   red_o[g][c] = acc;
   __syncthreads();
@@ -91,37 +96,35 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* part_m, const
 #pragma unroll
     for (int k = 0; k < G; ++k) {
       const float mk = red_m[k][c];
-      if (mk == -INFINITY) continue;
-      const float w = expf(mk - Mt);
+      const float w = mk == -INFINITY ? 0.f : fast_exp2(mk - Mt);
       lt += w * red_l[k][c];
       ot += w * red_o[k][c];
     }
     const bool ok = Mt != -INFINITY && lt > 0.f;
     ot *= ok ? 1.f / lt : 0.f;
-    const int64_t o = row * DV + 64 * part + 4 * c;
-    if (p.out_f32) {
-      *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + o) = ot;
+    const int64_t o = int64_t(row) * DV + 64 * part + 4 * c;
+    if (flags & (1 << 17)) {
+      *reinterpret_cast<f32x4*>(static_cast<float*>(out) + o) = ot;
     } else {
       u32x2 pk = {pack_bf16x2(ot[0], ot[1]), pack_bf16x2(ot[2], ot[3])};
-      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + o) = pk;
+      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + o) = pk;
     }
-    if (p.lse && part == 0 && c == 0) p.lse[row] = ok ? Mt + logf(lt) : -INFINITY;
+    if (lse && part == 0 && c == 0) lse[row] = ok ? (Mt + log2f(lt)) * kLn2 : -INFINITY;
   }
 }
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
-  if (p.d_v % 64 != 0) return hipErrorInvalidValue;
+  if (p.d_v % 64 != 0 || p.d_v > 0xffff) return hipErrorInvalidValue;
   const int dsplit = p.d_v / 64;
   const int64_t wgs = int64_t(p.B) * p.R * dsplit;
+  const int64_t SR = p.part_l - p.part_m;
+  if (wgs > INT32_MAX || SR > INT32_MAX / 8 ||
+      p.part_o != p.part_m + (2 * SR * 4 + 255) / 256 * 64)
+    return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(wgs)), block(256);
-  CombineRest r;
-  r.out = p.out;
-  r.lse = p.lse;
-  r.out_f32 = p.out_f32;
-  r.d_v = p.d_v;
-  r.skip_single = p.skip_single;
-  hipLaunchKernelGGL(combine_kernel, grid, block, 0, stream, p.part_m, p.part_l, p.part_o,
-                     p.num_splits, p.slot_offset, p.R, dsplit, r);
+  const int32_t flags = p.d_v | (p.skip_single ? 1 << 16 : 0) | (p.out_f32 ? 1 << 17 : 0);
+  hipLaunchKernelGGL(combine_kernel, grid, block, 0, stream, p.part_m, p.num_splits, p.slot_offset,
+                     p.out, p.lse, p.R, dsplit, flags, int32_t(SR));
   return hipGetLastError();
 }
 
