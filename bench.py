@@ -46,7 +46,7 @@ def parse():
     ap.add_argument("--workload", default="few-kv-long",
                     choices=["few-kv-long", "fp8-batched", "mla", "ragged", "tiny-gqa"],
                     help="few-kv-long is the headline; the others are extra measurements")
-    ap.add_argument("--L", type=int, default=None, help="sequence length (few-kv-long, mla)")
+    ap.add_argument("--L", type=int, default=None, help="sequence length (few-kv-long, mla, tiny-gqa)")
     ap.add_argument("--sweep", type=str, default="1,2,3,4,6,8,12,16,24,32,48,64,96,128,192,256",
                     help="comma-separated num_splits to sweep ('' to skip); the workload's own "
                          "sweep is 1..64, larger counts are extra points")
@@ -71,7 +71,7 @@ def make_workload(name, L):
         return synth.mla_decode(L=L or 65536)
     if name == "ragged":
         return synth.ragged()
-    return synth.tiny_gqa()
+    return synth.tiny_gqa(L=L or 256)
 
 
 def describe(case, name):
@@ -84,7 +84,8 @@ def describe(case, name):
         return f"MLA decode: B=1 T=6 Hq=128 latent 576/512 L={int(case.seq_lens[0])} P=64 bf16"
     if name == "ragged":
         return f"ragged GQA decode: B=32 Hq=32 Hkv=8 D=128 bf16 P=16, sum L={int(case.seq_lens.sum())}"
-    return "tiny GQA decode: B=1 T=1 Hq=8 Hkv=2 D=128 L=256 contiguous bf16, fp32 out"
+    return (f"tiny GQA decode: B=1 T=1 Hq=8 Hkv=2 D=128 L={int(case.seq_lens[0])} contiguous bf16, "
+            "fp32 out")
 
 
 def cold_copies(case, device, warm):

@@ -81,9 +81,11 @@ typedef int32_t splitkv_status;
 
 /* Split-range contract (see splitkv_plan). */
 #define SPLITKV_GRANULE 16             /* tokens; split ranges start on multiples of it */
-#define SPLITKV_AUTO_MIN_TOKENS 96     /* auto mode: fewest tokens per split */
-#define SPLITKV_AUTO_WG_PER_CU 2       /* auto mode: target GQA workgroups per compute unit */
-#define SPLITKV_AUTO_WG_PER_CU_MLA 1   /* auto mode: target MLA workgroups per compute unit */
+#define SPLITKV_AUTO_SPLIT_MIN_BYTES 196608  /* auto: no split unless a sequence has this many KV bytes per workgroup */
+#define SPLITKV_AUTO_LAT_NUM 3                /* auto: latency floor isqrt(L_max * NUM / DEN) tokens per split */
+#define SPLITKV_AUTO_LAT_DEN 2
+#define SPLITKV_AUTO_BALANCE 4                /* auto: workgroups per compute unit of the balanced candidate */
+#define SPLITKV_AUTO_WG_OVERHEAD_BYTES 32768  /* auto: fixed cost of one workgroup, in bytes of streaming */
 #define SPLITKV_MAX_SPLITS_LIMIT 256   /* upper bound of max_splits */
 #define SPLITKV_ROWS_PER_WG_GQA 16     /* query rows (g*T) one GQA workgroup covers */
 #define SPLITKV_ROWS_PER_WG_MLA 64     /* query rows (T*Hq) one MLA workgroup covers */
@@ -99,6 +101,8 @@ typedef struct {
   int32_t requested_splits;  /* > 0: honoured exactly when <= min(max_splits, nblk); 0: auto */
   int32_t max_splits;        /* 1 .. SPLITKV_MAX_SPLITS_LIMIT */
   int32_t num_cus;           /* > 0: compute units to plan for; 0: query the current device */
+  int32_t d_qk, d_v;         /* head dimensions (auto mode sizes splits in bytes) */
+  int32_t kv_dtype;          /* SPLITKV_KV_BF16 or SPLITKV_KV_E4M3 */
 } splitkv_plan_args;
 
 /*
@@ -108,14 +112,31 @@ typedef struct {
  * min(n, max_splits, nblk) non-empty splits, nblk = ceil(L / 16) (the
  * regression in "vLLM 0.30.0 FA4 SplitKV Bug ...", section "The actual bug is
  * one missing constructor argument", read a stored count of one and gave
- * every other split an empty range).  n == 0 sizes splits for the machine:
- * at most R = SPLITKV_AUTO_WG_PER_CU * num_cus workgroups in total
- * (SPLITKV_AUTO_WG_PER_CU_MLA for the MLA kernel), at least
- * SPLITKV_AUTO_MIN_TOKENS tokens per split, because the merge has a cost that
- * can eat the gain of more splits ("Shipped: 484.5 tok/s on one GB300 ...",
- * section "Why 8 splits lost"): with units = Hkv * ceil(g*T / rows_per_wg)
- * workgroups per split, chunk = max(MIN, ceil(sum_b L_b * units / R)) and
- * n_b = clamp(floor(L_b / chunk), 1, min(max_splits, nblk_b)).
+ * every other split an empty range).
+ *
+ * n == 0 sizes splits for the machine, weighing the merge, which has a cost
+ * that can eat the gain of more splits ("Shipped: 484.5 tok/s on one GB300
+ * ...", section "Why 8 splits lost").  With cap_b = min(max_splits,
+ * max(nblk_b, 1)), units = Hkv * ceil(g*T / rows_per_wg) workgroups per split,
+ * tb = bytes one workgroup streams per token ((d_qk + d_v) * elem for GQA,
+ * d_qk * elem for MLA, whose V is the first d_v features of the same row;
+ * elem = 2 for bf16, 1 for e4m3) and L_max the longest sequence:
+ *   1. if L_max * tb < SPLITKV_AUTO_SPLIT_MIN_BYTES no sequence is split
+ *      (the merge launch would cost more than it saves);
+ *   2. c_lat = max(16, isqrt(L_max * SPLITKV_AUTO_LAT_NUM / SPLITKV_AUTO_LAT_DEN)),
+ *      the tokens per split below which the merge of more partials costs
+ *      more than the shorter split saves;  W = units * sum_b L_b;
+ *   3. candidate A, one round: c = max(c_lat, ceil(W / num_cus)),
+ *      n_b = clamp(floor(L_b / c), 1, cap_b) -- at most one workgroup per
+ *      compute unit when the batch allows it;
+ *      candidate B, balanced: c = max(c_lat, ceil(W / (SPLITKV_AUTO_BALANCE *
+ *      num_cus))), n_b = clamp(ceil(L_b / c), 1, cap_b) -- no workgroup
+ *      longer than c, for batches of unequal lengths;
+ *   4. each candidate's step is estimated by list scheduling its workgroups,
+ *      in launch order (slot by slot, the units of a slot consecutively),
+ *      onto num_cus identical compute units, a workgroup costing
+ *      ceil(SPLITKV_AUTO_WG_OVERHEAD_BYTES / tb) + (end - start) tokens; the
+ *      candidate whose busiest unit finishes first wins, A on a tie.
  *
  * Split i of n covers [16*floor(i*nblk/n), min(L, 16*floor((i+1)*nblk/n))).
  * L == 0 gives one empty split.

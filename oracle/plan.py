@@ -21,26 +21,42 @@ two are compared bit for bit.
 * Granule G = 16 tokens; nblk(L) = ceil(L / G).
 * A request n > 0 is honoured exactly whenever n <= min(max_splits, nblk):
   n_eff = clamp(n, 1, min(max_splits, max(nblk, 1))).
-* Auto mode (n == 0): R = AUTO_WG_PER_CU * num_cus target workgroups
-  (AUTO_WG_PER_CU_MLA for the MLA kernel, whose workgroup fills a CU),
-  units = Hkv * ceil(g*T / rows_per_wg) workgroups per split of a sequence,
-  chunk = max(AUTO_MIN_TOKENS, ceil(sum_b L_b * units / R)),
-  n_b = clamp(floor(L_b / chunk), 1, min(max_splits, max(nblk_b, 1))) -- floor,
-  so the total never exceeds R workgroups (a second partial round of
-  workgroups would double the step time).
+* Auto mode (n == 0) weighs more splits against the merge they add and the
+  start-up latency of every extra workgroup.  Per token a workgroup streams
+  tb = (d_qk + d_v) * elem bytes (MLA: d_qk * elem, V being part of the same
+  row); a split of a sequence is units = Hkv * ceil(g*T / rows_per_wg)
+  workgroups; cap_b = min(max_splits, max(nblk_b, 1)); L_max = max_b L_b.
+  - If L_max * tb < AUTO_SPLIT_MIN_BYTES, every n_b = 1 (nothing to merge).
+  - Latency floor c_lat = max(G, isqrt(L_max * AUTO_LAT_NUM // AUTO_LAT_DEN))
+    tokens per split; W = units * sum_b L_b.
+  - Candidate "one round": c = max(c_lat, ceil(W / num_cus)),
+    n_b = clamp(floor(L_b / c), 1, cap_b).
+  - Candidate "balanced": c = max(c_lat, ceil(W / (AUTO_BALANCE * num_cus))),
+    n_b = clamp(ceil(L_b / c), 1, cap_b).
+  - Each candidate is scored by greedy list scheduling: its workgroups, in
+    launch order (slots in order, the units of a slot one after another),
+    each go to whichever of num_cus compute units is free first, costing
+    ceil(AUTO_WG_OVERHEAD_BYTES / tb) + (end - start) tokens; the score is
+    the latest finish.  The balanced candidate is taken only if its score is
+    strictly lower.
 * Split i of n covers [G*floor(i*nblk/n), min(L, G*floor((i+1)*nblk/n))).
   Because n <= nblk every range holds at least one token, the ranges are
   disjoint and contiguous and their union is [0, L).  L == 0 gives one empty
   range [0, 0).
 """
+import heapq
+import math
+
 import numpy as np
 
 # Constants of the contract (the library publishes its own copies; a test
 # checks that the two agree).
 GRANULE = 16
-AUTO_MIN_TOKENS = 96
-AUTO_WG_PER_CU = 2
-AUTO_WG_PER_CU_MLA = 1
+AUTO_SPLIT_MIN_BYTES = 196608
+AUTO_LAT_NUM = 3
+AUTO_LAT_DEN = 2
+AUTO_BALANCE = 4
+AUTO_WG_OVERHEAD_BYTES = 32768
 MAX_SPLITS_LIMIT = 256
 ROWS_PER_WG_GQA = 16
 ROWS_PER_WG_MLA = 64
@@ -67,25 +83,56 @@ def clamp_request(L: int, n: int, max_splits: int) -> int:
     return max(1, min(int(n), cap))
 
 
+def _latest_finish(L, ns, units, num_cus, overhead):
+    """Greedy list scheduling of the plan's workgroups (in launch order) on num_cus units."""
+    free = [0] * num_cus
+    latest = 0
+    for Lb, n in zip(L, ns):
+        for i in range(n):
+            s, e = split_range(Lb, n, i)
+            for _ in range(units):
+                t = heapq.heappop(free) + overhead + (e - s)
+                latest = max(latest, t)
+                heapq.heappush(free, t)
+    return latest
+
+
+def _auto_counts(L, *, T, Hq, Hkv, max_splits, num_cus, rows_per_wg, d_qk, d_v, elem):
+    mla = rows_per_wg == ROWS_PER_WG_MLA
+    tb = (d_qk if mla else d_qk + d_v) * elem
+    units = Hkv * _ceil_div((Hq // Hkv) * T, rows_per_wg)
+    lmax = max(L)
+    if lmax * tb < AUTO_SPLIT_MIN_BYTES:
+        return [1] * len(L)
+    c_lat = max(GRANULE, math.isqrt(lmax * AUTO_LAT_NUM // AUTO_LAT_DEN))
+    W = units * sum(L)
+    c1 = max(c_lat, _ceil_div(W, num_cus))
+    cb = max(c_lat, _ceil_div(W, AUTO_BALANCE * num_cus))
+    one = [clamp_request(Lb, Lb // c1, max_splits) for Lb in L]
+    bal = [clamp_request(Lb, _ceil_div(Lb, cb), max_splits) for Lb in L]
+    ov = _ceil_div(AUTO_WG_OVERHEAD_BYTES, tb)
+    if _latest_finish(L, bal, units, num_cus, ov) < _latest_finish(L, one, units, num_cus, ov):
+        return bal
+    return one
+
+
 def make_plan(seq_lens, *, T: int, Hq: int, Hkv: int, requested: int, max_splits: int,
-              num_cus: int, rows_per_wg: int):
+              num_cus: int, rows_per_wg: int, d_qk: int = 0, d_v: int = 0, elem: int = 2):
     """Return (num_splits[B], slot_offset[B+1], slot_info[S, 4]) as int32 arrays.
 
     ``slot_info[s]`` is the work record of slot ``s`` (split ``i`` of sequence
     ``b``): ``(b, (n_b << 16) | i, start, end)`` with [start, end) its range.
+    Auto mode (``requested == 0``) needs the head dimensions and the KV element
+    size in bytes (``elem``: 2 for bf16, 1 for e4m3).
     """
     L = [int(x) for x in seq_lens]
-    B = len(L)
     if requested > 0:
         ns = [clamp_request(Lb, requested, max_splits) for Lb in L]
     else:
-        g = Hq // Hkv
-        units = Hkv * _ceil_div(g * T, rows_per_wg)
-        work = sum(L) * units
-        per_cu = AUTO_WG_PER_CU_MLA if rows_per_wg == ROWS_PER_WG_MLA else AUTO_WG_PER_CU
-        target = per_cu * num_cus
-        chunk = max(AUTO_MIN_TOKENS, _ceil_div(work, target))
-        ns = [clamp_request(Lb, Lb // chunk, max_splits) for Lb in L]
+        if d_qk < 1 or d_v < 1:
+            raise ValueError("auto mode needs d_qk and d_v")
+        ns = _auto_counts(L, T=T, Hq=Hq, Hkv=Hkv, max_splits=max_splits, num_cus=num_cus,
+                          rows_per_wg=rows_per_wg, d_qk=d_qk, d_v=d_v, elem=elem)
     off = [0]
     for n in ns:
         off.append(off[-1] + n)

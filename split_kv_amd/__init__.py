@@ -29,9 +29,11 @@ SPLITKV_ERR_LAUNCH = -4
 SPLITKV_ERR_DEVICE = -5
 
 SPLITKV_GRANULE = 16
-SPLITKV_AUTO_MIN_TOKENS = 96
-SPLITKV_AUTO_WG_PER_CU = 2
-SPLITKV_AUTO_WG_PER_CU_MLA = 1
+SPLITKV_AUTO_SPLIT_MIN_BYTES = 196608
+SPLITKV_AUTO_LAT_NUM = 3
+SPLITKV_AUTO_LAT_DEN = 2
+SPLITKV_AUTO_BALANCE = 4
+SPLITKV_AUTO_WG_OVERHEAD_BYTES = 32768
 SPLITKV_MAX_SPLITS_LIMIT = 256
 SPLITKV_ROWS_PER_WG_GQA = 16
 SPLITKV_ROWS_PER_WG_MLA = 64
@@ -49,7 +51,8 @@ c_i32, c_i64, c_f32, c_vp, c_sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float
 
 class splitkv_plan_args(ctypes.Structure):
     _fields_ = [("B", c_i32), ("T", c_i32), ("Hq", c_i32), ("Hkv", c_i32), ("kernel", c_i32),
-                ("requested_splits", c_i32), ("max_splits", c_i32), ("num_cus", c_i32)]
+                ("requested_splits", c_i32), ("max_splits", c_i32), ("num_cus", c_i32),
+                ("d_qk", c_i32), ("d_v", c_i32), ("kv_dtype", c_i32)]
 
 
 class splitkv_args(ctypes.Structure):

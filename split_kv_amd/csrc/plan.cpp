@@ -4,13 +4,19 @@
 // is computed from the runtime value only, never from a stored default (the
 // defect analysed in "vLLM 0.30.0 FA4 SplitKV Bug: H100 Decode Can Be 48%
 // Slower", section "The actual bug is one missing constructor argument").
-// Auto mode aims at SPLITKV_AUTO_WG_PER_CU workgroups per compute unit with a
-// floor of SPLITKV_AUTO_MIN_TOKENS tokens per split, since every extra split
-// adds merge work ("Shipped: 484.5 tok/s on one GB300 ...", section "Why 8
-// splits lost").
+// Auto mode weighs the gain of more splits against their cost -- every extra
+// split adds merge work ("Shipped: 484.5 tok/s on one GB300 ...", section "Why
+// 8 splits lost") and every extra workgroup a fixed start-up latency -- by
+// estimating two candidate plans with a list-scheduling model of the compute
+// units and keeping the faster one.
+#include <algorithm>
+#include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <functional>
+#include <queue>
 #include <string>
+#include <vector>
 
 #include "internal.h"
 
@@ -37,6 +43,69 @@ static int32_t clamp_request(int64_t L, int64_t n, int64_t max_splits) {
   return static_cast<int32_t>(n);
 }
 
+// floor(sqrt(x)) for x >= 0.
+static int64_t isqrt64(int64_t x) {
+  int64_t r = static_cast<int64_t>(std::sqrt(static_cast<double>(x)));
+  while (r > 0 && r * r > x) --r;
+  while ((r + 1) * (r + 1) <= x) ++r;
+  return r;
+}
+
+// Finish time of the busiest compute unit when the plan's workgroups are
+// handed out in launch order (slot by slot, the units of a slot one after
+// another), each to the unit that becomes free first; a workgroup costs
+// `overhead` plus its range length, in tokens.
+static int64_t list_schedule(const int32_t* seq_lens, const std::vector<int32_t>& ns,
+                             int64_t units, int32_t num_cus, int64_t overhead) {
+  std::priority_queue<int64_t, std::vector<int64_t>, std::greater<int64_t>> free_at;
+  for (int32_t c = 0; c < num_cus; ++c) free_at.push(0);
+  int64_t busiest = 0;
+  for (size_t b = 0; b < ns.size(); ++b)
+    for (int32_t i = 0; i < ns[b]; ++i) {
+      int64_t s, e;
+      split_range(seq_lens[b], ns[b], i, &s, &e);
+      for (int64_t u = 0; u < units; ++u) {
+        const int64_t t = free_at.top() + overhead + (e - s);
+        free_at.pop();
+        free_at.push(t);
+        busiest = std::max(busiest, t);
+      }
+    }
+  return busiest;
+}
+
+// Auto split counts (the rule documented at splitkv_plan).
+static void auto_splits(const splitkv_plan_args& a, int32_t num_cus, const int32_t* seq_lens,
+                        int32_t* num_splits) {
+  const int64_t rows_per_wg =
+      a.kernel == SPLITKV_KERNEL_MLA ? SPLITKV_ROWS_PER_WG_MLA : SPLITKV_ROWS_PER_WG_GQA;
+  const int64_t units = int64_t(a.Hkv) * ceil_div(int64_t(a.Hq / a.Hkv) * a.T, rows_per_wg);
+  const int64_t elem = a.kv_dtype == SPLITKV_KV_E4M3 ? 1 : 2;
+  const int64_t tb = (a.kernel == SPLITKV_KERNEL_MLA ? int64_t(a.d_qk) : int64_t(a.d_qk) + a.d_v) * elem;
+  int64_t lmax = 0, sum_len = 0;
+  for (int32_t b = 0; b < a.B; ++b) {
+    lmax = std::max<int64_t>(lmax, seq_lens[b]);
+    sum_len += seq_lens[b];
+  }
+  std::fill(num_splits, num_splits + a.B, 1);
+  if (lmax * tb < SPLITKV_AUTO_SPLIT_MIN_BYTES) return;
+  const int64_t c_lat =
+      std::max<int64_t>(SPLITKV_GRANULE, isqrt64(lmax * SPLITKV_AUTO_LAT_NUM / SPLITKV_AUTO_LAT_DEN));
+  const int64_t work = sum_len > (INT64_MAX / 4) / units ? INT64_MAX / 4 : sum_len * units;
+  const int64_t c_one = std::max(c_lat, ceil_div(work, int64_t(num_cus)));
+  const int64_t c_bal = std::max(c_lat, ceil_div(work, int64_t(SPLITKV_AUTO_BALANCE) * num_cus));
+  std::vector<int32_t> one(a.B), bal(a.B);
+  for (int32_t b = 0; b < a.B; ++b) {
+    const int64_t L = seq_lens[b];
+    one[b] = clamp_request(L, L / c_one, a.max_splits);
+    bal[b] = clamp_request(L, ceil_div(L, c_bal), a.max_splits);
+  }
+  const int64_t overhead = ceil_div(int64_t(SPLITKV_AUTO_WG_OVERHEAD_BYTES), tb);
+  const bool take_bal = list_schedule(seq_lens, bal, units, num_cus, overhead) <
+                        list_schedule(seq_lens, one, units, num_cus, overhead);
+  std::copy((take_bal ? bal : one).begin(), (take_bal ? bal : one).end(), num_splits);
+}
+
 splitkv_status plan_host(const splitkv_plan_args& a, int32_t num_cus, const int32_t* seq_lens,
                          int32_t* num_splits, int32_t* slot_offset, int32_t* slot_info,
                          int32_t slot_info_capacity, int32_t* total_slots) {
@@ -54,32 +123,20 @@ splitkv_status plan_host(const splitkv_plan_args& a, int32_t num_cus, const int3
   if (a.kernel != SPLITKV_KERNEL_GQA && a.kernel != SPLITKV_KERNEL_MLA)
     return fail(SPLITKV_ERR_INVALID_ARG, "splitkv_plan: unknown kernel %d", a.kernel);
   if (num_cus < 1) return fail(SPLITKV_ERR_INVALID_ARG, "splitkv_plan: num_cus=%d", num_cus);
-  int64_t sum_len = 0;
-  for (int32_t b = 0; b < a.B; ++b) {
+  if (a.d_qk < 1 || a.d_v < 1 || (a.kv_dtype != SPLITKV_KV_BF16 && a.kv_dtype != SPLITKV_KV_E4M3))
+    return fail(SPLITKV_ERR_INVALID_ARG, "splitkv_plan: d_qk=%d d_v=%d kv_dtype=%d", a.d_qk, a.d_v,
+                a.kv_dtype);
+  for (int32_t b = 0; b < a.B; ++b)
     if (seq_lens[b] < 0)
       return fail(SPLITKV_ERR_INVALID_ARG, "splitkv_plan: seq_lens[%d]=%d < 0", b, seq_lens[b]);
-    sum_len += seq_lens[b];
-  }
-  int64_t chunk = 0;
-  if (a.requested_splits == 0) {
-    const int64_t rows_per_wg =
-        a.kernel == SPLITKV_KERNEL_MLA ? SPLITKV_ROWS_PER_WG_MLA : SPLITKV_ROWS_PER_WG_GQA;
-    const int64_t g = a.Hq / a.Hkv;
-    const int64_t units = int64_t(a.Hkv) * ceil_div(g * a.T, rows_per_wg);
-    // an MLA workgroup fills a compute unit; grouped-query workgroups fit two
-    const int64_t per_cu =
-        a.kernel == SPLITKV_KERNEL_MLA ? SPLITKV_AUTO_WG_PER_CU_MLA : SPLITKV_AUTO_WG_PER_CU;
-    const int64_t target = per_cu * num_cus;
-    chunk = ceil_div(sum_len * units, target);
-    if (chunk < SPLITKV_AUTO_MIN_TOKENS) chunk = SPLITKV_AUTO_MIN_TOKENS;
-  }
+  if (a.requested_splits == 0)
+    auto_splits(a, num_cus, seq_lens, num_splits);
+  else
+    for (int32_t b = 0; b < a.B; ++b)
+      num_splits[b] = clamp_request(seq_lens[b], a.requested_splits, a.max_splits);
   int64_t off = 0;
   slot_offset[0] = 0;
   for (int32_t b = 0; b < a.B; ++b) {
-    const int64_t L = seq_lens[b];
-    // auto: floor, so the plan never asks for more than the target workgroups
-    const int64_t want = a.requested_splits > 0 ? a.requested_splits : L / chunk;
-    num_splits[b] = clamp_request(L, want, a.max_splits);
     off += num_splits[b];
     if (off > INT32_MAX) return fail(SPLITKV_ERR_INVALID_ARG, "splitkv_plan: too many slots");
     slot_offset[b + 1] = static_cast<int32_t>(off);

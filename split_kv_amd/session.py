@@ -12,7 +12,7 @@ from __future__ import annotations
 import numpy as np
 
 from . import (SPLITKV_KERNEL_GQA, SPLITKV_KERNEL_MLA, SPLITKV_KV_BF16, SPLITKV_KV_E4M3,
-               SPLITKV_OUT_BF16, SPLITKV_OUT_F32, SPLITKV_ROWS_PER_WG_GQA, SPLITKV_ROWS_PER_WG_MLA,
+               SPLITKV_MAX_SPLITS_LIMIT, SPLITKV_OUT_BF16, SPLITKV_OUT_F32, SPLITKV_ROWS_PER_WG_GQA, SPLITKV_ROWS_PER_WG_MLA,
                splitkv_args, splitkv_combine, splitkv_decode, splitkv_decode_partial,
                splitkv_decode_partial_fp8, splitkv_mla_decode_partial, splitkv_plan,
                splitkv_plan_args, splitkv_workspace_bytes)
@@ -36,7 +36,7 @@ class DecodeSession:
 
     def __init__(self, *, q, k_cache, v_cache, block_table, seq_lens, scale: float,
                  k_scale: float = 1.0, v_scale: float = 1.0, mla: bool = False,
-                 requested_splits: int = 0, max_splits: int = 64, num_cus: int = 0,
+                 requested_splits: int = 0, max_splits: int = SPLITKV_MAX_SPLITS_LIMIT, num_cus: int = 0,
                  out_fp32: bool = False, with_lse: bool = True, debug: bool = False):
         torch = _torch()
         self.torch = torch
@@ -69,7 +69,8 @@ class DecodeSession:
         s = self.shape
         pa = splitkv_plan_args(B=s["B"], T=s["T"], Hq=s["Hq"], Hkv=s["Hkv"], kernel=self.kernel,
                                requested_splits=requested_splits, max_splits=self.max_splits,
-                               num_cus=self.num_cus)
+                               num_cus=self.num_cus, d_qk=s["d_qk"], d_v=s["d_v"],
+                               kv_dtype=self.kv_dtype)
         ns, off, info = splitkv_plan(pa, self.seq_lens_host)
         self.requested_splits = requested_splits
         self.num_splits_host, self.slot_offset_host, self.slot_info_host = ns, off, info

@@ -39,15 +39,17 @@ def test_struct_layouts_match():
 
 def test_constants_agree_with_oracle():
     assert sk.SPLITKV_GRANULE == oplan.GRANULE
-    assert sk.SPLITKV_AUTO_MIN_TOKENS == oplan.AUTO_MIN_TOKENS
-    assert sk.SPLITKV_AUTO_WG_PER_CU == oplan.AUTO_WG_PER_CU
-    assert sk.SPLITKV_AUTO_WG_PER_CU_MLA == oplan.AUTO_WG_PER_CU_MLA
+    assert sk.SPLITKV_AUTO_SPLIT_MIN_BYTES == oplan.AUTO_SPLIT_MIN_BYTES
+    assert sk.SPLITKV_AUTO_LAT_NUM == oplan.AUTO_LAT_NUM
+    assert sk.SPLITKV_AUTO_LAT_DEN == oplan.AUTO_LAT_DEN
+    assert sk.SPLITKV_AUTO_BALANCE == oplan.AUTO_BALANCE
+    assert sk.SPLITKV_AUTO_WG_OVERHEAD_BYTES == oplan.AUTO_WG_OVERHEAD_BYTES
     assert sk.SPLITKV_MAX_SPLITS_LIMIT == oplan.MAX_SPLITS_LIMIT
     assert sk.SPLITKV_ROWS_PER_WG_GQA == oplan.ROWS_PER_WG_GQA
     assert sk.SPLITKV_ROWS_PER_WG_MLA == oplan.ROWS_PER_WG_MLA
     header = open(os.path.join(ROOT, "include", "splitkv.h")).read()
-    for name in ("GRANULE", "AUTO_MIN_TOKENS", "AUTO_WG_PER_CU", "AUTO_WG_PER_CU_MLA", "MAX_SPLITS_LIMIT",
-                 "ROWS_PER_WG_GQA", "ROWS_PER_WG_MLA"):
+    for name in ("GRANULE", "AUTO_SPLIT_MIN_BYTES", "AUTO_LAT_NUM", "AUTO_LAT_DEN", "AUTO_BALANCE",
+                 "AUTO_WG_OVERHEAD_BYTES", "MAX_SPLITS_LIMIT", "ROWS_PER_WG_GQA", "ROWS_PER_WG_MLA"):
         m = re.search(rf"#define SPLITKV_{name} (\d+)", header)
         assert int(m.group(1)) == getattr(sk, f"SPLITKV_{name}")
 
@@ -63,38 +65,52 @@ def test_split_range_matches_oracle():
                 assert sk.splitkv_split_range(L, n, i) == oplan.split_range(L, n, i)
 
 
-def _plan(lens, T, Hq, Hkv, kernel, req, mx, cus):
+def _plan(lens, T, Hq, Hkv, kernel, req, mx, cus, d_qk=128, d_v=128, kv=sk.SPLITKV_KV_BF16):
     pa = sk.splitkv_plan_args(B=len(lens), T=T, Hq=Hq, Hkv=Hkv, kernel=kernel, requested_splits=req,
-                              max_splits=mx, num_cus=cus)
+                              max_splits=mx, num_cus=cus, d_qk=d_qk, d_v=d_v, kv_dtype=kv)
     return sk.splitkv_plan(pa, lens)
+
+
+def _oplan(lens, T, Hq, Hkv, kernel, req, mx, cus, d_qk=128, d_v=128, kv=sk.SPLITKV_KV_BF16):
+    rpw = oplan.ROWS_PER_WG_MLA if kernel == sk.SPLITKV_KERNEL_MLA else oplan.ROWS_PER_WG_GQA
+    return oplan.make_plan(lens, T=T, Hq=Hq, Hkv=Hkv, requested=req, max_splits=mx, num_cus=cus,
+                           rows_per_wg=rpw, d_qk=d_qk, d_v=d_v,
+                           elem=1 if kv == sk.SPLITKV_KV_E4M3 else 2)
+
+
+# (d_qk, d_v, kv dtype) per kernel: the configurations the kernels are built for
+HEADS = {sk.SPLITKV_KERNEL_GQA: [(128, 128, sk.SPLITKV_KV_BF16), (256, 256, sk.SPLITKV_KV_BF16),
+                                 (128, 128, sk.SPLITKV_KV_E4M3)],
+         sk.SPLITKV_KERNEL_MLA: [(576, 512, sk.SPLITKV_KV_BF16)]}
 
 
 @pytest.mark.parametrize("kernel", [sk.SPLITKV_KERNEL_GQA, sk.SPLITKV_KERNEL_MLA])
 def test_planner_bit_exact_against_oracle(kernel):
     _lib()
-    rpw = oplan.ROWS_PER_WG_MLA if kernel == sk.SPLITKV_KERNEL_MLA else oplan.ROWS_PER_WG_GQA
-    rng = np.random.default_rng(0)
     shapes = [(1, 16, 2), (1, 32, 4), (6, 128, 1), (1, 32, 8), (2, 8, 2)]
     for L in list(range(0, 4097, 37)) + [5900, 32000, 65536, 131072]:
         for (T, Hq, Hkv) in shapes:
             for n in (0, 1, 2, 3, 8, 17, 64):
                 for mx in (1, 8, 64, 256):
                     for cus in (1, 80, 256):
-                        got = _plan([L], T, Hq, Hkv, kernel, n, mx, cus)
-                        ref = oplan.make_plan([L], T=T, Hq=Hq, Hkv=Hkv, requested=n,
-                                              max_splits=mx, num_cus=cus, rows_per_wg=rpw)
+                        for hd in HEADS[kernel]:
+                            got = _plan([L], T, Hq, Hkv, kernel, n, mx, cus, *hd)
+                            ref = _oplan([L], T, Hq, Hkv, kernel, n, mx, cus, *hd)
+                            for a, b in zip(got, ref):
+                                assert np.array_equal(a, b), (L, T, Hq, Hkv, n, mx, cus, hd)
+    # batches: ragged ones as the ragged workload draws them, and uniform ones
+    import synth
+    batches = [synth.log_uniform_lengths(np.random.default_rng(seed), 32) for seed in range(20)]
+    batches += [[32000] * 8, [5900] * 3, [1, 2, 15, 16, 17, 255, 131072], [300] * 64, [0, 0, 7]]
+    for lens in batches:
+        for (T, Hq, Hkv) in [(1, 32, 8), (1, 32, 4), (6, 128, 1)]:
+            for n in (0, 1, 4, 16, 64):
+                for mx in (64, 256):
+                    for hd in HEADS[kernel]:
+                        got = _plan(lens, T, Hq, Hkv, kernel, n, mx, 256, *hd)
+                        ref = _oplan(lens, T, Hq, Hkv, kernel, n, mx, 256, *hd)
                         for a, b in zip(got, ref):
-                            assert np.array_equal(a, b), (L, T, Hq, Hkv, n, mx, cus)
-    # ragged batches as the ragged workload draws them
-    for seed in range(20):
-        import synth
-        lens = synth.log_uniform_lengths(np.random.default_rng(seed), 32)
-        for n in (0, 1, 4, 16, 64):
-            got = _plan(lens, 1, 32, 8, kernel, n, 64, 256)
-            ref = oplan.make_plan(lens, T=1, Hq=32, Hkv=8, requested=n, max_splits=64,
-                                  num_cus=256, rows_per_wg=rpw)
-            for a, b in zip(got, ref):
-                assert np.array_equal(a, b)
+                            assert np.array_equal(a, b), (lens, T, Hq, Hkv, n, mx, hd)
 
 
 def test_requested_count_is_honoured():
@@ -114,6 +130,10 @@ def test_plan_errors():
         _plan([-1], 1, 16, 2, 0, 1, 64, 256)            # negative length
     with pytest.raises(sk.SplitKVError):
         _plan([10], 1, 16, 2, 7, 1, 64, 256)            # unknown kernel
+    with pytest.raises(sk.SplitKVError):
+        _plan([10], 1, 16, 2, 0, 0, 64, 256, d_qk=0)    # head dimension missing
+    with pytest.raises(sk.SplitKVError):
+        _plan([10], 1, 16, 2, 0, 0, 64, 256, kv=5)      # unknown KV dtype
 
 
 def test_workspace_bytes():

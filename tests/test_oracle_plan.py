@@ -66,31 +66,66 @@ def test_clamps():
     assert P.split_range(0, 1, 0) == (0, 0)
 
 
-def test_auto_plan_never_exceeds_target():
-    # the floor keeps sum_b n_b * units <= target workgroups
-    import numpy as np
+def _auto(lens, *, T=1, Hq=16, Hkv=2, d=(256, 256), elem=2, cus=256, rpw=16, mx=256):
+    return P.make_plan(lens, T=T, Hq=Hq, Hkv=Hkv, requested=0, max_splits=mx, num_cus=cus,
+                       rows_per_wg=rpw, d_qk=d[0], d_v=d[1], elem=elem)[0].tolist()
+
+
+def test_auto_plan_invariants():
     rng = np.random.default_rng(3)
-    for _ in range(200):
+    for _ in range(150):
         B = int(rng.integers(1, 40))
         lens = rng.integers(0, 200000, size=B).tolist()
-        for (T, Hq, Hkv, rpw) in [(1, 32, 8, 16), (6, 128, 1, 64), (1, 16, 2, 16)]:
-            ns, off, _ = P.make_plan(lens, T=T, Hq=Hq, Hkv=Hkv, requested=0, max_splits=256,
-                                     num_cus=256, rows_per_wg=rpw)
-            units = Hkv * -(-(Hq // Hkv) * T // rpw)
-            per_cu = P.AUTO_WG_PER_CU_MLA if rpw == 64 else P.AUTO_WG_PER_CU
-            over = [n for n, Lb in zip(ns, lens) if n > 1]
-            assert sum(over) * units <= per_cu * 256 or not over
+        for (T, Hq, Hkv, rpw, d, elem) in [(1, 32, 8, 16, (128, 128), 2), (6, 128, 1, 64, (576, 512), 2),
+                                           (1, 16, 2, 16, (256, 256), 2), (1, 32, 4, 16, (128, 128), 1)]:
+            ns = _auto(lens, T=T, Hq=Hq, Hkv=Hkv, d=d, elem=elem, rpw=rpw)
+            tb = (d[0] if rpw == 64 else d[0] + d[1]) * elem
+            c_lat = max(16, int(np.floor(np.sqrt(1.5 * max(lens)))) - 1)
+            for n, Lb in zip(ns, lens):
+                assert 1 <= n <= max(1, min(256, -(-Lb // 16)))
+                if Lb < c_lat:
+                    assert n == 1                         # shorter than the latency floor
+            if max(lens) * tb < P.AUTO_SPLIT_MIN_BYTES:
+                assert ns == [1] * B
 
 
-def test_auto_plan_targets_two_wg_per_cu():
-    # 8 x 32000 tokens, 4 KV heads, g=8 rows -> 32 units per split; 512 target WGs
-    ns, off, seq = P.make_plan([32000] * 8, T=1, Hq=32, Hkv=4, requested=0, max_splits=256,
-                               num_cus=256, rows_per_wg=16)
-    assert ns.tolist() == [16] * 8                # chunk = ceil(8*32000*4/512) = 2000
-    # minimum chunk: short sequences get one split
-    ns, _, _ = P.make_plan([90, 300, 600], T=1, Hq=8, Hkv=2, requested=0, max_splits=64,
-                           num_cus=256, rows_per_wg=16)
-    assert ns.tolist() == [1, 3, 6]               # chunk = AUTO_MIN_TOKENS = 96, floor
+def test_auto_plan_worked_examples():
+    # Below the byte threshold nothing is split: D=128 bf16 reads tb = 512 B per
+    # token, and 383 * 512 = 196096 < 196608 <= 384 * 512.
+    assert _auto([383], Hq=8, d=(128, 128)) == [1]
+    # L=384: c_lat = max(16, isqrt(576)) = 24, W = 384 * 2 = 768, so both
+    # candidates use c = 24: floor(384/24) = ceil(384/24) = 16 splits.
+    assert _auto([384], Hq=8, d=(128, 128)) == [16]
+    assert _auto([256], Hq=8, d=(128, 128)) == [1]          # the tiny decode shape
+    # Few-KV-head decode at L=5900, D=256 bf16 (tb = 1024, overhead 32 tokens):
+    # c_lat = isqrt(8850) = 94 (94^2 = 8836); W = 11800 -> c = 94 for both.
+    # one round: floor(5900/94) = 62 splits, ranges of 5 or 6 granules -> the
+    # longest workgroup costs 96 + 32 = 128; balanced: ceil(5900/94) = 63
+    # splits, also at most 6 granules -> 128.  A tie keeps one round.
+    assert _auto([5900]) == [62]
+    # Eight e4m3 sequences of 32000, Hq=32, Hkv=4, D=128 (tb = 256, overhead
+    # 128): units = 4, W = 1024000, c_lat = isqrt(48000) = 219.  One round:
+    # c = 4000 -> 8 splits, 256 workgroups of 4000 tokens -> 4128.  Balanced:
+    # c = 1000 -> 32 splits, 1024 workgroups of ~1000 tokens on 256 units ->
+    # four each, ~4512.  One round wins.
+    assert _auto([32000] * 8, Hq=32, Hkv=4, d=(128, 128), elem=1) == [8] * 8
+    # MLA decode at L=65536 (T=6, 128 heads -> units = 12, tb = 1152):
+    # c_lat = isqrt(98304) = 313; one round: c = 786432/256 = 3072 -> 21
+    # splits, 252 workgroups; balanced: c = 768 -> 86 splits, 1032 workgroups,
+    # about four per unit.  One round wins.
+    assert _auto([65536], T=6, Hq=128, Hkv=1, d=(576, 512), rpw=64) == [21]
+    # Unequal lengths on 4 units (Hq = Hkv = 1 -> units = 1; D=128 bf16, overhead
+    # 64): lens 4096, 3000, 200, 200, W = 7496, c_lat = 78.  One round: c = 1874
+    # -> [2, 1, 1, 1]; the 3000-token workgroup alone costs 3064.  Balanced:
+    # c = ceil(7496/16) = 469 -> [9, 7, 1, 1], 18 workgroups costing 8648 in
+    # total, none above 528, so list scheduling ends by 8648/4 + 528 < 3064.
+    assert _auto([4096, 3000, 200, 200], Hq=1, Hkv=1, d=(128, 128), cus=4) == [9, 7, 1, 1]
+    # max_splits caps the count; nblk caps short sequences
+    assert _auto([5900], mx=16) == [16]
+    assert _auto([0, 0]) == [1, 1]
+
+
+def test_plan_records():
     # slot_info holds (b, n << 16 | i, start, end)
     ns, off, info = P.make_plan([40, 5000], T=1, Hq=8, Hkv=2, requested=3, max_splits=64,
                                 num_cus=256, rows_per_wg=16)
