@@ -8,30 +8,39 @@
 // 128-head shape), 1,671,168 FLOPs per 1152-byte row.  A workgroup keeps 64
 // query rows and streams the split's tokens through LDS in 32-token tiles:
 //   * tiles arrive by direct global->LDS loads (16 bytes per lane, no
-//     register staging) into a ring of three, two tiles ahead of the one
-//     being computed;
-//   * a token's 1152 bytes sit at a pitch of 73 16-byte chunks, which makes
-//     both operand reads conflict-free: sixteen lanes reading one chunk of
-//     sixteen tokens fall in sixteen different bank groups (73 = 9 mod 16),
-//     and sixteen lanes reading sixteen chunks of one token are contiguous;
-//   * the four waves form two pairs; a pair owns 32 query rows (two blocks
-//     of 16), and its two waves split the feature dimension: each computes
-//     the partial scores over half of the 576 key features for all 32 rows,
-//     the two swap partials through LDS (fp32, summed in the same order by
-//     both, so both hold bit-identical scores and softmax state), and each
-//     accumulates O over half of the 512 value features.  Every operand read
-//     from LDS feeds two MFMAs (one per block), so LDS traffic per FLOP is
-//     half that of 16 rows per wave, while the query (32 rows x 288, 72
-//     VGPRs) and O (32 rows x 256 fp32, 128 accumulation registers) fit;
+//     register staging) into a ring of four, three tiles ahead of the one
+//     being computed (the loads of a tile take longer than two tiles of
+//     compute);
+//   * a token's 72 16-byte chunks are stored unpadded with chunk c of tile
+//     token t at position c ^ swz(t), swz(t) = ((t >> 1) & 3) << 1 |
+//     ((t >> 3) & 1) -- a permutation inside each aligned group of eight --
+//     which makes both operand reads conflict-free: sixteen lanes reading one
+//     chunk of sixteen tokens (K), and the value reads below, fall in
+//     distinct banks; the unpadded tile is what lets four of them fit in LDS;
+//   * eight waves, two per SIMD, so that one wave's LDS reads, exchange and
+//     softmax overlap the other's matrix work; they form four pairs, a pair
+//     owns 16 query rows, and its two waves split the feature dimension: each
+//     computes the partial scores over half of the 576 key features, the two
+//     swap partials through LDS (fp32, summed in the same order by both, so
+//     both hold bit-identical scores and softmax state; a wave takes every
+//     other 32-feature k-step, which keeps its K reads on one swizzle
+//     pattern), and each accumulates
+//     O over half of the 512 value features.  The query (16 rows x 288, 36
+//     VGPRs) and O (16 rows x 256 fp32, 64 registers) leave room for two
+//     waves per SIMD;
 //   * per tile: every K operand read of the tile is issued before its MFMAs
 //     (LDS latency otherwise stalls the single wave per SIMD), S^T[token][row]
 //     = K Q^T with v_mfma_f32_16x16x32_bf16, one partial exchange, then the
 //     online softmax in base 2 (lazily moved reference max) over the tile's
 //     32 tokens, and O^T[d][row] += V^T P^T with v_mfma_f32_16x16x32_bf16 over
-//     all 32 tokens at once, V read from LDS 16 bytes per token and
-//     transposed in registers (v_perm_b32).
+//     all 32 tokens at once, the V^T operand read straight from the
+//     token-major tile with the gfx950 transposing LDS read
+//     (ds_read_b64_tr_b16): a 16-lane group that points at 4 tokens x 4
+//     consecutive features receives, in lane x, feature x of the 4 tokens.
 // Workgroups of one split are placed on one XCD (dispatch is round-robin over
 // the eight XCDs), so the row blocks' reads of a tile share that XCD's L2.
+// The block-table entries a tile fill needs are read one step ahead, so the
+// fill's address computation never waits for them.
 #include "device.h"
 
 namespace splitkv {
@@ -41,37 +50,27 @@ namespace {
 constexpr int kMlaDqk = 576;
 constexpr int kMlaDv = 512;
 constexpr int kTile = 32;                        // tokens per LDS tile
-constexpr int kPitch = 73;                       // 16-byte chunks per token row (72 + 1 pad)
-constexpr int kChunks = kMlaDqk * 2 / 16;        // 72 chunks of a token's row
-constexpr int kTileChunks = kTile * kPitch;      // 2336
-constexpr int kTileLoads = (kTileChunks + 63) / 64;   // 37 wave-level 1 KB loads
-constexpr int kLoadsPerWave = (kTileLoads + 3) / 4;   // 10: every wave issues the same count
-constexpr int kSlotBytes = kTileLoads * 1024;    // 37888
-constexpr int kRing = 3;
+constexpr int kPitch = kMlaDqk * 2 / 16;         // 72 16-byte chunks per token row, unpadded
+constexpr int kTileChunks = kTile * kPitch;      // 2304
+constexpr int kWaves = 8;
+constexpr int kTileLoads = kTileChunks / 64;          // 36 wave-level 1 KB loads
+constexpr int kLoadsPerWave = (kTileLoads + kWaves - 1) / kWaves;   // 5: every wave issues the same count
+constexpr int kSlotBytes = kTileLoads * 1024;    // 36864
+constexpr int kRing = 4;
 constexpr int kRows = 64;                        // query rows per workgroup
 constexpr int kQk = kMlaDqk / 32 / 2;            // 9 k-steps of 32 key features per half
 constexpr int kPv = kMlaDv / 128 / 2;            // 2 chunks of 128 value features per half
-static_assert(kSlotBytes >= kTileChunks * 16, "slot holds a tile");
+static_assert(kSlotBytes == kTileChunks * 16 && kTileChunks % 64 == 0, "slot holds a tile");
 static_assert(SPLITKV_ROWS_PER_WG_MLA == kRows, "rows per workgroup");
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Transpose 8 tokens x 8 features (bf16) held as w[token] into 8 MFMA
-// operands op[feature] of 8 tokens each.
-__device__ __forceinline__ void transpose8x8(const u32x4 (&w)[8], bf16x8 (&op)[8]) {
-#pragma unroll
-  for (int x = 0; x < 4; ++x) {
-    u32x4 ev, od;
-#pragma unroll
-    for (int y = 0; y < 4; ++y) {
-      const uint32_t a = w[2 * y][x], b = w[2 * y + 1][x];
-      ev[y] = __builtin_amdgcn_perm(b, a, 0x05040100u);
-      od[y] = __builtin_amdgcn_perm(b, a, 0x07060302u);
-    }
-    op[2 * x] = __builtin_bit_cast(bf16x8, ev);
-    op[2 * x + 1] = __builtin_bit_cast(bf16x8, od);
-  }
-}
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// Position swizzle of a tile token's 16-byte chunks (see the file comment).
+__device__ __forceinline__ uint32_t swz(uint32_t t) { return ((t >> 1) & 3u) << 1 | ((t >> 3) & 1u); }
 
 // Workgroup barrier after this wave's LDS operations have completed (a bare
 // s_barrier does not wait for them); the signal fences keep the compiler from
@@ -85,10 +84,10 @@ __device__ __forceinline__ void lds_barrier() {
 
 }  // namespace
 
-__global__ __launch_bounds__(256) void mla_partial_kernel(PartialParams p, int per_xcd) {
+__global__ __launch_bounds__(512) void mla_partial_kernel(PartialParams p, int per_xcd) {
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kRing][kSlotBytes];
-  // partial-score exchange: [wave][group][block][lane]
-  __shared__ f32x4 xch[4][2][2][64];
+  // partial-score exchange: [wave][group][lane]
+  __shared__ f32x4 xch[kWaves][2][64];
 
   // XCD-aware placement: block id i runs on XCD i % 8; give each XCD a
   // contiguous run of (slot, row block) work items.
@@ -108,25 +107,26 @@ __global__ __launch_bounds__(256) void mla_partial_kernel(PartialParams p, int p
   const int b = work.b, split = work.split, nsplit = work.nsplit, s = work.s, e = work.e;
   const int L = ((cint32*)p.seq_lens)[b];
 
-  // This lane's two query rows (columns of the S^T tiles of the two blocks);
-  // rows past the last one read row rows-1 and are never stored.  The wave
-  // holds its half of their key features.
-  int rowv[2], limit[2];
-  bf16x8 q0[kQk], q1[kQk];
-#pragma unroll
-  for (int sb = 0; sb < 2; ++sb) {
-    rowv[sb] = rb * kRows + pair * 32 + sb * 16 + n16;
-    const int rc = min(rowv[sb], p.rows - 1);
+  // This lane's query row (column of the S^T tiles); rows past the last one
+  // read row rows-1 and are never stored.  The wave holds its half of the
+  // row's key features.
+  const int rowv = rb * kRows + pair * 16 + n16;
+  int limit;
+  bf16x8 q[kQk];
+  {
+    const int rc = min(rowv, p.rows - 1);
     const int t = rc / p.Hq, h = rc % p.Hq;
-    limit[sb] = L - p.T + t;
-    const uint16_t* qrow = p.q + b * p.qsb + t * p.qst + h * p.qsh + 32 * kQk * hf + 8 * qg;
+    limit = L - p.T + t;      // last key position this row sees
+    // k-step it of this wave is k-step 2*it + hf of the row: features 64*it + 32*hf + 8*qg ..
+    const uint16_t* qrow = p.q + b * p.qsb + t * p.qst + h * p.qsh + 32 * hf + 8 * qg;
 #pragma unroll
-    for (int it = 0; it < kQk; ++it) {
-      const bf16x8 v = *reinterpret_cast<const bf16x8*>(qrow + 32 * it);
-      if (sb == 0) q0[it] = v;
-      else q1[it] = v;
-    }
+    for (int it = 0; it < kQk; ++it) q[it] = *reinterpret_cast<const bf16x8*>(qrow + 64 * it);
   }
+
+  // Tiles that end at or before full_end need no mask: every token is in the
+  // range and visible to every row of the wave (its first row has the
+  // smallest causal limit).
+  const int full_end = min(e, L - p.T + min(rb * kRows + pair * 16, p.rows - 1) / p.Hq + 1);
 
   // The page size is a power of two for this kernel (checked on the host).
   const int psh = p.page_shift;
@@ -134,38 +134,63 @@ __global__ __launch_bounds__(256) void mla_partial_kernel(PartialParams p, int p
   cint32* cbt = (cint32*)(p.bt + b * p.bt_stride);
   const uint32_t ksp = uint32_t(p.ksp), kst = uint32_t(p.kst);   // < 2^31, checked on the host
 
-  // Tile fill: wave w issues the wave-level loads w, w+4, ..., w+36 of the
-  // 37 a tile needs; a wave with fewer repeats its last load (same lanes,
-  // same addresses, same bytes), so every wave issues ten per tile and the
+  // Tile fill: wave w issues the wave-level loads w, w+8, ..., w+32 of the
+  // 36 a tile needs; a wave with fewer repeats its last load (same lanes,
+  // same addresses, same bytes), so every wave issues five per tile and the
   // completion counts are the same for all.  Lane j of load i fills the
-  // 16-byte chunk q = 64*i + j of the slot: token q / 73, chunk q % 73.  The
-  // pad chunk and the chunks past the tile reload a valid chunk; tokens past
-  // the range end load the range's last token (finite, masked later).  A
-  // 32-token tile starting on a multiple of 16 spans at most two pages.
+  // 16-byte position q = 64*i + j of the slot: token q / 72, holding chunk
+  // (q % 72) ^ swz(token) of that token's row.  Tokens past the range
+  // end load the range's last token (finite, masked later).  A 32-token tile
+  // starting on a multiple of 16 spans at most two pages.
   const int nt = (e - s + kTile - 1) / kTile;      // tiles of the range
   // (token, byte offset) of every chunk this lane fills, the same for every tile
-  uint32_t fl[kLoadsPerWave];
+  // Loads 0-17 hold tokens 0-15 and loads 18-35 tokens 16-31 (16 x 72 =
+  // 18 x 64 chunks), and a 16-token half of a tile lies in one page (tiles
+  // start on multiples of 16, pages hold a power of two >= 16 tokens), so for
+  // a tile inside the range a load reads one page: its address is a uniform
+  // page base plus the lane's offset inside the half, lo[u].
+  uint32_t fl[kLoadsPerWave], lo[kLoadsPerWave];
 #pragma unroll
   for (int u = 0; u < kLoadsPerWave; ++u) {
-    int i = wave + 4 * u;
-    if (i >= kTileLoads) i -= 4;
-    const uint32_t q = uint32_t(64 * i + lane);
-    uint32_t tk = (q * 1796u) >> 17;                  // q / 73 for q < 3640
-    uint32_t c = q - tk * kPitch;
-    if (tk >= uint32_t(kTile)) tk = kTile - 1;
-    if (c >= uint32_t(kChunks)) c = 0;
+    int i = wave + kWaves * u;
+    if (i >= kTileLoads) i -= kWaves;
+    const uint32_t qc = uint32_t(64 * i + lane);
+    const uint32_t tk = qc / uint32_t(kPitch);
+    const uint32_t c = (qc - tk * kPitch) ^ swz(tk);
     fl[u] = (tk << 16) | (16u * c);
+    lo[u] = (tk & 15u) * kst + 16u * c;
   }
-  auto fill = [&](int k, uint8_t* slotp) __attribute__((always_inline)) {
+  // Pages of tile k's first and last token (the tile past the range: the last
+  // tile's), read ahead of the fill that needs them.
+  auto tile_pages = [&](int k, int& pa, int& pb) __attribute__((always_inline)) {
+    const int t0 = s + kTile * min(k, nt - 1);
+    const int last = min(t0 + kTile - 1, e - 1);
+    pa = cbt[t0 >> psh];
+    pb = cbt[last >> psh];
+  };
+  auto fill = [&](int k, uint8_t* slotp, int pa, int pb) __attribute__((always_inline)) {
     const int t0 = s + kTile * min(k, nt - 1);      // beyond the last tile: reload it
+    if (t0 + kTile <= e) {
+      // whole tile in the range: half 0 in page pa, half 1 in page pb
+      const uint8_t* half0 = p.k + uint64_t(uint32_t(pa)) * ksp + uint32_t(t0 & pmask) * kst;
+      const uint8_t* half1 = p.k + uint64_t(uint32_t(pb)) * ksp + uint32_t((t0 + 16) & pmask) * kst;
+#pragma unroll
+      for (int u = 0; u < kLoadsPerWave; ++u) {
+        int i = wave + kWaves * u;
+        if (i >= kTileLoads) i -= kWaves;
+        const uint8_t* src = (i < kTileLoads / 2 ? half0 : half1) + lo[u];
+        __builtin_amdgcn_global_load_lds(src, (lds_void*)(slotp + 1024 * i), 16, 0, 0);
+      }
+      return;
+    }
     const int last = min(t0 + kTile - 1, e - 1);
     const int pi0 = t0 >> psh;
-    const uint64_t base0 = uint64_t(uint32_t(cbt[pi0])) * ksp;
-    const uint64_t base1 = uint64_t(uint32_t(cbt[last >> psh])) * ksp;
+    const uint64_t base0 = uint64_t(uint32_t(pa)) * ksp;
+    const uint64_t base1 = uint64_t(uint32_t(pb)) * ksp;
 #pragma unroll
     for (int u = 0; u < kLoadsPerWave; ++u) {
-      int i = wave + 4 * u;
-      if (i >= kTileLoads) i -= 4;
+      int i = wave + kWaves * u;
+      if (i >= kTileLoads) i -= kWaves;
       const int tok = min(t0 + int(fl[u] >> 16), last);
       const uint64_t base = (tok >> psh) == pi0 ? base0 : base1;
       const uint8_t* src = p.k + (base + uint64_t(uint32_t(tok & pmask) * kst + (fl[u] & 0xffffu)));
@@ -173,133 +198,127 @@ __global__ __launch_bounds__(256) void mla_partial_kernel(PartialParams p, int p
     }
   };
 
-  // O^T accumulators of the two blocks over this wave's value half: lane
-  // (n16, qg) holds O[row n16][256hf + 128c + 32qg + 8i + e8] in o[c*8+e8][i].
-  f32x4 o0[kPv * 8], o1[kPv * 8];
+  // O^T accumulators over this wave's value half: lane (n16, qg) holds
+  // O[row n16][256hf + 128c + 16e8 + 4qg + i] in o[c*8+e8][i].
+  f32x4 o[kPv * 8];
 #pragma unroll
-  for (int c = 0; c < kPv * 8; ++c) {
-    o0[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-    o1[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int c = 0; c < kPv * 8; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
   constexpr float kRescaleMargin = 8.f;
-  float m_ref[2] = {-INFINITY, -INFINITY}, m_true[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  float m_ref = -INFINITY, m_true = -INFINITY, l_run = 0.f;
   int dbg_groups = 0, dbg_xor = 0;
   uint32_t dbg_sum = 0;
+
+  // Byte offsets (inside a 128-feature chunk of the wave's value half) of
+  // this lane's transposing reads for the four values of e8 & 3.
+  uint32_t vofs[4];
+  {
+    const uint32_t vt = 4 * qg + (n16 >> 2);
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      vofs[m] = vt * (kPitch * 16) + 16 * ((2 * m + ((n16 & 3) >> 1)) ^ swz(vt)) + 8 * (n16 & 1);
+  }
 
   // One 32-token tile in slotp, tokens t0 .. t0+31 of the range.
   auto tile = [&](const uint8_t* slotp, int t0) __attribute__((always_inline)) {
     // ---- partial S^T = K Q^T over this wave's key half for both 16-token
-    // groups and both blocks: all eighteen operand reads first, then the
-    // MFMAs, four independent accumulation chains.
-    const uint8_t* krow = slotp + n16 * (kPitch * 16) + 16 * qg + 64 * kQk * hf;
+    // groups: all eighteen operand reads first, then the MFMAs, two
+    // independent accumulation chains.
+    // k-step it: chunk 8*it + 4*hf + qg of token n16 (and 16 + n16, same
+    // swizzle), stored at 8*it + ((4*hf + qg) ^ swz(n16))
+    const uint8_t* krow = slotp + n16 * (kPitch * 16) + 16 * ((4 * hf + qg) ^ swz(n16));
     bf16x8 k0[kQk], k1[kQk];
 #pragma unroll
     for (int it = 0; it < kQk; ++it) {
-      k0[it] = *reinterpret_cast<const bf16x8*>(krow + 64 * it);
-      k1[it] = *reinterpret_cast<const bf16x8*>(krow + 16 * (kPitch * 16) + 64 * it);
+      k0[it] = *reinterpret_cast<const bf16x8*>(krow + 128 * it);
+      k1[it] = *reinterpret_cast<const bf16x8*>(krow + 16 * (kPitch * 16) + 128 * it);
     }
-    f32x4 s00 = {0.f, 0.f, 0.f, 0.f}, s01 = {0.f, 0.f, 0.f, 0.f};
-    f32x4 s10 = {0.f, 0.f, 0.f, 0.f}, s11 = {0.f, 0.f, 0.f, 0.f};   // s[group][block]
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};   // s[group]
 #pragma unroll
     for (int it = 0; it < kQk; ++it) {
-      s00 = mfma16x16x32(k0[it], q0[it], s00);
-      s01 = mfma16x16x32(k0[it], q1[it], s01);
-      s10 = mfma16x16x32(k1[it], q0[it], s10);
-      s11 = mfma16x16x32(k1[it], q1[it], s11);
+      s0 = mfma16x16x32(k0[it], q[it], s0);
+      s1 = mfma16x16x32(k1[it], q[it], s1);
     }
     // ---- swap partials with the pair's other wave; both sum own + other,
     // the same two values, so both hold identical scores
-    xch[wave][0][0][lane] = s00;
-    xch[wave][0][1][lane] = s01;
-    xch[wave][1][0][lane] = s10;
-    xch[wave][1][1][lane] = s11;
+    xch[wave][0][lane] = s0;
+    xch[wave][1][lane] = s1;
     lds_barrier();
     const int w2 = wave ^ 1;
-    const f32x4 sc[2][2] = {{s00 + xch[w2][0][0][lane], s01 + xch[w2][0][1][lane]},
-                            {s10 + xch[w2][1][0][lane], s11 + xch[w2][1][1][lane]}};
+    const f32x4 sc[2] = {s0 + xch[w2][0][lane], s1 + xch[w2][1][lane]};
     // ---- online softmax over the tile: lane (n16, qg) holds tokens
-    // 4qg..4qg+3 of each group for row n16 of each block
-    float sv[2][8], mx[2];
-    bool bump[2];
+    // 4qg..4qg+3 of each group for row n16
+    float sv[8];
+    if (t0 + kTile <= full_end) {
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sv[4 * g + i] = sc[g][i] * p.scale_log2;
+    } else {
 #pragma unroll
       for (int g = 0; g < 2; ++g)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int tk = t0 + 16 * g + 4 * qg + i;
-          sv[sb][4 * g + i] = (tk < e && tk <= limit[sb]) ? sc[g][sb][i] * p.scale_log2 : -INFINITY;
+          sv[4 * g + i] = (tk < e && tk <= limit) ? sc[g][i] * p.scale_log2 : -INFINITY;
         }
-      float m8 = sv[sb][0];
-#pragma unroll
-      for (int i = 1; i < 8; ++i) m8 = fmaxf(m8, sv[sb][i]);
-      mx[sb] = column_max4(m8);
-      m_true[sb] = fmaxf(m_true[sb], mx[sb]);
-      bump[sb] = mx[sb] > m_ref[sb] + kRescaleMargin;
     }
-    if (__any(bump[0] || bump[1])) {
-      float alpha[2];
+    float m8 = sv[0];
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        const float m_new = bump[sb] ? mx[sb] : m_ref[sb];
-        alpha[sb] = fast_exp2(m_ref[sb] - m_new);   // 0 on the first visible tile, 1 if unmoved
-        l_run[sb] *= alpha[sb];
-        m_ref[sb] = m_new;
-      }
+    for (int i = 1; i < 8; ++i) m8 = fmaxf(m8, sv[i]);
+    const float mx = column_max4(m8);
+    m_true = fmaxf(m_true, mx);
+    const bool bump = mx > m_ref + kRescaleMargin;
+    if (__any(bump)) {
+      const float m_new = bump ? mx : m_ref;
+      const float alpha = fast_exp2(m_ref - m_new);   // 0 on the first visible tile, 1 if unmoved
+      l_run *= alpha;
+      m_ref = m_new;
 #pragma unroll
-      for (int c = 0; c < kPv * 8; ++c) {
-        o0[c] *= alpha[0];
-        o1[c] *= alpha[1];
-      }
+      for (int c = 0; c < kPv * 8; ++c) o[c] *= alpha;
     }
-    bf16x8 pop[2];
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      const float m_use = m_ref[sb] == -INFINITY ? 0.f : m_ref[sb];
+    bf16x8 pop;
+    {
+      const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
       float pv[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) pv[i] = fast_exp2(sv[sb][i] - m_use);
-      l_run[sb] += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+      for (int i = 0; i < 8; ++i) pv[i] = fast_exp2(sv[i] - m_use);
+      l_run += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
       u32x4 pw = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
                   pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])};
-      pop[sb] = __builtin_bit_cast(bf16x8, pw);
+      pop = __builtin_bit_cast(bf16x8, pw);
     }
     // ---- O^T += V^T P^T over this wave's value half, all 32 tokens per MFMA:
     // k index 8qg + j is token (j < 4 ? 0 : 16) + 4qg + (j & 3), for V and P
-    // alike.  The next chunk's eight rows are read while the current chunk is
-    // multiplied.
-    const uint8_t* vrow = slotp + (4 * qg) * (kPitch * 16) + 16 * n16 + 256 * kPv * hf;
-    auto vld = [&](int c, u32x4 (&w)[8]) {
+    // alike.  Block e8 of chunk c is features fb = 256hf + 128c + 16e8 ..
+    // +15; lane (x, qg) points at features fb + 4(x&3) .. +3 of token
+    // 4qg + (x >> 2) (then 16 + that), i.e. at chunk 2e8 + ((x&3) >> 1) of
+    // the chunk's 16, half x & 1.
+    const lds_u8* vbase = (const lds_u8*)slotp + 512 * hf;
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        w[j] = *reinterpret_cast<const u32x4*>(vrow + ((j < 4 ? 0 : 16) + (j & 3)) * (kPitch * 16) + 256 * c);
-    };
-    u32x4 wcur[8];
-    vld(0, wcur);
-#pragma unroll
-    for (int c = 0; c < kPv; ++c) {
-      bf16x8 vop[8];
-      transpose8x8(wcur, vop);
-      if (c + 1 < kPv) vld(c + 1, wcur);
+    for (int c = 0; c < kPv; ++c)
 #pragma unroll
       for (int e8 = 0; e8 < 8; ++e8) {
-        o0[c * 8 + e8] = mfma16x16x32(vop[e8], pop[0], o0[c * 8 + e8]);
-        o1[c * 8 + e8] = mfma16x16x32(vop[e8], pop[1], o1[c * 8 + e8]);
+        const lds_u8* a = vbase + vofs[e8 & 3] + 128 * (e8 >> 2) + 256 * c;
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)a);
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(a + 16 * (kPitch * 16)));
+        u32x4 w = {__builtin_bit_cast(u32x2, lo).x, __builtin_bit_cast(u32x2, lo).y,
+                   __builtin_bit_cast(u32x2, hi).x, __builtin_bit_cast(u32x2, hi).y};
+        o[c * 8 + e8] = mfma16x16x32(__builtin_bit_cast(bf16x8, w), pop, o[c * 8 + e8]);
       }
-    }
   };
 
-  // Tile k: wait until this wave's loads of tile k are done (the ten loads
-  // of tile k+1 may still be in flight), then a barrier so every wave's part
-  // of the tile has landed -- which also means every wave has finished tile
-  // k-1 (its LDS reads and its partial exchange), so its slot can be
-  // refilled with tile k+2 and the exchange buffer reused.  Tiles past the range
+  // Tile k: wait until this wave's loads of tile k are done (the loads of
+  // tiles k+1 and k+2 may still be in flight), then a barrier so every wave's
+  // part of the tile has landed -- which also means every wave has finished
+  // tile k-1 (its LDS reads and its partial exchange), so its slot can be
+  // refilled with tile k+3 and the exchange buffer reused.  Tiles past the range
   // reload the last tile (never computed), so the counts stay static.
+  int pa = 0, pb = 0;     // pages of the next tile to fill
   auto step = [&](int k) __attribute__((always_inline)) {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0x0F70 | 10);               // vmcnt(10)
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kLoadsPerWave));   // vmcnt(10)
     lds_barrier();
-    fill(k + 2, ring[(k + 2) % kRing]);
+    fill(k + 3, ring[(k + 3) % kRing], pa, pb);
     const uint8_t* cur = ring[k % kRing];
     const int t0 = s + kTile * k;
     {
@@ -311,11 +330,18 @@ __global__ __launch_bounds__(256) void mla_partial_kernel(PartialParams p, int p
       dbg_sum += uint32_t(pg0) + uint32_t(pg1);
     }
     tile(cur, t0);
+    // pages for the next step's fill; their wait is the next step's barrier
+    tile_pages(k + 4, pa, pb);
   };
 
   if (nt > 0) {
-    fill(0, ring[0]);
-    fill(1, ring[1]);
+    tile_pages(0, pa, pb);
+    fill(0, ring[0], pa, pb);
+    tile_pages(1, pa, pb);
+    fill(1, ring[1], pa, pb);
+    tile_pages(2, pa, pb);
+    fill(2, ring[2], pa, pb);
+    tile_pages(3, pa, pb);
     for (int k = 0; k < nt; ++k) step(k);
   }
   // no wave leaves while loads it issued may still write LDS
@@ -324,13 +350,13 @@ __global__ __launch_bounds__(256) void mla_partial_kernel(PartialParams p, int p
 
   const bool direct = p.direct && nsplit == 1;
   const int64_t R = int64_t(p.T) * p.Hq;
-  auto finish = [&](int sb, const f32x4 (&oacc)[kPv * 8]) __attribute__((always_inline)) {
+  {
     // bring (l, o) from the reference max to the true max of the row
-    const float f = (m_ref[sb] == -INFINITY) ? 0.f : fast_exp2(m_ref[sb] - m_true[sb]);
-    const float m_run = m_true[sb];
-    const float l_tot = column_sum4(l_run[sb] * f);
-    const int row = rowv[sb];
-    if (row >= p.rows) return;
+    const float f = (m_ref == -INFINITY) ? 0.f : fast_exp2(m_ref - m_true);
+    const float m_run = m_true;
+    const float l_tot = column_sum4(l_run * f);
+    const int row = min(rowv, p.rows - 1);
+    const bool real = rowv < p.rows;
     const int t = row / p.Hq, h = row % p.Hq;
     const int64_t rix = int64_t(t) * p.Hq + h;
     float mul = p.v_scale * f;
@@ -338,27 +364,25 @@ __global__ __launch_bounds__(256) void mla_partial_kernel(PartialParams p, int p
 #pragma unroll
     for (int c = 0; c < kPv; ++c)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int e4 = 0; e4 < 2; ++e4) {
-          const int d = 256 * hf + 128 * c + 32 * qg + 8 * i + 4 * e4;
-          f32x4 v4 = {oacc[c * 8 + 4 * e4 + 0][i], oacc[c * 8 + 4 * e4 + 1][i],
-                      oacc[c * 8 + 4 * e4 + 2][i], oacc[c * 8 + 4 * e4 + 3][i]};
-          v4 *= mul;
-          if (direct) {
-            const int64_t o = (int64_t(b) * R + rix) * kMlaDv + d;
-            if (p.out_f32) {
-              *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + o) = v4;
-            } else {
-              u32x2 pk = {pack_bf16x2(v4[0], v4[1]), pack_bf16x2(v4[2], v4[3])};
-              *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + o) = pk;
-            }
+      for (int e8 = 0; e8 < 8; ++e8) {
+        const int d = 256 * hf + 128 * c + 16 * e8 + 4 * qg;
+        f32x4 v4 = o[c * 8 + e8];
+        v4 *= mul;
+        if (!real) continue;
+        if (direct) {
+          const int64_t oo = (int64_t(b) * R + rix) * kMlaDv + d;
+          if (p.out_f32) {
+            *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + oo) = v4;
           } else {
-            *reinterpret_cast<f32x4*>(p.part_o + (int64_t(slot) * R + rix) * kMlaDv + d) = v4;
+            u32x2 pk = {pack_bf16x2(v4[0], v4[1]), pack_bf16x2(v4[2], v4[3])};
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + oo) = pk;
           }
+        } else {
+          *reinterpret_cast<f32x4*>(p.part_o + (int64_t(slot) * R + rix) * kMlaDv + d) = v4;
         }
+      }
     // both waves of the pair hold the same (m, l); one writes them
-    if (qg == 0 && hf == 0) {
+    if (real && qg == 0 && hf == 0) {
       const bool empty = m_run == -INFINITY;
       if (direct) {
         if (p.lse)
@@ -369,9 +393,7 @@ __global__ __launch_bounds__(256) void mla_partial_kernel(PartialParams p, int p
         p.part_l[int64_t(slot) * R + rix] = l_tot;
       }
     }
-  };
-  finish(0, o0);
-  finish(1, o1);
+  }
 
   if (p.debug && tid == 0) {
     int32_t* rec = p.debug + (int64_t(slot) * p.row_blocks + rb) * 8;
@@ -388,7 +410,7 @@ __global__ __launch_bounds__(256) void mla_partial_kernel(PartialParams p, int p
 
 hipError_t launch_mla_partial(const PartialParams& p, hipStream_t stream) {
   const int per_xcd = (p.total_wg + 7) / 8;
-  const dim3 grid(unsigned(per_xcd * 8)), block(256);
+  const dim3 grid(unsigned(per_xcd * 8)), block(512);
   hipLaunchKernelGGL(mla_partial_kernel, grid, block, 0, stream, p, per_xcd);
   return hipGetLastError();
 }
