@@ -73,16 +73,12 @@ __device__ __forceinline__ f32x4 mfma16x16x16(bf16x4 a, bf16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
-// Round an fp32 value to bfloat16 (round to nearest even; NaN stays NaN).
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
-  uint32_t u = __float_as_uint(x);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
+// Two fp32 values to a bf16 pair (lo in the low half) with one
+// v_cvt_pk_bf16_f32: round to nearest even, NaN stays NaN.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // Widen four e4m3 codes (one dword) to four bf16 codes (two dwords).  Every
