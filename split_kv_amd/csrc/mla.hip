@@ -238,6 +238,16 @@ __global__ __launch_bounds__(512) void mla_partial_kernel(PartialParams p, int p
       s0 = mfma16x16x32(k0[it], q[it], s0);
       s1 = mfma16x16x32(k1[it], q[it], s1);
     }
+    // the first value chunk's operands do not depend on the scores: their
+    // reads overlap the exchange and the softmax
+    const lds_u8* vbase = (const lds_u8*)slotp + 512 * hf;
+    v4i16 vpre[16];
+#pragma unroll
+    for (int e8 = 0; e8 < 8; ++e8) {
+      const lds_u8* a = vbase + vofs[e8 & 3] + 128 * (e8 >> 2);
+      vpre[2 * e8] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)a);
+      vpre[2 * e8 + 1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(a + 16 * (kPitch * 16)));
+    }
     // ---- swap partials with the pair's other wave; both sum own + other,
     // the same two values, so both hold identical scores
     xch[wave][0][lane] = s0;
@@ -293,14 +303,14 @@ __global__ __launch_bounds__(512) void mla_partial_kernel(PartialParams p, int p
     // +15; lane (x, qg) points at features fb + 4(x&3) .. +3 of token
     // 4qg + (x >> 2) (then 16 + that), i.e. at chunk 2e8 + ((x&3) >> 1) of
     // the chunk's 16, half x & 1.
-    const lds_u8* vbase = (const lds_u8*)slotp + 512 * hf;
 #pragma unroll
     for (int c = 0; c < kPv; ++c)
 #pragma unroll
       for (int e8 = 0; e8 < 8; ++e8) {
         const lds_u8* a = vbase + vofs[e8 & 3] + 128 * (e8 >> 2) + 256 * c;
-        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)a);
-        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(a + 16 * (kPitch * 16)));
+        const v4i16 lo = c == 0 ? vpre[2 * e8] : __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)a);
+        const v4i16 hi = c == 0 ? vpre[2 * e8 + 1]
+                                : __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(a + 16 * (kPitch * 16)));
         u32x4 w = {__builtin_bit_cast(u32x2, lo).x, __builtin_bit_cast(u32x2, lo).y,
                    __builtin_bit_cast(u32x2, hi).x, __builtin_bit_cast(u32x2, hi).y};
         o[c * 8 + e8] = mfma16x16x32(__builtin_bit_cast(bf16x8, w), pop, o[c * 8 + e8]);
