@@ -95,10 +95,12 @@ def test_few_kv_long_sweep(L):
     case = synth.few_kv_long(L=L)
     O, LSE = oracle.attend(case)
     outs = {}
-    for n in [1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64]:
+    for n in [1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64, 0]:
+        # n = 0: the auto plan, the launch configuration bench.py times
         log(f"few-kv-long L={L} seed={case.seed} n={n}")
-        sess, _ = session_for(case, requested_splits=n, debug=True)
-        assert sess.total_slots == min(n, -(-L // 16))
+        sess, _ = session_for(case, requested_splits=n, debug=True, max_splits=256)
+        if n > 0:
+            assert sess.total_slots == min(n, -(-L // 16))
         sess.decode()
         torch.cuda.synchronize()
         e = assert_close(to_np(sess.out), O, 1e-2, 2e-2, f"L={L} n={n} out")
@@ -211,6 +213,20 @@ def test_mla_small_full_compare(n):
     _check_debug(case, sess, 1, 12)
 
 
+def test_mla_tiles_cut_by_ranges_and_pages():
+    # L = 2000, n = 3: splits [0, 656), [656, 1328), [1328, 2000) end inside a
+    # 32-token tile, and the third starts 48 tokens into a 64-token page, so
+    # each of its tiles has its two halves in different pages
+    _need_gpu()
+    case = synth.mla_decode(L=2000, seed=13)
+    log("mla L=2000 n=3 (partial tiles, tiles across pages)")
+    sess, _ = session_for(case, requested_splits=3, debug=True)
+    assert [tuple(r[2:]) for r in sess.slot_info_host] == [(0, 656), (656, 1328), (1328, 2000)]
+    sess.decode()
+    _check_full(case, sess, "mla L=2000 n=3")
+    _check_debug(case, sess, 1, 12)
+
+
 def test_mla_short_causal_edge():
     # L = 21: the last split holds keys only the later draft tokens see
     _need_gpu()
@@ -285,12 +301,12 @@ def test_fp8_full_size_sampled():
     _check_rows(case, sess, rows, "fp8 full")
 
 
-@pytest.mark.parametrize("n", [1, 4, 8])
+@pytest.mark.parametrize("n", [1, 4, 8, 0])
 def test_mla_full_size_sampled(n):
     _need_gpu()
     case = synth.mla_decode(L=65536)
     log(f"mla full L=65536 n={n}")
-    sess, _ = session_for(case, requested_splits=n)
+    sess, _ = session_for(case, requested_splits=n, max_splits=256)
     sess.decode()
     rows = [(0, t, h) for t in (0, 5) for h in (0, 77, 127)] + [(0, 3, 64)]
     _check_rows(case, sess, rows, f"mla full n={n}")
