@@ -69,6 +69,23 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
+// Direct global->LDS load of 16 bytes per lane into the 1 KiB at LDS byte
+// address lds (lane j at lds + 16 j), issued as inline assembly so that the
+// compiler does not track it: it would otherwise make every LDS read of the
+// tile ring wait for all such loads in flight (it cannot tell which slot a
+// load fills).  The kernel waits for these loads explicitly (s_waitcnt vmcnt
+// and a workgroup barrier before a slot is read), and loads complete in
+// order, so the compiler's own waits for other loads stay correct.  M0 holds
+// the LDS address; nothing else in the kernel uses M0.
+__device__ __forceinline__ void dma16(const uint8_t* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory");
+}
+// The same with a uniform 64-bit base and a 32-bit per-lane offset.
+__device__ __forceinline__ void dma16_sbase(const uint8_t* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds)
+               : "memory");
+}
+
 // Position swizzle of a tile token's 16-byte chunks: entry t & 15 of a
 // 16-entry table of 3-bit values, chosen (by search against measured gfx950
 // LDS behaviour: 16-byte reads are served 32 lanes at a time from 128
@@ -128,6 +145,10 @@ __global__ __launch_bounds__(512) void mla_partial_kernel(PartialParams p, int p
 #pragma unroll
     for (int it = 0; it < kQk; ++it) q[it] = *reinterpret_cast<const bf16x8*>(qrow + 64 * it);
   }
+  // The query has landed before the first tile fill is issued: the compiler
+  // would otherwise wait for it inside the tile loop with load counts that,
+  // not knowing about the fills, would also drain the fills in flight.
+  __builtin_amdgcn_s_waitcnt(0x0F70);                      // vmcnt(0)
 
   // Tiles that end at or before full_end need no mask: every token is in the
   // range and visible to every row of the wave (its first row has the
@@ -184,8 +205,8 @@ __global__ __launch_bounds__(512) void mla_partial_kernel(PartialParams p, int p
       for (int u = 0; u < kLoadsPerWave; ++u) {
         int i = wave + kWaves * u;
         if (i >= kTileLoads) i -= kWaves;
-        const uint8_t* src = (i < kTileLoads / 2 ? half0 : half1) + lo[u];
-        __builtin_amdgcn_global_load_lds(src, (lds_void*)(slotp + 1024 * i), 16, 0, 0);
+        dma16_sbase(i < kTileLoads / 2 ? half0 : half1, lo[u],
+                    uint32_t(size_t((lds_u8*)(slotp + 1024 * i))));
       }
       return;
     }
@@ -200,7 +221,7 @@ __global__ __launch_bounds__(512) void mla_partial_kernel(PartialParams p, int p
       const int tok = min(t0 + int(fl[u] >> 16), last);
       const uint64_t base = (tok >> psh) == pi0 ? base0 : base1;
       const uint8_t* src = p.k + (base + uint64_t(uint32_t(tok & pmask) * kst + (fl[u] & 0xffffu)));
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(slotp + 1024 * i), 16, 0, 0);
+      dma16(src, uint32_t(size_t((lds_u8*)(slotp + 1024 * i))));
     }
   };
 
