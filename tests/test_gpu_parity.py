@@ -248,6 +248,22 @@ def test_ragged_small_full_compare(n):
     _check_debug(case, sess, case.Hkv, 1)
 
 
+@pytest.mark.parametrize("d,kv", [(128, synth.KV_BF16), (256, synth.KV_BF16), (128, synth.KV_E4M3)])
+@pytest.mark.parametrize("n", [1, 3, 0])
+def test_gqa_multi_token_causal(d, kv, n):
+    # T = 4 query tokens per sequence (speculative decode on a grouped-query
+    # cache): g*T = 32 rows, two row blocks; L = T leaves the first token a
+    # single visible key
+    _need_gpu()
+    case = synth.make_case("gqa-multitoken", B=3, T=4, Hq=16, Hkv=2, d_qk=d, d_v=d,
+                           seq_lens=[4, 37, 700], page_size=16, kv_dtype=kv, seed=21)
+    log(f"gqa T=4 d={d} kv={kv} n={n}")
+    sess, _ = session_for(case, requested_splits=n, debug=True)
+    sess.decode()
+    _check_full(case, sess, f"gqa T=4 d={d} n={n}")
+    _check_debug(case, sess, case.Hkv, 2)
+
+
 def test_layouts_and_noncontiguous_query():
     _need_gpu()
     case = synth.ragged(B=8, hi=2000, seed=41)
