@@ -185,6 +185,11 @@ typedef struct {
   int32_t out_dtype;               /* SPLITKV_OUT_BF16 or SPLITKV_OUT_F32 */
   float* lse;                      /* may be NULL */
   int32_t* debug;                  /* may be NULL */
+  int32_t uniform_splits;          /* > 0: every sequence has exactly this many splits (then
+                                      slot_offset[b] = b * uniform_splits and total_slots =
+                                      B * uniform_splits, checked); the merge then takes its plan
+                                      from this value instead of reading num_splits/slot_offset.
+                                      0: no such promise */
 } splitkv_args;
 
 /*

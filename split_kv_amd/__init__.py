@@ -69,6 +69,7 @@ class splitkv_args(ctypes.Structure):
         ("scale", c_f32), ("k_scale", c_f32), ("v_scale", c_f32),
         ("workspace", c_vp), ("workspace_bytes", c_sz),
         ("out", c_vp), ("out_dtype", c_i32), ("lse", c_vp), ("debug", c_vp),
+        ("uniform_splits", c_i32),
     ]
 
 

@@ -238,6 +238,10 @@ splitkv_status run_combine(const splitkv_args* a, bool skip_single, void* stream
   if (!a->workspace || !aligned(a->workspace, 16) || a->workspace_bytes < need)
     return fail(SPLITKV_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, a->workspace_bytes,
                 need);
+  if (a->uniform_splits < 0 || a->uniform_splits > SPLITKV_MAX_SPLITS_LIMIT ||
+      (a->uniform_splits > 0 && int64_t(a->uniform_splits) * a->B != a->total_slots))
+    return fail(SPLITKV_ERR_INVALID_ARG, "%s: uniform_splits=%d inconsistent with B=%d, total_slots=%d",
+                fn, a->uniform_splits, a->B, a->total_slots);
   st = check_device(nullptr);
   if (st != SPLITKV_OK) return st;
   const Layout w = workspace_layout(*a);
@@ -254,6 +258,7 @@ splitkv_status run_combine(const splitkv_args* a, bool skip_single, void* stream
   p.R = a->T * a->Hq;
   p.d_v = a->d_v;
   p.skip_single = skip_single ? 1 : 0;
+  p.uniform_splits = a->uniform_splits;
   const hipError_t err = launch_combine(p, static_cast<hipStream_t>(stream));
   if (err != hipSuccess) return fail(SPLITKV_ERR_LAUNCH, "%s: launch failed: %s", fn, hipGetErrorString(err));
   return SPLITKV_OK;

@@ -13,7 +13,9 @@
 // workgroup's 256 threads are 16 float4 columns x 16 groups over splits, so
 // that at decode sizes every load of the row is in flight at once (the kernel
 // is latency-bound): each thread loads m, l and one float4 of o for each of
-// its splits, eight at a time, merges them against its own running max, and
+// its splits, up to eight at a time (as many as the row's split count needs:
+// a pass issues no load it would only mask away), merges them against its
+// own running max, and
 // the groups are merged through LDS (the same rescaling as across splits).
 #include "device.h"
 
@@ -22,43 +24,12 @@ namespace splitkv {
 constexpr int kCombineCols = 16;                // float4 columns per workgroup (64 features)
 constexpr int kCombineGroups = 256 / kCombineCols;
 
-// All fourteen argument dwords (workspace, plan, output and log-sum-exp
-// pointers, the row geometry and flags) are preloaded into scalar registers
-// at wave launch, so the two plan reads of the row's sequence are the first
-// memory accesses, issued together, and the stores need no argument load.
-// part_l and part_o follow part_m in the workspace: part_l at SR floats
-// (SR = total_slots * rows per sequence), part_o at the next 256-byte
-// boundary after 2 * SR floats.  The merge runs in base 2 on the hardware
-// exponential (every argument is <= 0: a difference from the running max).
-// flags: d_v (bits 0-15) | skip rows of single-split sequences (bit 16) |
-// fp32 output (bit 17).
-__global__ __launch_bounds__(256) void combine_kernel(const float* part_m, const int32_t* num_splits,
-                                                      const int32_t* slot_offset, void* out,
-                                                      float* lse, int32_t R, int32_t dsplit,
-                                                      int32_t flags, int32_t SR) {
-  constexpr int CH = kCombineCols, G = kCombineGroups, U = 8;
-  __shared__ float red_m[G][CH], red_l[G][CH];
-  __shared__ f32x4 red_o[G][CH];
-
-  const int tid = threadIdx.x;
-  const int row = int(blockIdx.x) / dsplit;
-  const int part = int(blockIdx.x) - row * dsplit;
-  const int b = row / R;
-  const int rix = row - b * R;
-  const int n = ((cint32*)num_splits)[b];
-  const int base = ((cint32*)slot_offset)[b];
-  asm volatile("" :: "s"(n), "s"(base));   // both reads in flight before either is used
-  if ((flags & (1 << 16)) && n == 1) return;
-  const int DV = flags & 0xffff;
-  const int c = tid % CH, g = tid / CH;
-  const float* part_l = part_m + SR;
-  const float* part_o = part_m + (int64_t(2) * SR * 4 + 255) / 256 * 64;
-
-  // running state in base 2: M2 = max of m_i * log2(e)
-  float M2 = -INFINITY, lam = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  const float* po = part_o + int64_t(rix) * DV + 64 * part + 4 * c;
-  const int64_t step = int64_t(R) * DV;
+// One thread's share of a row's splits: splits g, g+G, g+2G, ... of the n,
+// U loads in flight per pass, merged into the running (M2, lam, acc) in base 2.
+template <int U, int G>
+__device__ __forceinline__ void merge_splits(const float* part_m, const float* part_l, const float* po,
+                                             int64_t step, int R, int rix, int base, int n, int g,
+                                             float& M2, float& lam, f32x4& acc) {
   for (int i0 = g; i0 < n; i0 += U * G) {
     float mi[U], li[U];
     f32x4 oi[U];
@@ -83,6 +54,65 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* part_m, const
       M2 = Mn;
     }
   }
+}
+
+// All fourteen argument dwords (workspace, plan, output and log-sum-exp
+// pointers, the row geometry and flags) are preloaded into scalar registers
+// at wave launch, so the two plan reads of the row's sequence are the first
+// memory accesses, issued together, and the stores need no argument load.
+// part_l and part_o follow part_m in the workspace: part_l at SR floats
+// (SR = total_slots * rows per sequence), part_o at the next 256-byte
+// boundary after 2 * SR floats.  The merge runs in base 2 on the hardware
+// exponential (every argument is <= 0: a difference from the running max).
+// flags: d_v (bits 0-15) | skip rows of single-split sequences (bit 16) |
+// fp32 output (bit 17) | uniform split count (bits 18-26; 0: read the plan).
+// With a uniform count the row's plan is n = that count and base = b * n, so
+// the partial loads are the first memory accesses.
+__global__ __launch_bounds__(256) void combine_kernel(const float* part_m, const int32_t* num_splits,
+                                                      const int32_t* slot_offset, void* out,
+                                                      float* lse, int32_t R, int32_t dsplit,
+                                                      int32_t flags, int32_t SR) {
+  constexpr int CH = kCombineCols, G = kCombineGroups;
+  __shared__ float red_m[G][CH], red_l[G][CH];
+  __shared__ f32x4 red_o[G][CH];
+
+  const int tid = threadIdx.x;
+  const int row = int(blockIdx.x) / dsplit;
+  const int part = int(blockIdx.x) - row * dsplit;
+  const int b = row / R;
+  const int rix = row - b * R;
+  const int un = (flags >> 18) & 0x1ff;
+  int n, base;
+  if (un > 0) {
+    n = un;
+    base = b * un;
+  } else {
+    n = ((cint32*)num_splits)[b];
+    base = ((cint32*)slot_offset)[b];
+    asm volatile("" :: "s"(n), "s"(base));   // both reads in flight before either is used
+  }
+  if ((flags & (1 << 16)) && n == 1) return;
+  const int DV = flags & 0xffff;
+  const int c = tid % CH, g = tid / CH;
+  const float* part_l = part_m + SR;
+  const float* part_o = part_m + (int64_t(2) * SR * 4 + 255) / 256 * 64;
+
+  // running state in base 2: M2 = max of m_i * log2(e)
+  float M2 = -INFINITY, lam = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const float* po = part_o + int64_t(rix) * DV + 64 * part + 4 * c;
+  const int64_t step = int64_t(R) * DV;
+  // loads per thread and pass: just enough for the row's splits (uniform
+  // across the workgroup), so no pass issues loads it only masks away
+  const int per = (n + G - 1) / G;
+  if (per <= 1)
+    merge_splits<1, G>(part_m, part_l, po, step, R, rix, base, n, g, M2, lam, acc);
+  else if (per <= 2)
+    merge_splits<2, G>(part_m, part_l, po, step, R, rix, base, n, g, M2, lam, acc);
+  else if (per <= 4)
+    merge_splits<4, G>(part_m, part_l, po, step, R, rix, base, n, g, M2, lam, acc);
+  else
+    merge_splits<8, G>(part_m, part_l, po, step, R, rix, base, n, g, M2, lam, acc);
   red_m[g][c] = M2;
   red_l[g][c] = lam;
   red_o[g][c] = acc;
@@ -114,7 +144,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* part_m, const
 }
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
-  if (p.d_v % 64 != 0 || p.d_v > 0xffff) return hipErrorInvalidValue;
+  if (p.d_v % 64 != 0 || p.d_v > 0xffff || p.uniform_splits < 0 || p.uniform_splits > 0x1ff)
+    return hipErrorInvalidValue;
   const int dsplit = p.d_v / 64;
   const int64_t wgs = int64_t(p.B) * p.R * dsplit;
   const int64_t SR = p.part_l - p.part_m;
@@ -122,7 +153,8 @@ hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
       p.part_o != p.part_m + (2 * SR * 4 + 255) / 256 * 64)
     return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(wgs)), block(256);
-  const int32_t flags = p.d_v | (p.skip_single ? 1 << 16 : 0) | (p.out_f32 ? 1 << 17 : 0);
+  const int32_t flags = p.d_v | (p.skip_single ? 1 << 16 : 0) | (p.out_f32 ? 1 << 17 : 0) |
+                       (p.uniform_splits << 18);
   hipLaunchKernelGGL(combine_kernel, grid, block, 0, stream, p.part_m, p.num_splits, p.slot_offset,
                      p.out, p.lse, p.R, dsplit, flags, int32_t(SR));
   return hipGetLastError();

@@ -61,6 +61,7 @@ struct CombineParams {
   float* lse;
   int32_t B, R, d_v;            // R = T * Hq rows per sequence
   int32_t skip_single;          // rows of single-split sequences were written by the partial kernel
+  int32_t uniform_splits;       // > 0: every sequence has this many splits (no plan reads)
 };
 
 typedef short bf16x4 __attribute__((ext_vector_type(4)));

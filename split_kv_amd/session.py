@@ -119,6 +119,8 @@ class DecodeSession:
         a.out_dtype = SPLITKV_OUT_F32 if self.out_fp32 else SPLITKV_OUT_BF16
         a.lse = self.lse.data_ptr() if self.lse is not None else None
         a.debug = self.debug.data_ptr() if self.debug is not None else None
+        ns = self.num_splits_host
+        a.uniform_splits = int(ns[0]) if len(ns) and (ns == ns[0]).all() else 0
         self.args = a
 
     def set_block_table(self, block_table):

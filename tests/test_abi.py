@@ -190,6 +190,15 @@ def test_decode_argument_errors_without_device(over, code):
     assert sk.splitkv_last_error()
 
 
+def test_uniform_splits_must_match_the_slot_count():
+    lib = _lib()
+    a = _args(uniform_splits=3)             # B = 1 but total_slots = 1
+    assert lib.splitkv_combine(ctypes.byref(a), None) == sk.SPLITKV_ERR_INVALID_ARG
+    assert "uniform_splits" in sk.splitkv_last_error()
+    a = _args(uniform_splits=-1)
+    assert lib.splitkv_combine(ctypes.byref(a), None) == sk.SPLITKV_ERR_INVALID_ARG
+
+
 def test_mla_shape_errors_without_device():
     lib = _lib()
     a = _args(Hkv=1, d_qk=576, d_v=256, Hq=128, T=6)

@@ -163,6 +163,25 @@ def test_combine_alone_against_oracle_combine():
     assert (to_np(sess.out)[0, 0, 3] == 0).all() and np.isneginf(to_np(sess.lse)[0, 0, 3])
 
 
+def test_uniform_plan_promise_changes_nothing():
+    # with every sequence split alike the merge takes its plan from
+    # uniform_splits instead of reading it; both routes give the same bits
+    _need_gpu()
+    import torch
+    case = synth.fp8_batched(B=3, L=997, seed=31)
+    sess, _ = session_for(case, requested_splits=7)
+    assert sess.args.uniform_splits == 7
+    log("uniform plan: fp8 B=3 L=997 n=7")
+    sess.decode()
+    torch.cuda.synchronize()
+    o1, l1 = sess.out.clone(), sess.lse.clone()
+    sess.args.uniform_splits = 0
+    sess.decode()
+    torch.cuda.synchronize()
+    assert torch.equal(o1, sess.out) and torch.equal(l1, sess.lse)
+    _check_full(case, sess, "uniform plan")
+
+
 def test_combine_of_one_split_is_identity():
     _need_gpu()
     import torch
