@@ -157,7 +157,7 @@ __global__ __launch_bounds__(256) void gqa_partial_kernel(
   constexpr int LDS_STRIDE = D + 4;     // floats; padding against bank conflicts
   constexpr float kRescaleMargin = 8.f; // base-2 growth of a row max before O is rescaled
   __shared__ float sm_o[4][16][LDS_STRIDE];
-  __shared__ float sm_m[4][16], sm_r[4][16], sm_l[4][16];
+  __shared__ f32x4 sm_ml[4][16];      // per wave and row: true max, reference max, sum
   __shared__ int sm_dbg[4][3];
 
   const int lane = threadIdx.x & 63;
@@ -384,9 +384,7 @@ __global__ __launch_bounds__(256) void gqa_partial_kernel(
         *reinterpret_cast<f32x4*>(&sm_o[wave][n16][128 * c + 32 * qg + 8 * i + 4 * e4]) = v4;
       }
   if (qg == 0) {
-    sm_m[wave][n16] = m_true;
-    sm_r[wave][n16] = m_ref;
-    sm_l[wave][n16] = l_run;
+    sm_ml[wave][n16] = f32x4{m_true, m_ref, l_run, 0.f};
   }
   if (lane == 0) {
     sm_dbg[wave][0] = dbg_groups;
@@ -398,41 +396,44 @@ __global__ __launch_bounds__(256) void gqa_partial_kernel(
   const bool direct = a.direct && nsplit == 1;
   const int64_t R = a.R;
   {
-    // Wave w merges rows w, w+4, w+8, w+12 of the block (those that are real
-    // query rows): the per-row values are wave-uniform, so they are computed
-    // once per row in scalar registers, and each lane merges one float4 of
-    // features from the four waves' LDS copies.
-    constexpr int F4 = D / 4;
+    // Thread t merges row t / 16 of the block, float4 columns (t % 16) + 16q:
+    // the row's weights are computed by its sixteen threads in parallel, and
+    // sixteen threads read (and store) 256 contiguous bytes at a time.
+    constexpr int NQ = D / 64;             // float4 columns per thread
+    const int t = threadIdx.x;
+    const int row = t >> 4, cl = t & 15;
     const int nrow = min(16, a.rows - rb * 16);
+    f32x4 mlw[4];
+    f32x4 ov[4][NQ];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int r = wave + 4 * k;
-      if (r >= nrow) break;
-      // each wave's (l, o) is relative to its reference max; bring all four
-      // to the block's true max (reference maxima never exceed the true one)
-      const float M = fmaxf(fmaxf(sm_m[0][r], sm_m[1][r]), fmaxf(sm_m[2][r], sm_m[3][r]));
-      float wgt[4], Lsum = 0.f;
+    for (int w = 0; w < 4; ++w) {
+      mlw[w] = sm_ml[w][row];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float mr = sm_r[w][r];
-        wgt[w] = mr == -INFINITY ? 0.f : fast_exp2(mr - M);
-        Lsum += wgt[w] * sm_l[w][r];
-      }
-      const int grow = rb * 16 + r;
-      const int tt = grow / a.g, hh = hk * a.g + grow - (grow / a.g) * a.g;
+      for (int q = 0; q < NQ; ++q) ov[w][q] = *reinterpret_cast<const f32x4*>(&sm_o[w][row][4 * (cl + 16 * q)]);
+    }
+    // each wave's (l, o) is relative to its reference max; bring all four to
+    // the block's true max (reference maxima never exceed the true one)
+    const float M = fmaxf(fmaxf(mlw[0][0], mlw[1][0]), fmaxf(mlw[2][0], mlw[3][0]));
+    float wgt[4], Lsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      wgt[w] = mlw[w][1] == -INFINITY ? 0.f : fast_exp2(mlw[w][1] - M);
+      Lsum += wgt[w] * mlw[w][2];
+    }
+    if (row < nrow) {
+      const int grow = rb * 16 + row;
+      const int tt = grow / a.g, hh = hk * a.g + grow - tt * a.g;
       const int64_t rix = int64_t(tt) * a.Hq + hh;
       const bool empty = M == -INFINITY;
       const float mul = direct ? (Lsum > 0.f ? a.v_scale / Lsum : 0.f) : a.v_scale;
       const int64_t obase = ((direct ? int64_t(b) : int64_t(slot)) * R + rix) * D;
 #pragma unroll
-      for (int f0 = 0; f0 < F4; f0 += 64) {
-        const int f = f0 + lane;
-        if (F4 % 64 != 0 && f >= F4) break;
-        f32x4 acc = wgt[0] * *reinterpret_cast<const f32x4*>(&sm_o[0][r][4 * f]);
+      for (int q = 0; q < NQ; ++q) {
+        f32x4 acc = wgt[0] * ov[0][q];
 #pragma unroll
-        for (int w = 1; w < 4; ++w) acc += wgt[w] * *reinterpret_cast<const f32x4*>(&sm_o[w][r][4 * f]);
+        for (int w = 1; w < 4; ++w) acc += wgt[w] * ov[w][q];
         acc *= mul;
-        const int64_t o = obase + 4 * f;
+        const int64_t o = obase + 4 * (cl + 16 * q);
         if (direct) {
           if (a.out_f32) {
             *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + o) = acc;
@@ -444,7 +445,7 @@ __global__ __launch_bounds__(256) void gqa_partial_kernel(
           *reinterpret_cast<f32x4*>(a.part_o + o) = acc;
         }
       }
-      if (lane == 0) {
+      if (cl == 0) {
         if (direct) {
           if (a.lse)
             a.lse[int64_t(b) * R + rix] = (empty || !(Lsum > 0.f)) ? -INFINITY : (M + log2f(Lsum)) * kLn2;
