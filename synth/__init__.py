@@ -254,6 +254,35 @@ def ragged(B: int = 32, seed: int = 1005, hi: int = 131072, seq_lens=None) -> Ca
                      page_size=16, seed=seed)
 
 
+def ramp_keys(case: Case, steps, d0: int = 0, d1: Optional[int] = None) -> Case:
+    """Scale key features [d0, d1) of later tokens, in place (bf16 caches only).
+
+    ``steps`` is a list of (first_token, factor): logical token j of every
+    sequence gets the factor of the last step with first_token <= j (1 before
+    the first step).  Scaled values are re-rounded to bf16.  Scores then grow
+    along the sequence, so a running softmax maximum jumps inside a split;
+    with [d0, d1) inside the rope features of an MLA cache, the values (its
+    first d_v features) stay as drawn.
+    """
+    assert case.kv_dtype == KV_BF16
+    d1 = case.d_qk if d1 is None else d1
+    P = case.page_size
+    steps = sorted(steps)
+    for b, L in enumerate(case.seq_lens):
+        for j in range(int(L)):
+            f = 1.0
+            for j0, fac in steps:
+                if j >= j0:
+                    f = fac
+            if f == 1.0:
+                continue
+            page = case.block_table[b, j // P]
+            codes = case.k_cache[page, :, j % P, d0:d1]
+            vals = (codes.astype(np.uint32) << 16).view(np.float32) * np.float32(f)
+            case.k_cache[page, :, j % P, d0:d1] = to_bf16_codes(vals)
+    return case
+
+
 # --------------------------------------------------------------------------
 # bf16 code helpers for the GPU side's upload (bit views only, no rounding)
 # --------------------------------------------------------------------------

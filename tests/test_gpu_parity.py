@@ -358,3 +358,40 @@ def test_ragged_full_size_sampled():
     bmax = int(np.argmax(case.seq_lens))
     rows = [(b, 0, h) for b in (0, 2, 4, bmax) for h in (0, 13, 31)]
     _check_rows(case, sess, rows, "ragged full")
+
+
+# ---------------------------------------------------------------------------
+# Running-max jumps inside a split.  The kernels keep O relative to a reference
+# maximum per row and rescale O and l only when a tile's row maximum passes it
+# by more than 8 in base 2; keys scaled up part-way through the sequence make
+# that happen inside splits (tests/test_ramp_inputs.py checks the jump on the
+# CPU).
+
+def ramped_mla():
+    case = synth.mla_decode(L=2048, seed=21)
+    return synth.ramp_keys(case, [(700, 30.0), (1300, 100.0)], d0=512)
+
+
+def ramped_few_kv():
+    case = synth.few_kv_long(L=2000, seed=22)
+    return synth.ramp_keys(case, [(700, 4.0), (1300, 16.0)])
+
+
+@pytest.mark.parametrize("n", [1, 4])
+def test_mla_rescale_inside_split(n):
+    _need_gpu()
+    case = ramped_mla()
+    log(f"mla L=2048 keys ramped x30 at 700, x100 at 1300, n={n}")
+    sess, _ = session_for(case, requested_splits=n)
+    sess.decode()
+    _check_full(case, sess, f"mla ramp n={n}")
+
+
+@pytest.mark.parametrize("n", [1, 4])
+def test_gqa_rescale_inside_split(n):
+    _need_gpu()
+    case = ramped_few_kv()
+    log(f"few-kv L=2000 keys ramped x4 at 700, x16 at 1300, n={n}")
+    sess, _ = session_for(case, requested_splits=n)
+    sess.decode()
+    _check_full(case, sess, f"gqa ramp n={n}")
