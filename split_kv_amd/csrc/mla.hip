@@ -245,6 +245,8 @@ __global__ __launch_bounds__(512) void mla_partial_kernel(PartialParams p, int p
       vofs[m] = vt * (kPitch * 16) + 16 * ((2 * m + ((n16 & 3) >> 1)) ^ swz(vt)) + 8 * (n16 & 1);
   }
 
+  int fill_k = 0;          // the tile the current step fills
+  int pa = 0, pb = 0;      // its pages (the tile after it's, once read ahead)
   // One 32-token tile in slotp, tokens t0 .. t0+31 of the range.
   auto tile = [&](const uint8_t* slotp, int t0) __attribute__((always_inline)) {
     // ---- partial S^T = K Q^T over this wave's key half for both 16-token
@@ -280,6 +282,11 @@ __global__ __launch_bounds__(512) void mla_partial_kernel(PartialParams p, int p
     xch[wave][0][lane] = s0;
     xch[wave][1][lane] = s1;
     lds_barrier();
+    // tile k+3's loads into the slot tile k-1 left (every wave finished tile
+    // k-1 before the step barrier): issued here rather than at the step start,
+    // so the tile's K reads and QK go first and the loads queue under the
+    // softmax and PV
+    fill(fill_k, ring[fill_k % kRing], pa, pb);
     const int w2 = wave ^ 1;
     const f32x4 sc[2] = {s0 + xch[w2][0][lane], s1 + xch[w2][1][lane]};
     // ---- online softmax over the tile: lane (n16, qg) holds tokens
@@ -348,14 +355,14 @@ __global__ __launch_bounds__(512) void mla_partial_kernel(PartialParams p, int p
   // tiles k+1 and k+2 may still be in flight), then a barrier so every wave's
   // part of the tile has landed -- which also means every wave has finished
   // tile k-1 (its LDS reads and its partial exchange), so its slot can be
-  // refilled with tile k+3 and the exchange buffer reused.  Tiles past the range
-  // reload the last tile (never computed), so the counts stay static.
-  int pa = 0, pb = 0;     // pages of the next tile to fill
+  // refilled with tile k+3 (issued inside the tile, after the exchange) and
+  // the exchange buffer reused.  Tiles past the range reload the last tile
+  // (never computed), so the counts stay static.
   auto step = [&](int k) __attribute__((always_inline)) {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kLoadsPerWave));   // vmcnt(10)
     lds_barrier();
-    fill(k + 3, ring[(k + 3) % kRing], pa, pb);
+    fill_k = k + 3;
     const uint8_t* cur = ring[k % kRing];
     const int t0 = s + kTile * k;
     {
