@@ -39,6 +39,8 @@
 //     contiguous bytes of V for each of its 4 tokens (a quarter-wave reads 256
 //     contiguous bytes) and transposes them in registers with v_perm_b32, so P
 //     never leaves the register file.
+#include <type_traits>
+
 #include "device.h"
 
 namespace splitkv {
@@ -370,19 +372,24 @@ __global__ __launch_bounds__(256) void gqa_partial_kernel(
     compute(j + 2, ra);
   }
 
-  // ---- per-wave row totals; then merge the four waves through LDS
+  // ---- per-wave row totals; then merge the four waves through LDS (only
+  // the block's real query rows: a KV head with g < 16 query rows leaves
+  // the rest of the MFMA block unused)
   l_run = column_sum4(l_run);
+  const int nrow = min(16, a.rows - rb * 16);
   // lane (n16, qg) holds O[row n16][128c + 32qg + 8i + e8] in oacc[c*8+e8][i]
+  if (n16 < nrow) {
 #pragma unroll
-  for (int c = 0; c < NC; ++c)
+    for (int c = 0; c < NC; ++c)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int e4 = 0; e4 < 2; ++e4) {
-        f32x4 v4 = {oacc[c * 8 + 4 * e4 + 0][i], oacc[c * 8 + 4 * e4 + 1][i],
-                    oacc[c * 8 + 4 * e4 + 2][i], oacc[c * 8 + 4 * e4 + 3][i]};
-        *reinterpret_cast<f32x4*>(&sm_o[wave][n16][128 * c + 32 * qg + 8 * i + 4 * e4]) = v4;
-      }
+        for (int e4 = 0; e4 < 2; ++e4) {
+          f32x4 v4 = {oacc[c * 8 + 4 * e4 + 0][i], oacc[c * 8 + 4 * e4 + 1][i],
+                      oacc[c * 8 + 4 * e4 + 2][i], oacc[c * 8 + 4 * e4 + 3][i]};
+          *reinterpret_cast<f32x4*>(&sm_o[wave][n16][128 * c + 32 * qg + 8 * i + 4 * e4]) = v4;
+        }
+  }
   if (qg == 0) {
     sm_ml[wave][n16] = f32x4{m_true, m_ref, l_run, 0.f};
   }
@@ -395,21 +402,24 @@ __global__ __launch_bounds__(256) void gqa_partial_kernel(
 
   const bool direct = a.direct && nsplit == 1;
   const int64_t R = a.R;
-  {
-    // Thread t merges row t / 16 of the block, float4 columns (t % 16) + 16q:
-    // the row's weights are computed by its sixteen threads in parallel, and
-    // sixteen threads read (and store) 256 contiguous bytes at a time.
-    constexpr int NQ = D / 64;             // float4 columns per thread
+  // Thread t merges row t / TPR of the block, float4 columns (t % TPR) +
+  // TPR*q, TPR = 256 / RR threads per row for a block of RR rows (8 when
+  // the block has at most 8 real rows, else 16): the row's weights are
+  // computed by its threads in parallel, and they read (and store) 256 or 512
+  // contiguous bytes at a time.
+  auto merge = [&](auto rows_c) __attribute__((always_inline)) {
+    constexpr int RR = decltype(rows_c)::value;
+    constexpr int TPR = 256 / RR;
+    constexpr int NQ = D / 4 / TPR;        // float4 columns per thread
     const int t = threadIdx.x;
-    const int row = t >> 4, cl = t & 15;
-    const int nrow = min(16, a.rows - rb * 16);
+    const int row = t / TPR, cl = t % TPR;
     f32x4 mlw[4];
     f32x4 ov[4][NQ];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       mlw[w] = sm_ml[w][row];
 #pragma unroll
-      for (int q = 0; q < NQ; ++q) ov[w][q] = *reinterpret_cast<const f32x4*>(&sm_o[w][row][4 * (cl + 16 * q)]);
+      for (int q = 0; q < NQ; ++q) ov[w][q] = *reinterpret_cast<const f32x4*>(&sm_o[w][row][4 * (cl + TPR * q)]);
     }
     // each wave's (l, o) is relative to its reference max; bring all four to
     // the block's true max (reference maxima never exceed the true one)
@@ -433,7 +443,7 @@ __global__ __launch_bounds__(256) void gqa_partial_kernel(
 #pragma unroll
         for (int w = 1; w < 4; ++w) acc += wgt[w] * ov[w][q];
         acc *= mul;
-        const int64_t o = obase + 4 * (cl + 16 * q);
+        const int64_t o = obase + 4 * (cl + TPR * q);
         if (direct) {
           if (a.out_f32) {
             *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + o) = acc;
@@ -455,7 +465,11 @@ __global__ __launch_bounds__(256) void gqa_partial_kernel(
         }
       }
     }
-  }
+  };
+  if (nrow <= 8)
+    merge(std::integral_constant<int, 8>{});
+  else
+    merge(std::integral_constant<int, 16>{});
   if (a.debug && threadIdx.x == 0) {
     int groups = 0, x = 0;
     uint32_t sum = 0;
