@@ -19,14 +19,17 @@ What it computes follows the split-KV pages:
   honour the runtime split count (same page, section "The actual bug is one
   missing constructor argument");
 * exact decoders for bf16 and OCP e4m3fn codes (``codes``), for the FP8 KV
-  cache read with bf16 queries ("Xqa decode kernels", section "Purpose").
+  cache read with bf16 queries ("Xqa decode kernels", section "Purpose");
+* the step before decode: the new tokens' key/value rows written into their
+  pages, quantised to e4m3 for an FP8 cache (``append``).
 
 Every function is pinned by ``-m "not gpu"`` tests against brute force, closed
 forms, library special cases and exhaustive code tables; none is "parity
 unpinned".
 """
-from . import codes, plan, attention  # noqa: F401
+from . import codes, plan, attention, append  # noqa: F401
 from .codes import decode_bf16, decode_e4m3  # noqa: F401
 from .plan import split_range, make_plan, debug_records  # noqa: F401
 from .attention import (dequant_kv, attend, split_partials, combine,  # noqa: F401
                         attend_rows)
+from .append import e4m3_encode, quantise_bf16, append_kv  # noqa: F401
