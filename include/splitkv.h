@@ -241,6 +241,42 @@ splitkv_status splitkv_combine(const splitkv_args* args, void* stream);
  */
 splitkv_status splitkv_decode(const splitkv_args* args, int32_t kernel, void* stream);
 
+/* Arguments of splitkv_append_kv. */
+typedef struct {
+  const void* k_new;               /* bf16 [B][T][Hkv][d_k], strides k_new_stride_b/_t/_h */
+  const void* v_new;               /* bf16 [B][T][Hkv][d_v]; NULL exactly when v_cache is NULL */
+  int64_t k_new_stride_b, k_new_stride_t, k_new_stride_h;
+  int64_t v_new_stride_b, v_new_stride_t, v_new_stride_h;
+  void* k_cache;                   /* bf16 or e4m3 codes, [num_pages][Hkv][page_size][d_k] via strides */
+  void* v_cache;                   /* same dtype with d_v; NULL for a latent cache (MLA: V = K[..., :d_v]) */
+  int64_t k_stride_page, k_stride_head, k_stride_tok;
+  int64_t v_stride_page, v_stride_head, v_stride_tok;
+  const int32_t* block_table;      /* [B][bt_stride] */
+  int64_t bt_stride;
+  const int32_t* positions;        /* [B] logical position of sequence b's first new token */
+  int32_t B, T, Hkv, d_k, d_v, page_size, num_pages;
+  int32_t kv_dtype;                /* SPLITKV_KV_BF16 or SPLITKV_KV_E4M3 */
+  float k_scale, v_scale;          /* e4m3 cache: the per-tensor scales the decode reads it with */
+} splitkv_append_args;
+
+/*
+ * splitkv_append_kv -- the step before decode: new token t of sequence b is
+ * written to logical position positions[b] + t, i.e. to page
+ * block_table[b][pos / page_size], slot pos % page_size, for every KV head.
+ * A bf16 cache stores the bf16 codes unchanged.  An e4m3 cache, which the
+ * decode reads as code x scale ("Xqa decode kernels", section "Purpose":
+ * bf16 queries over an FP8 KV cache; "Test Plan": the fp8 cache dtype),
+ * stores the inverse: the e4m3 code nearest to x / scale (an fp32
+ * division), saturated to +-448, ties to the even code; NaN stays NaN.
+ * Device data is not trusted: a token whose position is negative or past
+ * the block-table row (bt_stride entries), or whose page is outside
+ * [0, num_pages), is skipped and nothing of it is written.  Requires d_k and
+ * d_v multiples of 8, 16-byte aligned new rows and caches (bases and
+ * strides).  Rows of one call must not overlap (two new tokens mapped to the
+ * same slot race).
+ */
+splitkv_status splitkv_append_kv(const splitkv_append_args* args, void* stream);
+
 /*
  * splitkv_validate_block_table -- host-side check that every block-table
  * entry a sequence reads (the first ceil(L_b / page_size)) lies in
@@ -262,6 +298,7 @@ const char* splitkv_last_error(void);   /* thread-local message of the last fail
 const char* splitkv_version(void);      /* source revision the library was built from */
 size_t splitkv_args_size(void);         /* sizeof(splitkv_args), for binding checks */
 size_t splitkv_plan_args_size(void);    /* sizeof(splitkv_plan_args) */
+size_t splitkv_append_args_size(void);  /* sizeof(splitkv_append_args) */
 
 #ifdef __cplusplus
 }

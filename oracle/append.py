@@ -13,9 +13,10 @@ the inverse of that read, is taken here and stated in the design doc:
 
     code = nearest e4m3 value of clamp(x / scale, -448, 448)   (fp32 division)
 
-with ties going to the code whose mantissa is even, the sign kept (a
-negative value that rounds to zero gives -0), and NaN giving the NaN code of
-its sign.  A bf16 cache stores the bf16 codes unchanged.
+with ties going to the code whose mantissa is even and the sign kept (a
+negative value that rounds to zero gives -0).  NaN gives a NaN code (this
+oracle keeps the sign; the format's two NaN codes are equivalent, and parity
+checks accept either).  A bf16 cache stores the bf16 codes unchanged.
 """
 import numpy as np
 

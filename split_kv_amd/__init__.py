@@ -73,6 +73,21 @@ class splitkv_args(ctypes.Structure):
     ]
 
 
+class splitkv_append_args(ctypes.Structure):
+    _fields_ = [
+        ("k_new", c_vp), ("v_new", c_vp),
+        ("k_new_stride_b", c_i64), ("k_new_stride_t", c_i64), ("k_new_stride_h", c_i64),
+        ("v_new_stride_b", c_i64), ("v_new_stride_t", c_i64), ("v_new_stride_h", c_i64),
+        ("k_cache", c_vp), ("v_cache", c_vp),
+        ("k_stride_page", c_i64), ("k_stride_head", c_i64), ("k_stride_tok", c_i64),
+        ("v_stride_page", c_i64), ("v_stride_head", c_i64), ("v_stride_tok", c_i64),
+        ("block_table", c_vp), ("bt_stride", c_i64), ("positions", c_vp),
+        ("B", c_i32), ("T", c_i32), ("Hkv", c_i32), ("d_k", c_i32), ("d_v", c_i32),
+        ("page_size", c_i32), ("num_pages", c_i32), ("kv_dtype", c_i32),
+        ("k_scale", c_f32), ("v_scale", c_f32),
+    ]
+
+
 class SplitKVError(RuntimeError):
     def __init__(self, fn, status, message):
         super().__init__(f"{fn} returned {status}: {message}")
@@ -105,6 +120,8 @@ def load():
             "splitkv_decode": (c_i32, [P(splitkv_args), c_i32, c_vp]),
             "splitkv_validate_block_table": (c_i32, [c_vp, c_vp, c_i32, c_i64, c_i32, c_i32]),
             "splitkv_e4m3_to_bf16": (c_i32, [c_vp, c_vp, c_i64, c_vp]),
+            "splitkv_append_kv": (c_i32, [P(splitkv_append_args), c_vp]),
+            "splitkv_append_args_size": (c_sz, []),
             "splitkv_last_error": (ctypes.c_char_p, []),
             "splitkv_version": (ctypes.c_char_p, []),
             "splitkv_args_size": (c_sz, []),
@@ -115,7 +132,8 @@ def load():
             fn.restype = res
             fn.argtypes = args
         if lib.splitkv_args_size() != ctypes.sizeof(splitkv_args) or \
-                lib.splitkv_plan_args_size() != ctypes.sizeof(splitkv_plan_args):
+                lib.splitkv_plan_args_size() != ctypes.sizeof(splitkv_plan_args) or \
+                lib.splitkv_append_args_size() != ctypes.sizeof(splitkv_append_args):
             raise RuntimeError("splitkv_args layout of the binding does not match the library")
         _lib = lib
         return lib
@@ -124,8 +142,8 @@ def load():
 EXPORTED = ("splitkv_plan", "splitkv_split_range", "splitkv_workspace_bytes",
             "splitkv_decode_partial", "splitkv_decode_partial_fp8", "splitkv_mla_decode_partial",
             "splitkv_combine", "splitkv_decode", "splitkv_validate_block_table",
-            "splitkv_e4m3_to_bf16", "splitkv_last_error", "splitkv_version", "splitkv_args_size",
-            "splitkv_plan_args_size")
+            "splitkv_e4m3_to_bf16", "splitkv_append_kv", "splitkv_last_error", "splitkv_version",
+            "splitkv_args_size", "splitkv_plan_args_size", "splitkv_append_args_size")
 
 
 def _check(fn, status):
@@ -203,3 +221,7 @@ def splitkv_validate_block_table(block_table, seq_lens, page_size: int, num_page
 
 def splitkv_e4m3_to_bf16(src: int, dst: int, n: int, stream: int = 0):
     _check("splitkv_e4m3_to_bf16", load().splitkv_e4m3_to_bf16(src, dst, n, stream))
+
+
+def splitkv_append_kv(args: splitkv_append_args, stream: int = 0):
+    _check("splitkv_append_kv", load().splitkv_append_kv(ctypes.byref(args), stream))

@@ -18,6 +18,8 @@ hipError_t launch_mla_partial(const PartialParams& p, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
 hipError_t launch_e4m3_to_bf16(const uint8_t* in, uint16_t* out, int64_t n, hipStream_t stream);
 
+hipError_t launch_append(const AppendParams& p, int rows, int kinds, hipStream_t stream);
+
 namespace {
 
 struct DeviceInfo {
@@ -324,6 +326,84 @@ splitkv_status splitkv_e4m3_to_bf16(const uint8_t* in, uint16_t* out, int64_t n,
   if (err != hipSuccess) return fail(SPLITKV_ERR_LAUNCH, "splitkv_e4m3_to_bf16: %s", hipGetErrorString(err));
   return SPLITKV_OK;
 }
+
+splitkv_status splitkv_append_kv(const splitkv_append_args* a, void* stream) {
+  const char* fn = "splitkv_append_kv";
+  if (!a) return fail(SPLITKV_ERR_INVALID_ARG, "%s: null args", fn);
+  if (!a->k_new || !a->k_cache || !a->block_table || !a->positions)
+    return fail(SPLITKV_ERR_INVALID_ARG, "%s: null k_new, k_cache, block_table or positions", fn);
+  if ((a->v_new == nullptr) != (a->v_cache == nullptr))
+    return fail(SPLITKV_ERR_INVALID_ARG, "%s: v_new and v_cache must both be given or both be NULL", fn);
+  if (a->B < 1 || a->T < 1 || a->Hkv < 1 || a->page_size < 1 || a->num_pages < 1 || a->bt_stride < 1)
+    return fail(SPLITKV_ERR_INVALID_ARG, "%s: bad shape B=%d T=%d Hkv=%d page_size=%d num_pages=%d", fn,
+                a->B, a->T, a->Hkv, a->page_size, a->num_pages);
+  const bool has_v = a->v_cache != nullptr;
+  if (a->d_k < 8 || a->d_k % 8 || (has_v && (a->d_v < 8 || a->d_v % 8)))
+    return fail(SPLITKV_ERR_UNSUPPORTED, "%s: d_k=%d d_v=%d must be positive multiples of 8", fn, a->d_k,
+                a->d_v);
+  if (a->kv_dtype != SPLITKV_KV_BF16 && a->kv_dtype != SPLITKV_KV_E4M3)
+    return fail(SPLITKV_ERR_INVALID_ARG, "%s: kv_dtype=%d", fn, a->kv_dtype);
+  const bool fp8 = a->kv_dtype == SPLITKV_KV_E4M3;
+  if (fp8 && (!(a->k_scale > 0.f) || !(a->k_scale < INFINITY) ||
+              (has_v && (!(a->v_scale > 0.f) || !(a->v_scale < INFINITY)))))
+    return fail(SPLITKV_ERR_INVALID_ARG, "%s: e4m3 scales must be positive and finite", fn);
+  const int64_t elem = fp8 ? 1 : 2;
+  auto rows_ok = [&](const void* base, int64_t sb, int64_t st, int64_t sh) {
+    return aligned(base, 16) && (sb * 2) % 16 == 0 && (st * 2) % 16 == 0 && (sh * 2) % 16 == 0;
+  };
+  auto cache_ok = [&](const void* base, int64_t sp, int64_t sh, int64_t sk) {
+    return aligned(base, 16) && (sp * elem) % 16 == 0 && (sh * elem) % 16 == 0 && (sk * elem) % 16 == 0;
+  };
+  if (!rows_ok(a->k_new, a->k_new_stride_b, a->k_new_stride_t, a->k_new_stride_h) ||
+      (has_v && !rows_ok(a->v_new, a->v_new_stride_b, a->v_new_stride_t, a->v_new_stride_h)))
+    return fail(SPLITKV_ERR_UNSUPPORTED, "%s: new rows or their strides not 16-byte aligned", fn);
+  if (!cache_ok(a->k_cache, a->k_stride_page, a->k_stride_head, a->k_stride_tok) ||
+      (has_v && !cache_ok(a->v_cache, a->v_stride_page, a->v_stride_head, a->v_stride_tok)))
+    return fail(SPLITKV_ERR_UNSUPPORTED, "%s: caches or their strides not 16-byte aligned", fn);
+  if (!aligned(a->block_table, 4) || !aligned(a->positions, 4))
+    return fail(SPLITKV_ERR_INVALID_ARG, "%s: block_table or positions misaligned", fn);
+  const int64_t rows = int64_t(a->B) * a->T * a->Hkv;
+  if (rows > INT32_MAX) return fail(SPLITKV_ERR_INVALID_ARG, "%s: grid too large", fn);
+  splitkv_status st = check_device(nullptr);
+  if (st != SPLITKV_OK) return st;
+  AppendParams p;
+  memset(&p, 0, sizeof(p));
+  p.src[0] = static_cast<const uint16_t*>(a->k_new);
+  p.ssb[0] = a->k_new_stride_b;
+  p.sst[0] = a->k_new_stride_t;
+  p.ssh[0] = a->k_new_stride_h;
+  p.dst[0] = static_cast<uint8_t*>(a->k_cache);
+  p.dsp[0] = a->k_stride_page * elem;
+  p.dsh[0] = a->k_stride_head * elem;
+  p.dsk[0] = a->k_stride_tok * elem;
+  p.d[0] = a->d_k;
+  p.scale[0] = a->k_scale;
+  if (has_v) {
+    p.src[1] = static_cast<const uint16_t*>(a->v_new);
+    p.ssb[1] = a->v_new_stride_b;
+    p.sst[1] = a->v_new_stride_t;
+    p.ssh[1] = a->v_new_stride_h;
+    p.dst[1] = static_cast<uint8_t*>(a->v_cache);
+    p.dsp[1] = a->v_stride_page * elem;
+    p.dsh[1] = a->v_stride_head * elem;
+    p.dsk[1] = a->v_stride_tok * elem;
+    p.d[1] = a->d_v;
+    p.scale[1] = a->v_scale;
+  }
+  p.bt = a->block_table;
+  p.bt_stride = a->bt_stride;
+  p.positions = a->positions;
+  p.T = a->T;
+  p.Hkv = a->Hkv;
+  p.page_size = a->page_size;
+  p.num_pages = a->num_pages;
+  p.fp8 = fp8 ? 1 : 0;
+  const hipError_t err = launch_append(p, int(rows), has_v ? 2 : 1, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return fail(SPLITKV_ERR_LAUNCH, "%s: %s", fn, hipGetErrorString(err));
+  return SPLITKV_OK;
+}
+
+size_t splitkv_append_args_size(void) { return sizeof(splitkv_append_args); }
 
 const char* splitkv_version(void) { return SPLITKV_REVISION; }
 

@@ -64,6 +64,20 @@ struct CombineParams {
   int32_t uniform_splits;       // > 0: every sequence has this many splits (no plan reads)
 };
 
+// Parameters of the KV append kernel (index 0: keys, 1: values).
+struct AppendParams {
+  const uint16_t* src[2];            // new keys, new values (bf16 codes)
+  int64_t ssb[2], sst[2], ssh[2];    // their element strides
+  uint8_t* dst[2];                   // key and value caches, as bytes
+  int64_t dsp[2], dsh[2], dsk[2];    // cache byte strides: page, head, token
+  int32_t d[2];                      // row widths
+  const int32_t* bt;
+  int64_t bt_stride;
+  const int32_t* positions;
+  int32_t T, Hkv, page_size, num_pages, fp8;
+  float scale[2];
+};
+
 typedef short bf16x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {

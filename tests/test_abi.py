@@ -35,6 +35,7 @@ def test_struct_layouts_match():
     lib = _lib()
     assert lib.splitkv_args_size() == ctypes.sizeof(sk.splitkv_args)
     assert lib.splitkv_plan_args_size() == ctypes.sizeof(sk.splitkv_plan_args)
+    assert lib.splitkv_append_args_size() == ctypes.sizeof(sk.splitkv_append_args)
 
 
 def test_constants_agree_with_oracle():
@@ -205,6 +206,44 @@ def test_mla_shape_errors_without_device():
     assert lib.splitkv_mla_decode_partial(ctypes.byref(a), None) == sk.SPLITKV_ERR_UNSUPPORTED
     a = _args(kv_dtype=1)
     assert lib.splitkv_decode(ctypes.byref(a), 5, None) == sk.SPLITKV_ERR_INVALID_ARG
+
+
+def _append_args(**over):
+    a = sk.splitkv_append_args()
+    base = dict(k_new=0x1000, v_new=0x1800, k_new_stride_b=2 * 128, k_new_stride_t=2 * 128,
+                k_new_stride_h=128, v_new_stride_b=2 * 128, v_new_stride_t=2 * 128,
+                v_new_stride_h=128, k_cache=0x2000, v_cache=0x3000, k_stride_page=2 * 16 * 128,
+                k_stride_head=16 * 128, k_stride_tok=128, v_stride_page=2 * 16 * 128,
+                v_stride_head=16 * 128, v_stride_tok=128, block_table=0x4000, bt_stride=4,
+                positions=0x5000, B=1, T=1, Hkv=2, d_k=128, d_v=128, page_size=16, num_pages=4,
+                kv_dtype=1, k_scale=0.5, v_scale=0.5)
+    base.update(over)
+    for k, v in base.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(k_new=None), sk.SPLITKV_ERR_INVALID_ARG),
+    (dict(v_new=None), sk.SPLITKV_ERR_INVALID_ARG),          # v_cache given without v_new
+    (dict(positions=None), sk.SPLITKV_ERR_INVALID_ARG),
+    (dict(T=0), sk.SPLITKV_ERR_INVALID_ARG),
+    (dict(num_pages=0), sk.SPLITKV_ERR_INVALID_ARG),
+    (dict(d_k=100), sk.SPLITKV_ERR_UNSUPPORTED),
+    (dict(kv_dtype=7), sk.SPLITKV_ERR_INVALID_ARG),
+    (dict(k_scale=0.0), sk.SPLITKV_ERR_INVALID_ARG),
+    (dict(v_scale=float("inf")), sk.SPLITKV_ERR_INVALID_ARG),
+    (dict(k_new=0x1008), sk.SPLITKV_ERR_UNSUPPORTED),
+    (dict(k_stride_tok=100), sk.SPLITKV_ERR_UNSUPPORTED),
+    (dict(kv_dtype=0, k_stride_tok=4), sk.SPLITKV_ERR_UNSUPPORTED),   # 8 bytes: not 16-aligned for bf16
+    (dict(block_table=0x4002), sk.SPLITKV_ERR_INVALID_ARG),
+])
+def test_append_argument_errors_without_device(over, code):
+    lib = _lib()
+    a = _append_args(**over)
+    st = lib.splitkv_append_kv(ctypes.byref(a), None)
+    assert st == code, (st, sk.splitkv_last_error())
+    assert sk.splitkv_last_error()
 
 
 def test_version_string():
