@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--warm-cache", action="store_true", help="reuse one page pool copy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--append", action="store_true",
+                    help="only time the KV append step (splitkv_append_kv) for the FP8 batch and "
+                         "MLA decode shapes; an extra measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy, the known-size reference that "
                          "scales the FETCH_SIZE / WRITE_SIZE counters")
@@ -276,10 +279,88 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
 
 
+def append_measurement(steps, warmup):
+    """Time splitkv_append_kv from a captured graph for two decode shapes.
+
+    FP8 batch: B=8 sequences, one new token, 4 KV heads of 128, e4m3 cache
+    (keys and values quantised); MLA: one sequence, six new tokens of the
+    576-wide latent row, bf16 cache.  Bytes = bf16 rows read + cache bytes
+    written.  The append is latency-bound at these sizes (a few KB per call).
+    """
+    import numpy as np
+    import torch
+    import synth
+    import split_kv_amd as sk
+    sk.load()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    out = []
+    shapes = [("fp8-batch append: B=8 T=1 Hkv=4 D=128 e4m3 cache", dict(
+                   B=8, T=1, Hq=32, Hkv=4, d_qk=128, d_v=128, seq_lens=[4096] * 8, page_size=16,
+                   kv_dtype=synth.KV_E4M3, seed=1003)),
+              ("mla append: B=1 T=6 latent 576 bf16 cache", dict(
+                   B=1, T=6, Hq=128, Hkv=1, d_qk=576, d_v=512, seq_lens=[4096], page_size=64,
+                   mla=True, std=0.5, seed=1004))]
+    for desc, kw in shapes:
+        case = synth.make_case("append", **kw)
+        t = synth.to_torch(case, dev)
+        rng = np.random.default_rng(7)
+        Tn, Hkv = case.T, case.Hkv
+        kn = torch.from_numpy(synth.to_bf16_codes(rng.standard_normal(
+            (case.B, Tn, Hkv, case.d_qk), dtype=np.float32)).view(np.int16)).to(dev)
+        vn = None if case.mla else torch.from_numpy(synth.to_bf16_codes(rng.standard_normal(
+            (case.B, Tn, Hkv, case.d_v), dtype=np.float32)).view(np.int16)).to(dev)
+        pos = torch.from_numpy((case.seq_lens - Tn).astype(np.int32)).to(dev)
+        kc, vc, bt = t["k_cache"], t["v_cache"], t["block_table"]
+        a = sk.splitkv_append_args()
+        a.k_new, a.v_new = kn.data_ptr(), (vn.data_ptr() if vn is not None else None)
+        a.k_new_stride_b, a.k_new_stride_t, a.k_new_stride_h = kn.stride()[:3]
+        if vn is not None:
+            a.v_new_stride_b, a.v_new_stride_t, a.v_new_stride_h = vn.stride()[:3]
+        a.k_cache, a.v_cache = kc.data_ptr(), (vc.data_ptr() if vc is not None else None)
+        a.k_stride_page, a.k_stride_head, a.k_stride_tok = kc.stride()[:3]
+        if vc is not None:
+            a.v_stride_page, a.v_stride_head, a.v_stride_tok = vc.stride()[:3]
+        a.block_table, a.bt_stride, a.positions = bt.data_ptr(), bt.shape[1], pos.data_ptr()
+        a.B, a.T, a.Hkv, a.d_k, a.d_v = case.B, Tn, Hkv, case.d_qk, case.d_v
+        a.page_size, a.num_pages = case.page_size, case.num_pages
+        a.kv_dtype = sk.SPLITKV_KV_E4M3 if case.kv_dtype == synth.KV_E4M3 else sk.SPLITKV_KV_BF16
+        a.k_scale, a.v_scale = case.k_scale, case.v_scale
+        for _ in range(warmup):
+            sk.splitkv_append_kv(a, stream.cuda_stream)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(steps):
+                sk.splitkv_append_kv(a, torch.cuda.current_stream().cuda_stream)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        elem = 1 if case.kv_dtype == synth.KV_E4M3 else 2
+        rows = case.B * Tn * Hkv
+        nbytes = rows * (case.d_qk + (0 if case.mla else case.d_v)) * (2 + elem)
+        out.append({"workload": desc, "us_per_append": round(us, 3), "bytes": nbytes,
+                    "GBps": round(nbytes / us / 1e3, 2)})
+        print(f"# {desc}: {us:.3f} us per append ({nbytes} bytes read + written)", file=sys.stderr,
+              flush=True)
+    print(json.dumps({"metric": "KV append us per call", "unit": "us", "higher_is_better": False,
+                      "data": "synthetic", "steps": steps, "timing": f"{steps} appends replayed "
+                      "from one captured HIP graph, events around the replay",
+                      "results": out, "note": "extra measurement; the bench line is the "
+                      "few-kv-long workload"}), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.append:
+        append_measurement(args.steps, args.warmup)
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "

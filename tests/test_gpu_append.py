@@ -129,9 +129,11 @@ def test_append_latent_mla(kv_dtype):
     _check(*_run(case, kn, None, positions), f"mla {kv_dtype}")
 
 
-@pytest.mark.parametrize("scale", [1.0, 1 / 64, 37.0])
+@pytest.mark.parametrize("scale", [1.0, 1 / 64, 7.0, 37.0])
 def test_append_quantises_every_bf16_code(scale):
     # one row per 128 bf16 codes: all 65536 codes pass through the conversion
+    # (at scale 7, 60 of them round differently if x / scale were computed as
+    # x times a rounded reciprocal)
     _need_gpu()
     case = synth.make_case("append-all", B=1, T=1, Hq=1, Hkv=1, d_qk=128, d_v=128,
                            seq_lens=[512], page_size=16, kv_dtype=synth.KV_E4M3, seed=19)

@@ -70,9 +70,11 @@ def test_matches_torch_conversion_on_every_bf16_value():
     assert np.array_equal(e4m3_encode(xs), ref)
 
 
-@pytest.mark.parametrize("scale", [1.0, 0.0625, 3.0, 1 / 300, 200.0])
+# 7 and 14: for 60 bf16 values each, x / scale and x * (1/scale) round to
+# different codes, so these scales tell the division from a reciprocal
+@pytest.mark.parametrize("scale", [1.0, 0.0625, 3.0, 7.0, 14.0, 1 / 300, 200.0])
 def test_quantise_divides_in_fp32(scale):
-    codes = np.arange(0, 65536, 7, dtype=np.uint32).astype(np.uint16)
+    codes = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     x = oracle.decode_bf16(codes).astype(np.float32)
     keep = ~np.isnan(x)
     with np.errstate(over="ignore", divide="ignore", invalid="ignore"):

@@ -76,3 +76,57 @@ def test_ignored_request_is_caught(monkeypatch):
     # the regression the pages describe: the stored default of one wins
     monkeypatch.setattr(P, "clamp_request", lambda L, n, mx: 1)
     _fails(TP.test_request_is_honoured_exactly)
+
+
+# ---- the append oracle
+
+import oracle.append as AP  # noqa: E402
+import tests.test_oracle_append as TAP  # noqa: E402
+
+
+def test_ties_away_from_zero_are_caught(monkeypatch):
+    orig_vals = AP._POS_VALUES
+
+    def bad(x):
+        x = np.asarray(x, dtype=np.float64)
+        neg = np.signbit(x)
+        ax = np.minimum(np.abs(np.nan_to_num(x)), AP.E4M3_MAX)
+        hi = np.minimum(np.searchsorted(orig_vals, ax), len(orig_vals) - 1)
+        lo = np.maximum(hi - 1, 0)
+        pick_hi = (orig_vals[hi] - ax) <= (ax - orig_vals[lo])      # ties upward
+        code = np.where(pick_hi, hi, lo).astype(np.uint8)
+        code = np.where(np.isnan(x), np.uint8(0x7F), code)
+        return (code | np.where(neg, np.uint8(0x80), np.uint8(0))).astype(np.uint8)
+    monkeypatch.setattr(TAP, "e4m3_encode", bad)
+    _fails(TAP.test_midpoints_go_to_the_even_code_and_off_midpoints_to_the_nearer)
+    _fails(TAP.test_matches_torch_conversion_on_every_bf16_value)
+
+
+def test_missing_saturation_is_caught(monkeypatch):
+    orig = AP.e4m3_encode
+
+    def bad(x):
+        x = np.asarray(x, dtype=np.float64)
+        out = orig(x)
+        return np.where(np.abs(x) > AP.E4M3_MAX, np.uint8(0x7F) | (out & 0x80), out).astype(np.uint8)
+    monkeypatch.setattr(TAP, "e4m3_encode", bad)
+    _fails(TAP.test_saturation_and_nan)
+
+
+def test_multiplying_by_a_rounded_reciprocal_is_caught(monkeypatch):
+    def bad(codes, scale):
+        x = C.decode_bf16(codes).astype(np.float32)
+        with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
+            y = x * (np.float32(1) / np.float32(scale))
+        return AP.e4m3_encode(y)
+    monkeypatch.setattr(TAP, "quantise_bf16", bad)
+    _fails(TAP.test_quantise_divides_in_fp32, 7.0)
+
+
+def test_wrong_slot_is_caught(monkeypatch):
+    orig = AP.append_kv
+
+    def bad(kc, vc, kn, vn, bt, pos, P, dt, k_scale=1.0, v_scale=1.0):
+        return orig(kc, vc, kn, vn, bt, np.asarray(pos) + 1, P, dt, k_scale, v_scale)
+    monkeypatch.setattr(TAP, "append_kv", bad)
+    _fails(TAP.test_append_writes_exactly_the_target_rows, "bf16", False)
