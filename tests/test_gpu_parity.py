@@ -395,3 +395,33 @@ def test_gqa_rescale_inside_split(n):
     sess, _ = session_for(case, requested_splits=n)
     sess.decode()
     _check_full(case, sess, f"gqa ramp n={n}")
+
+
+# ---------------------------------------------------------------------------
+# Empty sequences: L = 0 (no cached token at all; its one page holds only
+# poison) and, for six draft tokens, L < T (the first tokens see no key).
+# Such rows give out = 0 and lse = -inf.
+
+@pytest.mark.parametrize("kv_dtype", [synth.KV_BF16, synth.KV_E4M3])
+@pytest.mark.parametrize("n", [0, 1, 4])
+def test_gqa_zero_length_sequences(kv_dtype, n):
+    _need_gpu()
+    case = synth.make_case("zero-len", B=4, T=1, Hq=8, Hkv=2, d_qk=128, d_v=128,
+                           seq_lens=[0, 5, 300, 0], page_size=16, kv_dtype=kv_dtype, seed=3)
+    log(f"gqa {kv_dtype} seq_lens=[0,5,300,0] n={n}")
+    sess, _ = session_for(case, requested_splits=n, debug=True)
+    sess.decode()
+    _check_full(case, sess, f"zero-len {kv_dtype} n={n}")
+    _check_debug(case, sess, case.Hkv, 1)
+
+
+@pytest.mark.parametrize("n", [1, 4])
+def test_mla_sequences_shorter_than_the_draft(n):
+    _need_gpu()
+    case = synth.make_case("mla-short", B=3, T=6, Hq=128, Hkv=1, d_qk=576, d_v=512,
+                           seq_lens=[0, 3, 100], page_size=64, mla=True, std=0.5, seed=4)
+    log(f"mla seq_lens=[0,3,100] T=6 n={n}")
+    sess, _ = session_for(case, requested_splits=n, debug=True)
+    sess.decode()
+    _check_full(case, sess, f"mla short n={n}")
+    _check_debug(case, sess, 1, 12)
