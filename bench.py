@@ -44,9 +44,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="few-kv-long",
-                    choices=["few-kv-long", "fp8-batched", "mla", "ragged", "tiny-gqa"],
+                    choices=["few-kv-long", "fp8-batched", "mla", "mla-fp8", "ragged", "tiny-gqa"],
                     help="few-kv-long is the headline; the others are extra measurements")
-    ap.add_argument("--L", type=int, default=None, help="sequence length (few-kv-long, mla, tiny-gqa)")
+    ap.add_argument("--L", type=int, default=None, help="sequence length (few-kv-long, mla, mla-fp8, tiny-gqa)")
     ap.add_argument("--sweep", type=str, default="1,2,3,4,6,8,12,16,24,32,48,64,96,128,192,256",
                     help="comma-separated num_splits to sweep ('' to skip); the workload's own "
                          "sweep is 1..64, larger counts are extra points")
@@ -72,6 +72,8 @@ def make_workload(name, L):
         return synth.fp8_batched()
     if name == "mla":
         return synth.mla_decode(L=L or 65536)
+    if name == "mla-fp8":
+        return synth.mla_decode(L=L or 65536, kv_dtype=synth.KV_E4M3)
     if name == "ragged":
         return synth.ragged()
     return synth.tiny_gqa(L=L or 256)
@@ -83,8 +85,9 @@ def describe(case, name):
                 f"bf16 paged (P=16, permuted)")
     if name == "fp8-batched":
         return "batched GQA decode, e4m3 KV: B=8 T=1 Hq=32 Hkv=4 D=128 L=32000 P=16, bf16 Q"
-    if name == "mla":
-        return f"MLA decode: B=1 T=6 Hq=128 latent 576/512 L={int(case.seq_lens[0])} P=64 bf16"
+    if name in ("mla", "mla-fp8"):
+        return (f"MLA decode: B=1 T=6 Hq=128 latent 576/512 L={int(case.seq_lens[0])} P=64 "
+                f"{'e4m3 cache, bf16 Q' if case.kv_dtype == 'e4m3' else 'bf16'}")
     if name == "ragged":
         return f"ragged GQA decode: B=32 Hq=32 Hkv=8 D=128 bf16 P=16, sum L={int(case.seq_lens.sum())}"
     return (f"tiny GQA decode: B=1 T=1 Hq=8 Hkv=2 D=128 L={int(case.seq_lens[0])} contiguous bf16, "

@@ -218,7 +218,11 @@ splitkv_status splitkv_decode_partial_fp8(const splitkv_args* args, void* stream
  * columns as value; one workgroup per (slot, block of 64 query rows in
  * (t, h) order).  Causal within the T query tokens ("Shipped: 484.5 tok/s on
  * one GB300 ...", table "What shipped": split-KV MLA decode of one request
- * at six tokens).  Requires kv_dtype == BF16.
+ * at six tokens).  The latent cache is bf16 or e4m3 (kv_dtype); e4m3 codes
+ * widen exactly to bf16 and k_scale / v_scale (the same value for a latent
+ * cache whose values are its keys' first columns) scale the scores and the
+ * output; the query stays bf16 ("Xqa decode kernels", section "Purpose":
+ * bf16 queries over an FP8 KV cache).
  */
 splitkv_status splitkv_mla_decode_partial(const splitkv_args* args, void* stream);
 

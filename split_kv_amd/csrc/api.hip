@@ -14,7 +14,7 @@
 namespace splitkv {
 
 hipError_t launch_gqa_partial(const PartialParams& p, int D, bool fp8, hipStream_t stream);
-hipError_t launch_mla_partial(const PartialParams& p, hipStream_t stream);
+hipError_t launch_mla_partial(const PartialParams& p, bool fp8, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
 hipError_t launch_e4m3_to_bf16(const uint8_t* in, uint16_t* out, int64_t n, hipStream_t stream);
 
@@ -106,7 +106,8 @@ splitkv_status check_partial(const splitkv_args* a, Kind kind, bool need_ws, con
   if (a->num_pages < 1) return fail(SPLITKV_ERR_INVALID_ARG, "%s: num_pages=%d", fn, a->num_pages);
   if (a->bt_stride < 1) return fail(SPLITKV_ERR_INVALID_ARG, "%s: bt_stride < 1", fn);
   const int want_kv = kind == Kind::GqaFp8 ? SPLITKV_KV_E4M3 : SPLITKV_KV_BF16;
-  if (a->kv_dtype != want_kv)
+  // the MLA kernel reads a bf16 or an e4m3 latent cache
+  if (a->kv_dtype != want_kv && !(kind == Kind::Mla && a->kv_dtype == SPLITKV_KV_E4M3))
     return fail(SPLITKV_ERR_INVALID_ARG, "%s: kv_dtype=%d, this entry point takes %d", fn,
                 a->kv_dtype, want_kv);
   if (kind == Kind::Mla) {
@@ -125,7 +126,7 @@ splitkv_status check_partial(const splitkv_args* a, Kind kind, bool need_ws, con
   if (!(a->scale > 0.f) || !(a->k_scale > 0.f) || !(a->v_scale > 0.f))
     return fail(SPLITKV_ERR_INVALID_ARG, "%s: scales must be positive", fn);
   // 16-byte vector loads of q rows and cache rows
-  const int64_t elem = kind == Kind::GqaFp8 ? 1 : 2;
+  const int64_t elem = a->kv_dtype == SPLITKV_KV_E4M3 ? 1 : 2;
   if (!aligned(a->q, 16) || (a->q_stride_b * 2) % 16 || (a->q_stride_t * 2) % 16 ||
       (a->q_stride_h * 2) % 16)
     return fail(SPLITKV_ERR_UNSUPPORTED, "%s: q or its strides not 16-byte aligned", fn);
@@ -169,7 +170,7 @@ splitkv_status check_partial(const splitkv_args* a, Kind kind, bool need_ws, con
 }
 
 PartialParams make_partial_params(const splitkv_args& a, Kind kind, int row_blocks, bool direct) {
-  const int64_t elem = kind == Kind::GqaFp8 ? 1 : 2;
+  const int64_t elem = a.kv_dtype == SPLITKV_KV_E4M3 ? 1 : 2;
   PartialParams p;
   memset(&p, 0, sizeof(p));
   p.q = static_cast<const uint16_t*>(a.q);
@@ -224,7 +225,7 @@ splitkv_status run_partial(const splitkv_args* a, Kind kind, bool direct, void* 
   if (st != SPLITKV_OK) return st;
   const PartialParams p = make_partial_params(*a, kind, row_blocks, direct);
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t err = kind == Kind::Mla ? launch_mla_partial(p, s)
+  const hipError_t err = kind == Kind::Mla ? launch_mla_partial(p, a->kv_dtype == SPLITKV_KV_E4M3, s)
                                            : launch_gqa_partial(p, a->d_qk, kind == Kind::GqaFp8, s);
   if (err != hipSuccess) return fail(SPLITKV_ERR_LAUNCH, "%s: launch failed: %s", fn, hipGetErrorString(err));
   return SPLITKV_OK;

@@ -57,6 +57,18 @@ constexpr int kTileLoads = kTileChunks / 64;          // 36 wave-level 1 KB load
 constexpr int kLoadsPerWave = (kTileLoads + kWaves - 1) / kWaves;   // 5: every wave issues the same count
 constexpr int kSlotBytes = kTileLoads * 1024;    // 36864
 constexpr int kRing = 4;
+// e4m3 cache: a tile's codes (32 x 576 bytes) are 18 wave-level loads; waves
+// 0-1 issue three, the others two plus a repeat of their second, so every
+// wave issues three.  The codes land in a four-deep staging ring and are
+// widened into a two-deep ring of bf16 tiles laid out as above.
+constexpr int kF8Pitch = kMlaDqk / 16;                // 36 16-byte chunks per code row
+constexpr int kF8TileLoads = kTile * kMlaDqk / 1024;  // 18
+constexpr int kF8LoadsPerWave = 3;
+constexpr int kF8StageBytes = kF8TileLoads * 1024;    // 18432
+constexpr int kPoolBytes = kRing * kSlotBytes;        // 147456 either way
+static_assert(2 * kSlotBytes + 4 * kF8StageBytes == kPoolBytes, "e4m3 rings fill the pool");
+static_assert((kF8LoadsPerWave - 1) * kWaves < kF8TileLoads && kF8LoadsPerWave * kWaves >= kF8TileLoads,
+              "three loads per wave cover an e4m3 tile");
 constexpr int kRows = 64;                        // query rows per workgroup
 constexpr int kQk = kMlaDqk / 32 / 2;            // 9 k-steps of 32 key features per half
 constexpr int kPv = kMlaDv / 128 / 2;            // 2 chunks of 128 value features per half
@@ -107,8 +119,17 @@ __device__ __forceinline__ void lds_barrier() {
 
 }  // namespace
 
+template <bool FP8>
 __global__ __launch_bounds__(512) void mla_partial_kernel(PartialParams p, int per_xcd) {
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[kRing][kSlotBytes];
+  // bf16: four tile slots.  e4m3: two bf16 tile slots, then four code slots.
+  __shared__ __attribute__((aligned(1024))) uint8_t pool[kPoolBytes];
+  constexpr int kLPW = FP8 ? kF8LoadsPerWave : kLoadsPerWave;   // loads per wave and tile
+  auto tile_slot = [&](int k) __attribute__((always_inline)) {
+    return pool + (FP8 ? (k & 1) : (k & 3)) * kSlotBytes;
+  };
+  auto fill_slot = [&](int k) __attribute__((always_inline)) {
+    return FP8 ? pool + 2 * kSlotBytes + (k & 3) * kF8StageBytes : pool + (k & 3) * kSlotBytes;
+  };
   // partial-score exchange: [wave][group][lane]
   __shared__ f32x4 xch[kWaves][2][64];
 
@@ -176,14 +197,26 @@ __global__ __launch_bounds__(512) void mla_partial_kernel(PartialParams p, int p
   // start on multiples of 16, pages hold a power of two >= 16 tokens), so for
   // a tile inside the range a load reads one page: its address is a uniform
   // page base plus the lane's offset inside the half, lo[u].
-  uint32_t fl[kLoadsPerWave], lo[kLoadsPerWave];
-#pragma unroll
-  for (int u = 0; u < kLoadsPerWave; ++u) {
+  // For an e4m3 cache, lane j of load i fills 16-byte position q = 64*i + j
+  // of the code slot in plain order: token q / 36, code bytes 16*(q % 36)
+  // .. +15 of its row; loads 0-8 hold tokens 0-15, loads 9-17 tokens 16-31.
+  auto load_index = [&](int u) __attribute__((always_inline)) {
     int i = wave + kWaves * u;
-    if (i >= kTileLoads) i -= kWaves;
-    const uint32_t qc = uint32_t(64 * i + lane);
-    const uint32_t tk = qc / uint32_t(kPitch);
-    const uint32_t c = (qc - tk * kPitch) ^ swz(tk);
+    if (i >= (FP8 ? kF8TileLoads : kTileLoads)) i -= kWaves;
+    return i;
+  };
+  uint32_t fl[kLPW], lo[kLPW];
+#pragma unroll
+  for (int u = 0; u < kLPW; ++u) {
+    const uint32_t qc = uint32_t(64 * load_index(u) + lane);
+    uint32_t tk, c;
+    if constexpr (FP8) {
+      tk = qc / uint32_t(kF8Pitch);
+      c = qc - tk * kF8Pitch;
+    } else {
+      tk = qc / uint32_t(kPitch);
+      c = (qc - tk * kPitch) ^ swz(tk);
+    }
     fl[u] = (tk << 16) | (16u * c);
     lo[u] = (tk & 15u) * kst + 16u * c;
   }
@@ -202,10 +235,9 @@ __global__ __launch_bounds__(512) void mla_partial_kernel(PartialParams p, int p
       const uint8_t* half0 = p.k + uint64_t(uint32_t(pa)) * ksp + uint32_t(t0 & pmask) * kst;
       const uint8_t* half1 = p.k + uint64_t(uint32_t(pb)) * ksp + uint32_t((t0 + 16) & pmask) * kst;
 #pragma unroll
-      for (int u = 0; u < kLoadsPerWave; ++u) {
-        int i = wave + kWaves * u;
-        if (i >= kTileLoads) i -= kWaves;
-        dma16_sbase(i < kTileLoads / 2 ? half0 : half1, lo[u],
+      for (int u = 0; u < kLPW; ++u) {
+        const int i = load_index(u);
+        dma16_sbase(i < (FP8 ? kF8TileLoads : kTileLoads) / 2 ? half0 : half1, lo[u],
                     uint32_t(size_t((lds_u8*)(slotp + 1024 * i))));
       }
       return;
@@ -215,9 +247,8 @@ __global__ __launch_bounds__(512) void mla_partial_kernel(PartialParams p, int p
     const uint64_t base0 = uint64_t(uint32_t(pa)) * ksp;
     const uint64_t base1 = uint64_t(uint32_t(pb)) * ksp;
 #pragma unroll
-    for (int u = 0; u < kLoadsPerWave; ++u) {
-      int i = wave + kWaves * u;
-      if (i >= kTileLoads) i -= kWaves;
+    for (int u = 0; u < kLPW; ++u) {
+      const int i = load_index(u);
       const int tok = min(t0 + int(fl[u] >> 16), last);
       const uint64_t base = (tok >> psh) == pi0 ? base0 : base1;
       const uint8_t* src = p.k + (base + uint64_t(uint32_t(tok & pmask) * kst + (fl[u] & 0xffffu)));
@@ -245,6 +276,34 @@ __global__ __launch_bounds__(512) void mla_partial_kernel(PartialParams p, int p
       vofs[m] = vt * (kPitch * 16) + 16 * ((2 * m + ((n16 & 3) >> 1)) ^ swz(vt)) + 8 * (n16 & 1);
   }
 
+  // e4m3: widen tile k's codes (exactly; the scales are applied to the scores
+  // and the output) into its bf16 slot, 16-byte chunk c of token t at
+  // position c ^ swz(t) as the bf16 fills place it.
+  // Thread tid widens chunks tid, tid + 512, ... of the tile's 2304 (waves
+  // 0-3 five, waves 4-7 four); the byte offsets are the same every tile.
+  constexpr int kWidenMax = (kTile * kPitch + kWaves * 64 - 1) / (kWaves * 64);   // 5
+  const int widen_n = (kTile * kPitch - int(tid) + kWaves * 64 - 1) / (kWaves * 64);
+  uint32_t wsrc[kWidenMax], wdst[kWidenMax];
+#pragma unroll
+  for (int j = 0; j < kWidenMax; ++j) {
+    const uint32_t u = min(uint32_t(tid) + uint32_t(kWaves * 64 * j), uint32_t(kTile * kPitch - 1));
+    const uint32_t t = u / kPitch, c = u - t * kPitch;
+    wsrc[j] = t * kMlaDqk + 8 * c;
+    wdst[j] = t * (kPitch * 16) + 16 * (c ^ swz(t));
+  }
+  auto widen_tile = [&](int k) __attribute__((always_inline)) {
+    const lds_u8* src = (const lds_u8*)fill_slot(k);
+    lds_u8* dst = (lds_u8*)tile_slot(k);
+#pragma unroll
+    for (int j = 0; j < kWidenMax; ++j) {
+      if (j < widen_n) {
+        const u32x2 w = *(const __attribute__((address_space(3))) u32x2*)(src + wsrc[j]);
+        const u32x2 a = e4m3x4_to_bf16x4(w.x), b2 = e4m3x4_to_bf16x4(w.y);
+        const u32x4 r = {a.x, a.y, b2.x, b2.y};
+        *(__attribute__((address_space(3))) u32x4*)(dst + wdst[j]) = r;
+      }
+    }
+  };
   int fill_k = 0;          // the tile the current step fills
   int pa = 0, pb = 0;      // its pages (the tile after it's, once read ahead)
   // One 32-token tile in slotp, tokens t0 .. t0+31 of the range.
@@ -286,7 +345,7 @@ __global__ __launch_bounds__(512) void mla_partial_kernel(PartialParams p, int p
     // k-1 before the step barrier): issued here rather than at the step start,
     // so the tile's K reads and QK go first and the loads queue under the
     // softmax and PV
-    fill(fill_k, ring[fill_k % kRing], pa, pb);
+    fill(fill_k, fill_slot(fill_k), pa, pb);
     const int w2 = wave ^ 1;
     const f32x4 sc[2] = {s0 + xch[w2][0][lane], s1 + xch[w2][1][lane]};
     // ---- online softmax over the tile: lane (n16, qg) holds tokens
@@ -358,12 +417,22 @@ __global__ __launch_bounds__(512) void mla_partial_kernel(PartialParams p, int p
   // refilled with tile k+3 (issued inside the tile, after the exchange) and
   // the exchange buffer reused.  Tiles past the range reload the last tile
   // (never computed), so the counts stay static.
+  // e4m3: the same three-ahead fills into the code ring; tile k+1 is widened
+  // at the start of step k, so at step k this wave waits for its loads of
+  // tile k+1 (those of tile k+2 may still be in flight) and the barrier makes
+  // tile k's widened slot and tile k+1's codes visible (widening at the step
+  // start measured faster than after the exchange or split around it).
   auto step = [&](int k) __attribute__((always_inline)) {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kLoadsPerWave));   // vmcnt(10)
+    if constexpr (FP8)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | kLPW);           // vmcnt(3)
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kLPW));     // vmcnt(10)
     lds_barrier();
     fill_k = k + 3;
-    const uint8_t* cur = ring[k % kRing];
+    // e4m3: widen tile k+1 (its codes have landed) into the slot tile k-1 left
+    if constexpr (FP8) widen_tile(k + 1);
+    const uint8_t* cur = tile_slot(k);
     const int t0 = s + kTile * k;
     {
       const int pg0 = cbt[t0 >> psh];
@@ -380,12 +449,19 @@ __global__ __launch_bounds__(512) void mla_partial_kernel(PartialParams p, int p
 
   if (nt > 0) {
     tile_pages(0, pa, pb);
-    fill(0, ring[0], pa, pb);
+    fill(0, fill_slot(0), pa, pb);
     tile_pages(1, pa, pb);
-    fill(1, ring[1], pa, pb);
+    fill(1, fill_slot(1), pa, pb);
     tile_pages(2, pa, pb);
-    fill(2, ring[2], pa, pb);
+    fill(2, fill_slot(2), pa, pb);
     tile_pages(3, pa, pb);
+    if constexpr (FP8) {
+      // tile 0 widened before the loop (tile k+1 is widened in step k)
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kLPW));     // vmcnt(6): tile 0 landed
+      lds_barrier();
+      widen_tile(0);
+    }
     for (int k = 0; k < nt; ++k) step(k);
   }
   // no wave leaves while loads it issued may still write LDS
@@ -452,10 +528,13 @@ __global__ __launch_bounds__(512) void mla_partial_kernel(PartialParams p, int p
   }
 }
 
-hipError_t launch_mla_partial(const PartialParams& p, hipStream_t stream) {
+hipError_t launch_mla_partial(const PartialParams& p, bool fp8, hipStream_t stream) {
   const int per_xcd = (p.total_wg + 7) / 8;
   const dim3 grid(unsigned(per_xcd * 8)), block(512);
-  hipLaunchKernelGGL(mla_partial_kernel, grid, block, 0, stream, p, per_xcd);
+  if (fp8)
+    hipLaunchKernelGGL(mla_partial_kernel<true>, grid, block, 0, stream, p, per_xcd);
+  else
+    hipLaunchKernelGGL(mla_partial_kernel<false>, grid, block, 0, stream, p, per_xcd);
   return hipGetLastError();
 }
 

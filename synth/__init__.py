@@ -238,10 +238,15 @@ def fp8_batched(B: int = 8, L: int = 32000, seed: int = 1003, fp8_scale=None) ->
                      fp8_scale=fp8_scale)
 
 
-def mla_decode(L: int = 2048, seed: int = 1004, T: int = 6, Hq: int = 128) -> Case:
-    """MLA decode: 6 causal query tokens, 128 heads, one 576-wide latent head (V = first 512)."""
-    return make_case("mla", B=1, T=T, Hq=Hq, Hkv=1, d_qk=576, d_v=512, seq_lens=[L],
-                     page_size=64, mla=True, std=0.5, seed=seed)
+def mla_decode(L: int = 2048, seed: int = 1004, T: int = 6, Hq: int = 128,
+               kv_dtype: str = KV_BF16) -> Case:
+    """MLA decode: 6 causal query tokens, 128 heads, one 576-wide latent head (V = first 512).
+
+    kv_dtype e4m3 stores the latent cache as FP8 codes with one per-tensor
+    scale (keys and values share it, being the same rows)."""
+    return make_case("mla" if kv_dtype == KV_BF16 else "mla-fp8", B=1, T=T, Hq=Hq, Hkv=1, d_qk=576,
+                     d_v=512, seq_lens=[L], page_size=64, mla=True, std=0.5, seed=seed,
+                     kv_dtype=kv_dtype)
 
 
 def ragged(B: int = 32, seed: int = 1005, hi: int = 131072, seq_lens=None) -> Case:

@@ -426,3 +426,54 @@ def test_mla_sequences_shorter_than_the_draft(n):
     sess.decode()
     _check_full(case, sess, f"mla short n={n}")
     _check_debug(case, sess, 1, 12)
+
+
+# ---------------------------------------------------------------------------
+# MLA over an e4m3 latent cache (bf16 queries, one per-tensor scale shared by
+# keys and values): the codes are widened exactly, so the bar is the FP8 one
+# against the oracle on the same dequantised values.
+
+@pytest.mark.parametrize("n", [1, 4, 8])
+def test_mla_fp8_small_full_compare(n):
+    _need_gpu()
+    case = synth.mla_decode(L=2048, kv_dtype=synth.KV_E4M3)
+    log(f"mla e4m3 L=2048 n={n} k_scale={case.k_scale}")
+    sess, _ = session_for(case, requested_splits=n, debug=True)
+    sess.decode()
+    _check_full(case, sess, f"mla e4m3 n={n}")
+    _check_debug(case, sess, 1, 12)
+
+
+def test_mla_fp8_tiles_cut_by_ranges_and_pages():
+    _need_gpu()
+    case = synth.mla_decode(L=2000, seed=13, kv_dtype=synth.KV_E4M3)
+    log("mla e4m3 L=2000 n=3 (partial tiles, tiles across pages)")
+    sess, _ = session_for(case, requested_splits=3, debug=True)
+    sess.decode()
+    _check_full(case, sess, "mla e4m3 L=2000 n=3")
+    _check_debug(case, sess, 1, 12)
+
+
+@pytest.mark.parametrize("n", [1, 4])
+def test_mla_fp8_sequences_shorter_than_the_draft(n):
+    _need_gpu()
+    case = synth.make_case("mla-fp8-short", B=3, T=6, Hq=128, Hkv=1, d_qk=576, d_v=512,
+                           seq_lens=[0, 3, 100], page_size=64, mla=True, std=0.5, seed=4,
+                           kv_dtype=synth.KV_E4M3)
+    log(f"mla e4m3 seq_lens=[0,3,100] n={n}")
+    sess, _ = session_for(case, requested_splits=n, debug=True)
+    sess.decode()
+    _check_full(case, sess, f"mla e4m3 short n={n}")
+    _check_debug(case, sess, 1, 12)
+
+
+def test_mla_fp8_full_size_sampled():
+    _need_gpu()
+    case = synth.mla_decode(L=65536, kv_dtype=synth.KV_E4M3)
+    log("mla e4m3 L=65536 auto plan, sampled rows")
+    sess, _ = session_for(case, requested_splits=0, max_splits=256)
+    sess.decode()
+    rng = np.random.default_rng(5)
+    rows = [(0, int(t), int(h)) for t, h in zip(rng.integers(0, 6, 24), rng.integers(0, 128, 24))]
+    rows += [(0, 0, 0), (0, 5, 127)]
+    _check_rows(case, sess, rows, "mla e4m3 L=65536")
