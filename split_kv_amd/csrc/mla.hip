@@ -10,7 +10,8 @@
 //   * tiles arrive by direct global->LDS loads (16 bytes per lane, no
 //     register staging) into a ring of four, three tiles ahead of the one
 //     being computed (the loads of a tile take longer than two tiles of
-//     compute);
+//     compute), issued after a tile's partial-score exchange so that the
+//     tile's own K reads and QK go first;
 //   * a token's 72 16-byte chunks are stored unpadded with chunk c of tile
 //     token t at position c ^ swz(t) -- a permutation inside each aligned
 //     group of eight, swz(t) a 3-bit table entry for t mod 16 -- which keeps
@@ -29,7 +30,7 @@
 //     VGPRs) and O (16 rows x 256 fp32, 64 registers) leave room for two
 //     waves per SIMD;
 //   * per tile: every K operand read of the tile is issued before its MFMAs
-//     (LDS latency otherwise stalls the single wave per SIMD), S^T[token][row]
+//     (so no MFMA waits on a read issued just before it), S^T[token][row]
 //     = K Q^T with v_mfma_f32_16x16x32_bf16, one partial exchange, then the
 //     online softmax in base 2 (lazily moved reference max) over the tile's
 //     32 tokens, and O^T[d][row] += V^T P^T with v_mfma_f32_16x16x32_bf16 over
@@ -37,6 +38,10 @@
 //     token-major tile with the gfx950 transposing LDS read
 //     (ds_read_b64_tr_b16): a 16-lane group that points at 4 tokens x 4
 //     consecutive features receives, in lane x, feature x of the 4 tokens.
+// An e4m3 latent cache (bf16 queries, "Xqa decode kernels", section
+// "Purpose") runs the same tile code: its codes, half the bytes, arrive the
+// same way into a four-deep code ring and are widened exactly to bf16 at the
+// start of each step into a two-deep ring of bf16 tiles laid out as above.
 // Workgroups of one split are placed on one XCD (dispatch is round-robin over
 // the eight XCDs), so the row blocks' reads of a tile share that XCD's L2.
 // The block-table entries a tile fill needs are read one step ahead, so the
