@@ -477,3 +477,19 @@ def test_mla_fp8_full_size_sampled():
     rows = [(0, int(t), int(h)) for t, h in zip(rng.integers(0, 6, 24), rng.integers(0, 128, 24))]
     rows += [(0, 0, 0), (0, 5, 127)]
     _check_rows(case, sess, rows, "mla e4m3 L=65536")
+
+
+# ---------------------------------------------------------------------------
+# MLA at other decode shapes: one token (no causal mask within the draft),
+# and head counts whose T*Hq rows leave the last 64-row block partly empty.
+
+@pytest.mark.parametrize("T,Hq,L,n", [(1, 128, 3000, 4), (2, 16, 777, 3), (3, 40, 1500, 0)])
+@pytest.mark.parametrize("kv_dtype", [synth.KV_BF16, synth.KV_E4M3])
+def test_mla_other_shapes(T, Hq, L, n, kv_dtype):
+    _need_gpu()
+    case = synth.mla_decode(L=L, seed=50 + T, T=T, Hq=Hq, kv_dtype=kv_dtype)
+    log(f"mla {kv_dtype} T={T} Hq={Hq} L={L} n={n}")
+    sess, _ = session_for(case, requested_splits=n, debug=True)
+    sess.decode()
+    _check_full(case, sess, f"mla {kv_dtype} T={T} Hq={Hq}")
+    _check_debug(case, sess, 1, -(-(T * Hq) // 64))
