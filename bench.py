@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+MFMA_FP8_PEAK_TFLOPS = 5000.0
 METRIC = "decode-attention µs/step and KV GB/s (% of HBM peak) vs num_splits"
 
 
@@ -44,9 +45,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="few-kv-long",
-                    choices=["few-kv-long", "fp8-batched", "mla", "mla-fp8", "ragged", "tiny-gqa"],
+                    choices=["few-kv-long", "fp8-batched", "mla", "mla-fp8", "mla-fp8q", "ragged",
+                             "tiny-gqa"],
                     help="few-kv-long is the headline; the others are extra measurements")
-    ap.add_argument("--L", type=int, default=None, help="sequence length (few-kv-long, mla, mla-fp8, tiny-gqa)")
+    ap.add_argument("--L", type=int, default=None, help="sequence length (few-kv-long, mla, mla-fp8, mla-fp8q, tiny-gqa)")
     ap.add_argument("--sweep", type=str, default="1,2,3,4,6,8,12,16,24,32,48,64,96,128,192,256",
                     help="comma-separated num_splits to sweep ('' to skip); the workload's own "
                          "sweep is 1..64, larger counts are extra points")
@@ -74,6 +76,8 @@ def make_workload(name, L):
         return synth.mla_decode(L=L or 65536)
     if name == "mla-fp8":
         return synth.mla_decode(L=L or 65536, kv_dtype=synth.KV_E4M3)
+    if name == "mla-fp8q":
+        return synth.mla_decode(L=L or 65536, kv_dtype=synth.KV_E4M3, fp8_queries=True)
     if name == "ragged":
         return synth.ragged()
     return synth.tiny_gqa(L=L or 256)
@@ -85,9 +89,11 @@ def describe(case, name):
                 f"bf16 paged (P=16, permuted)")
     if name == "fp8-batched":
         return "batched GQA decode, e4m3 KV: B=8 T=1 Hq=32 Hkv=4 D=128 L=32000 P=16, bf16 Q"
-    if name in ("mla", "mla-fp8"):
-        return (f"MLA decode: B=1 T=6 Hq=128 latent 576/512 L={int(case.seq_lens[0])} P=64 "
-                f"{'e4m3 cache, bf16 Q' if case.kv_dtype == 'e4m3' else 'bf16'}")
+    if name in ("mla", "mla-fp8", "mla-fp8q"):
+        kind = "bf16"
+        if case.kv_dtype == "e4m3":
+            kind = "e4m3 cache, e4m3 Q (FP8 matrix path)" if case.q_scale else "e4m3 cache, bf16 Q"
+        return f"MLA decode: B=1 T=6 Hq=128 latent 576/512 L={int(case.seq_lens[0])} P=64 {kind}"
     if name == "ragged":
         return f"ragged GQA decode: B=32 Hq=32 Hkv=8 D=128 bf16 P=16, sum L={int(case.seq_lens.sum())}"
     return (f"tiny GQA decode: B=1 T=1 Hq=8 Hkv=2 D=128 L={int(case.seq_lens[0])} contiguous bf16, "
@@ -389,7 +395,7 @@ def main():
         s = DecodeSession(q=q, k_cache=k, v_cache=v, block_table=bts[0], seq_lens=case.seq_lens,
                           scale=case.scale, k_scale=case.k_scale, v_scale=case.v_scale,
                           mla=case.mla, requested_splits=n, max_splits=256,
-                          out_fp32=case.out_fp32)
+                          out_fp32=case.out_fp32, q_scale=case.q_scale)
         return s, (time.perf_counter() - t0) * 1e6
 
     if args.only is not None:
@@ -433,9 +439,12 @@ def main():
     part_us = head["partial_kernel_us"]
     if case.mla:
         flops = 2 * case.T * case.Hq * (case.d_qk + case.d_v) * int(case.seq_lens.sum())
-        roof = {"bound": "mfma", "kernel": "mla_partial_kernel",
-                "achieved": round(flops / part_us / 1e6, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(flops / part_us / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4),
+        # e4m3 queries put the products on the FP8 matrix path: its own peak
+        peak = MFMA_FP8_PEAK_TFLOPS if case.q_scale else MFMA_BF16_PEAK_TFLOPS
+        roof = {"bound": "mfma",
+                "kernel": "mla_fp8q_partial_kernel" if case.q_scale else "mla_partial_kernel",
+                "achieved": round(flops / part_us / 1e6, 1), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(flops / part_us / 1e6 / peak, 4),
                 "traffic": None, "kernel_us": part_us, "flops_per_launch": flops}
     else:
         kname = ("gqa_partial_kernel<%d,%s>" % (case.d_qk, "e4m3" if case.kv_dtype == "e4m3" else "bf16"))
@@ -465,7 +474,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "e4m3-kv/bf16" if case.kv_dtype == "e4m3" else "bf16",
+        "dtype": ("e4m3" if case.q_scale else "e4m3-kv/bf16") if case.kv_dtype == "e4m3" else "bf16",
         "data": "synthetic",
         "config": {"workload": f"{describe(case, args.workload)}, "
                                f"{'warm' if args.warm_cache else 'cold'} cache ({R} pool copies)",

@@ -94,6 +94,7 @@ typedef int32_t splitkv_status;
 enum { SPLITKV_KV_BF16 = 0, SPLITKV_KV_E4M3 = 1 };
 enum { SPLITKV_KERNEL_GQA = 0, SPLITKV_KERNEL_MLA = 1 };
 enum { SPLITKV_OUT_BF16 = 0, SPLITKV_OUT_F32 = 1 };
+enum { SPLITKV_Q_BF16 = 0, SPLITKV_Q_E4M3 = 1 };
 
 typedef struct {
   int32_t B, T, Hq, Hkv;
@@ -190,6 +191,10 @@ typedef struct {
                                       B * uniform_splits, checked); the merge then takes its plan
                                       from this value instead of reading num_splits/slot_offset.
                                       0: no such promise */
+  int32_t q_dtype;                 /* SPLITKV_Q_BF16 (0: q used as given) or SPLITKV_Q_E4M3 (MLA
+                                      over an e4m3 cache only: q quantised to e4m3 codes of
+                                      q / q_scale inside the kernel) */
+  float q_scale;                   /* per-tensor query scale for SPLITKV_Q_E4M3 (ignored for bf16) */
 } splitkv_args;
 
 /*
@@ -223,6 +228,16 @@ splitkv_status splitkv_decode_partial_fp8(const splitkv_args* args, void* stream
  * cache whose values are its keys' first columns) scale the scores and the
  * output; the query stays bf16 ("Xqa decode kernels", section "Purpose":
  * bf16 queries over an FP8 KV cache).
+ *
+ * With q_dtype == SPLITKV_Q_E4M3 (e4m3 cache only) the queries go FP8 as well
+ * ("Xqa decode kernels", timeline: FP8-Q, used only where the cache is FP8):
+ * each bf16 query value is quantised to the e4m3 code of q / q_scale (fp32
+ * division, saturated to +-448, nearest code, ties to even -- the encoding of
+ * splitkv_append_kv) and the scores and P V run on the FP8 matrix path with
+ * the softmax weights rounded to e4m3 (each to within 2^-4 of itself; the
+ * weight sum adds the rounded weights).  The result approximates attention
+ * over the dequantised queries, keys and values.  q_scale must be positive
+ * and finite.
  */
 splitkv_status splitkv_mla_decode_partial(const splitkv_args* args, void* stream);
 

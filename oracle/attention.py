@@ -31,6 +31,7 @@ empty split), O = sum_i w_i o_i / sum_i w_i l_i, LSE = M + ln(sum_i w_i l_i).
 """
 import numpy as np
 
+from .append import quantise_bf16
 from .codes import decode_bf16, decode_e4m3
 from .plan import split_range
 
@@ -57,6 +58,21 @@ def dequant_kv(case, b: int, hk: int, upto: int = None):
         K = _decode(case.k_cache[pages, hk, slots, :], case.kv_dtype) * case.k_scale
         V = _decode(case.v_cache[pages, hk, slots, :], case.kv_dtype) * case.v_scale
     return K, V
+
+
+def dequant_q(case, b: int, t: int, h: int) -> np.ndarray:
+    """Query row (b, t, h) as the kernel must read it, in fp64.
+
+    bf16 queries: the decoded codes.  e4m3 queries (case.q_scale set): each
+    value is quantised to the e4m3 code of q / q_scale and read back as code
+    x q_scale, the same per-tensor encoding as an FP8 cache ("Xqa decode
+    kernels", timeline: FP8-Q, used only where the cache is FP8).
+    """
+    codes = case.q[b, t, h]
+    qs = getattr(case, "q_scale", None)
+    if qs is None:
+        return decode_bf16(codes)
+    return decode_e4m3(quantise_bf16(codes, qs)) * float(qs)
 
 
 def attend_rows(q, K, V, sigma, limits):
@@ -115,7 +131,7 @@ def attend(case, select=None):
     for (b, hk), rows in want.items():
         L = int(case.seq_lens[b])
         K, V = dequant_kv(case, b, hk)
-        qhat = np.stack([decode_bf16(case.q[b, t, h]) for (t, h) in rows])
+        qhat = np.stack([dequant_q(case, b, t, h) for (t, h) in rows])
         limits = [L - T + t for (t, h) in rows]
         o, lse = attend_rows(qhat, K, V, case.scale, limits)
         for r, (t, h) in enumerate(rows):
@@ -170,7 +186,7 @@ def split_partials(case, num_splits, slot_offset):
         for hk in range(case.Hkv):
             rows = _rows_of_group(case, hk)
             K, V = dequant_kv(case, b, hk)
-            qhat = np.stack([decode_bf16(case.q[b, t, h]) for (t, h) in rows])
+            qhat = np.stack([dequant_q(case, b, t, h) for (t, h) in rows])
             limits = [L - T + t for (t, h) in rows]
             for i in range(n):
                 s, e = split_range(L, n, i)

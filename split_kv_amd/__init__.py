@@ -45,6 +45,8 @@ SPLITKV_KERNEL_GQA = 0
 SPLITKV_KERNEL_MLA = 1
 SPLITKV_OUT_BF16 = 0
 SPLITKV_OUT_F32 = 1
+SPLITKV_Q_BF16 = 0
+SPLITKV_Q_E4M3 = 1
 
 c_i32, c_i64, c_f32, c_vp, c_sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 
@@ -70,6 +72,7 @@ class splitkv_args(ctypes.Structure):
         ("workspace", c_vp), ("workspace_bytes", c_sz),
         ("out", c_vp), ("out_dtype", c_i32), ("lse", c_vp), ("debug", c_vp),
         ("uniform_splits", c_i32),
+        ("q_dtype", c_i32), ("q_scale", c_f32),
     ]
 
 

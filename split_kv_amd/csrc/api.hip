@@ -15,6 +15,7 @@ namespace splitkv {
 
 hipError_t launch_gqa_partial(const PartialParams& p, int D, bool fp8, hipStream_t stream);
 hipError_t launch_mla_partial(const PartialParams& p, bool fp8, hipStream_t stream);
+hipError_t launch_mla_fp8q_partial(const PartialParams& p, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
 hipError_t launch_e4m3_to_bf16(const uint8_t* in, uint16_t* out, int64_t n, hipStream_t stream);
 
@@ -125,6 +126,15 @@ splitkv_status check_partial(const splitkv_args* a, Kind kind, bool need_ws, con
   }
   if (!(a->scale > 0.f) || !(a->k_scale > 0.f) || !(a->v_scale > 0.f))
     return fail(SPLITKV_ERR_INVALID_ARG, "%s: scales must be positive", fn);
+  if (a->q_dtype != SPLITKV_Q_BF16 && a->q_dtype != SPLITKV_Q_E4M3)
+    return fail(SPLITKV_ERR_INVALID_ARG, "%s: q_dtype=%d", fn, a->q_dtype);
+  if (a->q_dtype == SPLITKV_Q_E4M3) {
+    // e4m3 queries run only where the cache is e4m3 too, on the MLA kernel
+    if (kind != Kind::Mla || a->kv_dtype != SPLITKV_KV_E4M3)
+      return fail(SPLITKV_ERR_UNSUPPORTED, "%s: e4m3 queries need the MLA kernel over an e4m3 cache", fn);
+    if (!(a->q_scale > 0.f) || !(a->q_scale < INFINITY))
+      return fail(SPLITKV_ERR_INVALID_ARG, "%s: q_scale must be positive and finite", fn);
+  }
   // 16-byte vector loads of q rows and cache rows
   const int64_t elem = a->kv_dtype == SPLITKV_KV_E4M3 ? 1 : 2;
   if (!aligned(a->q, 16) || (a->q_stride_b * 2) % 16 || (a->q_stride_t * 2) % 16 ||
@@ -200,7 +210,9 @@ PartialParams make_partial_params(const splitkv_args& a, Kind kind, int row_bloc
   p.row_blocks = row_blocks;
   p.total_wg = a.total_slots * a.Hkv * row_blocks;
   p.page_shift = (a.page_size & (a.page_size - 1)) == 0 ? __builtin_ctz(unsigned(a.page_size)) : -1;
-  p.scale_log2 = a.scale * a.k_scale * kLog2e;
+  const bool q8 = a.q_dtype == SPLITKV_Q_E4M3;
+  p.q_scale = q8 ? a.q_scale : 1.f;
+  p.scale_log2 = a.scale * a.k_scale * p.q_scale * kLog2e;
   p.v_scale = a.v_scale;
   const Layout w = workspace_layout(a);
   p.part_m = w.m;
@@ -225,8 +237,13 @@ splitkv_status run_partial(const splitkv_args* a, Kind kind, bool direct, void* 
   if (st != SPLITKV_OK) return st;
   const PartialParams p = make_partial_params(*a, kind, row_blocks, direct);
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t err = kind == Kind::Mla ? launch_mla_partial(p, a->kv_dtype == SPLITKV_KV_E4M3, s)
-                                           : launch_gqa_partial(p, a->d_qk, kind == Kind::GqaFp8, s);
+  hipError_t err;
+  if (kind != Kind::Mla)
+    err = launch_gqa_partial(p, a->d_qk, kind == Kind::GqaFp8, s);
+  else if (a->q_dtype == SPLITKV_Q_E4M3)
+    err = launch_mla_fp8q_partial(p, s);
+  else
+    err = launch_mla_partial(p, a->kv_dtype == SPLITKV_KV_E4M3, s);
   if (err != hipSuccess) return fail(SPLITKV_ERR_LAUNCH, "%s: launch failed: %s", fn, hipGetErrorString(err));
   return SPLITKV_OK;
 }

@@ -12,35 +12,6 @@
 
 namespace splitkv {
 
-namespace {
-
-constexpr float kE4m3Max = 448.f;
-
-// x / s saturated to +-448 (NaN passes through: both comparisons are false).
-__device__ __forceinline__ float scaled_sat(float x, float s) {
-  const float y = x / s;
-  return y > kE4m3Max ? kE4m3Max : (y < -kE4m3Max ? -kE4m3Max : y);
-}
-
-// Eight bf16 values (four dwords) -> eight e4m3 codes (two dwords).
-__device__ __forceinline__ u32x2 quantise8(u32x4 w, float s) {
-  u32x2 r;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const uint32_t a = h ? w.z : w.x, b = h ? w.w : w.y;
-    const float f0 = scaled_sat(__uint_as_float(a << 16), s);
-    const float f1 = scaled_sat(__uint_as_float(a & 0xffff0000u), s);
-    const float f2 = scaled_sat(__uint_as_float(b << 16), s);
-    const float f3 = scaled_sat(__uint_as_float(b & 0xffff0000u), s);
-    int c = __builtin_amdgcn_cvt_pk_fp8_f32(f0, f1, 0, false);
-    c = __builtin_amdgcn_cvt_pk_fp8_f32(f2, f3, c, true);
-    if (h) r.y = uint32_t(c); else r.x = uint32_t(c);
-  }
-  return r;
-}
-
-}  // namespace
-
 __global__ __launch_bounds__(64) void append_kernel(AppendParams p) {
   const int which = blockIdx.y;          // 0: keys, 1: values
   int r = blockIdx.x;

@@ -38,7 +38,8 @@ struct PartialParams {
   const int32_t* slot_info;     // [S][4]: b, (n << 16) | split, start, end
   int32_t T, Hq, Hkv, g, page_size, rows, row_blocks, total_wg;
   int32_t page_shift;           // log2(page_size) when it is a power of two, else -1
-  float scale_log2;             // scale * k_scale * log2(e)
+  float scale_log2;             // scale * k_scale * log2(e) (times q_scale for e4m3 queries)
+  float q_scale;                // e4m3 queries: codes of q / q_scale
   float v_scale;
   float* part_m;                // [S][T*Hq]
   float* part_l;
@@ -104,6 +105,34 @@ __device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t w) {
   u32x2 r;
   r.x = __builtin_bit_cast(uint32_t, lo);
   r.y = __builtin_bit_cast(uint32_t, hi);
+  return r;
+}
+
+// e4m3 encoding of bf16 values x / s (fp32 division), saturated to the largest
+// finite magnitude and rounded to the nearest code by the hardware conversion
+// (v_cvt_pk_fp8_f32: OCP e4m3fn on gfx950, round to nearest even).
+constexpr float kE4m3Max = 448.f;
+
+// x / s saturated to +-448 (NaN passes through: both comparisons are false).
+__device__ __forceinline__ float scaled_sat(float x, float s) {
+  const float y = x / s;
+  return y > kE4m3Max ? kE4m3Max : (y < -kE4m3Max ? -kE4m3Max : y);
+}
+
+// Eight bf16 values (four dwords) -> eight e4m3 codes (two dwords).
+__device__ __forceinline__ u32x2 quantise8(u32x4 w, float s) {
+  u32x2 r;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t a = h ? w.z : w.x, b = h ? w.w : w.y;
+    const float f0 = scaled_sat(__uint_as_float(a << 16), s);
+    const float f1 = scaled_sat(__uint_as_float(a & 0xffff0000u), s);
+    const float f2 = scaled_sat(__uint_as_float(b << 16), s);
+    const float f3 = scaled_sat(__uint_as_float(b & 0xffff0000u), s);
+    int c = __builtin_amdgcn_cvt_pk_fp8_f32(f0, f1, 0, false);
+    c = __builtin_amdgcn_cvt_pk_fp8_f32(f2, f3, c, true);
+    if (h) r.y = uint32_t(c); else r.x = uint32_t(c);
+  }
   return r;
 }
 

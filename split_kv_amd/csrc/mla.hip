@@ -46,18 +46,18 @@
 // the eight XCDs), so the row blocks' reads of a tile share that XCD's L2.
 // The block-table entries a tile fill needs are read one step ahead, so the
 // fill's address computation never waits for them.
-#include "device.h"
+#include "mla_common.h"
 
 namespace splitkv {
 
 namespace {
 
-constexpr int kMlaDqk = 576;
-constexpr int kMlaDv = 512;
+using namespace mla;
+constexpr int kMlaDqk = kDqk;
+constexpr int kMlaDv = kDv;
 constexpr int kTile = 32;                        // tokens per LDS tile
 constexpr int kPitch = kMlaDqk * 2 / 16;         // 72 16-byte chunks per token row, unpadded
 constexpr int kTileChunks = kTile * kPitch;      // 2304
-constexpr int kWaves = 8;
 constexpr int kTileLoads = kTileChunks / 64;          // 36 wave-level 1 KB loads
 constexpr int kLoadsPerWave = (kTileLoads + kWaves - 1) / kWaves;   // 5: every wave issues the same count
 constexpr int kSlotBytes = kTileLoads * 1024;    // 36864
@@ -74,34 +74,14 @@ constexpr int kPoolBytes = kRing * kSlotBytes;        // 147456 either way
 static_assert(2 * kSlotBytes + 4 * kF8StageBytes == kPoolBytes, "e4m3 rings fill the pool");
 static_assert((kF8LoadsPerWave - 1) * kWaves < kF8TileLoads && kF8LoadsPerWave * kWaves >= kF8TileLoads,
               "three loads per wave cover an e4m3 tile");
-constexpr int kRows = 64;                        // query rows per workgroup
 constexpr int kQk = kMlaDqk / 32 / 2;            // 9 k-steps of 32 key features per half
 constexpr int kPv = kMlaDv / 128 / 2;            // 2 chunks of 128 value features per half
 static_assert(kSlotBytes == kTileChunks * 16 && kTileChunks % 64 == 0, "slot holds a tile");
-static_assert(SPLITKV_ROWS_PER_WG_MLA == kRows, "rows per workgroup");
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-
-// Direct global->LDS load of 16 bytes per lane into the 1 KiB at LDS byte
-// address lds (lane j at lds + 16 j), issued as inline assembly so that the
-// compiler does not track it: it would otherwise make every LDS read of the
-// tile ring wait for all such loads in flight (it cannot tell which slot a
-// load fills).  The kernel waits for these loads explicitly (s_waitcnt vmcnt
-// and a workgroup barrier before a slot is read), and loads complete in
-// order, so the compiler's own waits for other loads stay correct.  M0 holds
-// the LDS address; nothing else in the kernel uses M0.
-__device__ __forceinline__ void dma16(const uint8_t* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory");
-}
-// The same with a uniform 64-bit base and a 32-bit per-lane offset.
-__device__ __forceinline__ void dma16_sbase(const uint8_t* base, uint32_t off, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds)
-               : "memory");
-}
 
 // Position swizzle of a tile token's 16-byte chunks: entry t & 15 of a
 // 16-entry table of 3-bit values, chosen (by search against measured gfx950
@@ -110,16 +90,6 @@ __device__ __forceinline__ void dma16_sbase(const uint8_t* base, uint32_t off, u
 // that both the K reads and the transposing value reads are conflict-free.
 __device__ __forceinline__ uint32_t swz(uint32_t t) {
   return uint32_t((0x8c87fc16ec52ull >> (3 * (t & 15u))) & 7u);
-}
-
-// Workgroup barrier after this wave's LDS operations have completed (a bare
-// s_barrier does not wait for them); the signal fences keep the compiler from
-// moving memory operations across it.
-__device__ __forceinline__ void lds_barrier() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 }  // namespace
@@ -473,64 +443,9 @@ __global__ __launch_bounds__(512) void mla_partial_kernel(PartialParams p, int p
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0x0F70);                      // vmcnt(0)
 
-  const bool direct = p.direct && nsplit == 1;
-  const int64_t R = int64_t(p.T) * p.Hq;
-  {
-    // bring (l, o) from the reference max to the true max of the row
-    const float f = (m_ref == -INFINITY) ? 0.f : fast_exp2(m_ref - m_true);
-    const float m_run = m_true;
-    const float l_tot = column_sum4(l_run * f);
-    const int row = min(rowv, p.rows - 1);
-    const bool real = rowv < p.rows;
-    const int t = row / p.Hq, h = row % p.Hq;
-    const int64_t rix = int64_t(t) * p.Hq + h;
-    float mul = p.v_scale * f;
-    if (direct) mul = l_tot > 0.f ? p.v_scale * f / l_tot : 0.f;
-#pragma unroll
-    for (int c = 0; c < kPv; ++c)
-#pragma unroll
-      for (int e8 = 0; e8 < 8; ++e8) {
-        const int d = 256 * hf + 128 * c + 16 * e8 + 4 * qg;
-        f32x4 v4 = o[c * 8 + e8];
-        v4 *= mul;
-        if (!real) continue;
-        if (direct) {
-          const int64_t oo = (int64_t(b) * R + rix) * kMlaDv + d;
-          if (p.out_f32) {
-            *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + oo) = v4;
-          } else {
-            u32x2 pk = {pack_bf16x2(v4[0], v4[1]), pack_bf16x2(v4[2], v4[3])};
-            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + oo) = pk;
-          }
-        } else {
-          *reinterpret_cast<f32x4*>(p.part_o + (int64_t(slot) * R + rix) * kMlaDv + d) = v4;
-        }
-      }
-    // both waves of the pair hold the same (m, l); one writes them
-    if (real && qg == 0 && hf == 0) {
-      const bool empty = m_run == -INFINITY;
-      if (direct) {
-        if (p.lse)
-          p.lse[int64_t(b) * R + rix] =
-              (empty || !(l_tot > 0.f)) ? -INFINITY : (m_run + log2f(l_tot)) * kLn2;
-      } else {
-        p.part_m[int64_t(slot) * R + rix] = empty ? -INFINITY : m_run * kLn2;
-        p.part_l[int64_t(slot) * R + rix] = l_tot;
-      }
-    }
-  }
+  store_rows(p, o, rowv, qg, hf, b, slot, nsplit, m_ref, m_true, l_run);
 
-  if (p.debug && tid == 0) {
-    int32_t* rec = p.debug + (int64_t(slot) * p.row_blocks + rb) * 8;
-    rec[0] = b;
-    rec[1] = split;
-    rec[2] = 0;
-    rec[3] = s;
-    rec[4] = e;
-    rec[5] = dbg_groups;
-    rec[6] = dbg_xor;
-    rec[7] = int(dbg_sum & 0x7fffffffu);
-  }
+  if (p.debug && tid == 0) store_debug(p, slot, rb, b, split, s, e, dbg_groups, dbg_xor, dbg_sum);
 }
 
 hipError_t launch_mla_partial(const PartialParams& p, bool fp8, hipStream_t stream) {

@@ -1,0 +1,113 @@
+// Pieces shared by the MLA partial kernels (bf16 and e4m3 queries): the
+// direct global->LDS tile loads, the LDS barrier, and the epilogue that writes
+// a workgroup's partial (m, l, o) or, for a single-split sequence, the final
+// output and log-sum-exp.
+#pragma once
+
+#include "device.h"
+
+namespace splitkv {
+namespace mla {
+
+constexpr int kDqk = 576;                        // latent row: 512 value features + 64 rope
+constexpr int kDv = 512;
+constexpr int kRows = 64;                        // query rows per workgroup
+constexpr int kWaves = 8;
+static_assert(SPLITKV_ROWS_PER_WG_MLA == kRows, "rows per workgroup");
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+// Direct global->LDS load of 16 bytes per lane into the 1 KiB at LDS byte
+// address lds (lane j at lds + 16 j), issued as inline assembly so that the
+// compiler does not track it: it would otherwise make every LDS read of the
+// tile ring wait for all such loads in flight (it cannot tell which slot a
+// load fills).  The kernels wait for these loads explicitly (s_waitcnt vmcnt
+// and a workgroup barrier before a slot is read), and loads complete in
+// order, so the compiler's own waits for other loads stay correct.  M0 holds
+// the LDS address; nothing else in the kernels uses M0.
+__device__ __forceinline__ void dma16(const uint8_t* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory");
+}
+// The same with a uniform 64-bit base and a 32-bit per-lane offset.
+__device__ __forceinline__ void dma16_sbase(const uint8_t* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds)
+               : "memory");
+}
+
+// Workgroup barrier after this wave's LDS operations have completed (a bare
+// s_barrier does not wait for them); the signal fences keep the compiler from
+// moving memory operations across it.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Epilogue of one wave: lane (n16, qg) of wave half hf holds
+// O[row][256 hf + 16 e + 4 qg + i] in o[e][i] (unnormalised, relative to the
+// reference max m_ref), the running true max m_true and its part of the
+// weight sum l_run (the row's four qg lanes hold parts that add up).  Both
+// waves of a pair hold the same (m, l); the hf == 0 wave writes them.
+__device__ __forceinline__ void store_rows(const PartialParams& p, const f32x4 (&o)[16], int rowv,
+                                           int qg, int hf, int b, int slot, int nsplit, float m_ref,
+                                           float m_true, float l_run) {
+  const bool direct = p.direct && nsplit == 1;
+  const int64_t R = int64_t(p.T) * p.Hq;
+  // bring (l, o) from the reference max to the true max of the row
+  const float f = (m_ref == -INFINITY) ? 0.f : fast_exp2(m_ref - m_true);
+  const float m_run = m_true;
+  const float l_tot = column_sum4(l_run * f);
+  const int row = min(rowv, p.rows - 1);
+  const bool real = rowv < p.rows;
+  const int t = row / p.Hq, h = row % p.Hq;
+  const int64_t rix = int64_t(t) * p.Hq + h;
+  float mul = p.v_scale * f;
+  if (direct) mul = l_tot > 0.f ? p.v_scale * f / l_tot : 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int d = 256 * hf + 16 * e + 4 * qg;
+    f32x4 v4 = o[e];
+    v4 *= mul;
+    if (!real) continue;
+    if (direct) {
+      const int64_t oo = (int64_t(b) * R + rix) * kDv + d;
+      if (p.out_f32) {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + oo) = v4;
+      } else {
+        u32x2 pk = {pack_bf16x2(v4[0], v4[1]), pack_bf16x2(v4[2], v4[3])};
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + oo) = pk;
+      }
+    } else {
+      *reinterpret_cast<f32x4*>(p.part_o + (int64_t(slot) * R + rix) * kDv + d) = v4;
+    }
+  }
+  if (real && qg == 0 && hf == 0) {
+    const bool empty = m_run == -INFINITY;
+    if (direct) {
+      if (p.lse)
+        p.lse[int64_t(b) * R + rix] = (empty || !(l_tot > 0.f)) ? -INFINITY : (m_run + log2f(l_tot)) * kLn2;
+    } else {
+      p.part_m[int64_t(slot) * R + rix] = empty ? -INFINITY : m_run * kLn2;
+      p.part_l[int64_t(slot) * R + rix] = l_tot;
+    }
+  }
+}
+
+// The paged-addressing record of a workgroup (its range and a digest of the
+// pages its 16-token groups read), when the caller asked for it.
+__device__ __forceinline__ void store_debug(const PartialParams& p, int slot, int rb, int b, int split,
+                                            int s, int e, int groups, int pxor, uint32_t psum) {
+  int32_t* rec = p.debug + (int64_t(slot) * p.row_blocks + rb) * 8;
+  rec[0] = b;
+  rec[1] = split;
+  rec[2] = 0;
+  rec[3] = s;
+  rec[4] = e;
+  rec[5] = groups;
+  rec[6] = pxor;
+  rec[7] = int(psum & 0x7fffffffu);
+}
+
+}  // namespace mla
+}  // namespace splitkv

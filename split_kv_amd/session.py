@@ -12,7 +12,8 @@ from __future__ import annotations
 import numpy as np
 
 from . import (SPLITKV_KERNEL_GQA, SPLITKV_KERNEL_MLA, SPLITKV_KV_BF16, SPLITKV_KV_E4M3,
-               SPLITKV_MAX_SPLITS_LIMIT, SPLITKV_OUT_BF16, SPLITKV_OUT_F32, SPLITKV_ROWS_PER_WG_GQA, SPLITKV_ROWS_PER_WG_MLA,
+               SPLITKV_MAX_SPLITS_LIMIT, SPLITKV_OUT_BF16, SPLITKV_OUT_F32, SPLITKV_Q_BF16, SPLITKV_Q_E4M3,
+               SPLITKV_ROWS_PER_WG_GQA, SPLITKV_ROWS_PER_WG_MLA,
                splitkv_args, splitkv_combine, splitkv_decode, splitkv_decode_partial,
                splitkv_decode_partial_fp8, splitkv_mla_decode_partial, splitkv_plan,
                splitkv_plan_args, splitkv_workspace_bytes)
@@ -32,12 +33,15 @@ class DecodeSession:
     v_cache:     same with d_v (None for MLA, where V = K[..., :d_v])
     block_table: int32 [B, max_pages] on the device
     seq_lens:    host sequence lengths (numpy or list)
+    q_scale:     MLA over an e4m3 cache only: if given, the kernel quantises q to
+                 e4m3 codes of q / q_scale and runs on the FP8 matrix path
     """
 
     def __init__(self, *, q, k_cache, v_cache, block_table, seq_lens, scale: float,
                  k_scale: float = 1.0, v_scale: float = 1.0, mla: bool = False,
                  requested_splits: int = 0, max_splits: int = SPLITKV_MAX_SPLITS_LIMIT, num_cus: int = 0,
-                 out_fp32: bool = False, with_lse: bool = True, debug: bool = False):
+                 out_fp32: bool = False, with_lse: bool = True, debug: bool = False,
+                 q_scale: float | None = None):
         torch = _torch()
         self.torch = torch
         dev = q.device
@@ -54,6 +58,8 @@ class DecodeSession:
         self.seq_lens_host = np.ascontiguousarray(seq_lens, dtype=np.int32)
         self.seq_lens = torch.as_tensor(self.seq_lens_host, device=dev)
         self.scale, self.k_scale, self.v_scale = float(scale), float(k_scale), float(v_scale)
+        self.q_dtype = SPLITKV_Q_BF16 if q_scale is None else SPLITKV_Q_E4M3
+        self.q_scale = 1.0 if q_scale is None else float(q_scale)
         self.out_fp32 = out_fp32
         self.out = torch.empty((B, T, Hq, d_v), dtype=torch.float32 if out_fp32 else torch.bfloat16,
                                device=dev)
@@ -113,6 +119,7 @@ class DecodeSession:
         a.d_qk, a.d_v, a.page_size, a.num_pages = s["d_qk"], s["d_v"], s["P"], s["num_pages"]
         a.kv_dtype = self.kv_dtype
         a.scale, a.k_scale, a.v_scale = self.scale, self.k_scale, self.v_scale
+        a.q_dtype, a.q_scale = self.q_dtype, self.q_scale
         a.workspace = self.workspace.data_ptr()
         a.workspace_bytes = self.workspace.numel() * 4
         a.out = self.out.data_ptr()

@@ -67,6 +67,7 @@ class Case:
     k_cache: np.ndarray           # [num_pages, Hkv, P, d_qk] uint16 or uint8 codes
     v_cache: Optional[np.ndarray]  # [num_pages, Hkv, P, d_v] codes, None for MLA
     seed: int
+    q_scale: Optional[float] = None  # e4m3 queries: per-tensor scale (None: bf16 queries)
 
     @property
     def g(self) -> int:
@@ -192,8 +193,11 @@ def make_case(name: str, *, B: int, T: int, Hq: int, Hkv: int, d_qk: int, d_v: i
               seq_lens, page_size: int, kv_dtype: str = KV_BF16, mla: bool = False,
               std: float = 1.0, q_std: Optional[float] = None, scale: Optional[float] = None,
               out_fp32: bool = False, seed: int = 0, contiguous: bool = False,
-              fp8_scale: Optional[float] = None) -> Case:
-    """Generic generator; every workload below is one call of it."""
+              fp8_scale: Optional[float] = None, fp8_queries: bool = False) -> Case:
+    """Generic generator; every workload below is one call of it.
+
+    fp8_queries: the caller asks for e4m3 queries with the per-tensor scale
+    amax|q| / 448 (the recipe of the e4m3 caches); q itself stays bf16."""
     rng = np.random.default_rng(seed)
     seq_lens = np.asarray(seq_lens, dtype=np.int32).reshape(B)
     if scale is None:
@@ -212,10 +216,14 @@ def make_case(name: str, *, B: int, T: int, Hq: int, Hkv: int, d_qk: int, d_v: i
                                        seq_lens, fp8_scale)
         v_cache, v_scale = _fill_cache(rng, num_pages, Hkv, page_size, d_v, std, kv_dtype, bt,
                                        seq_lens, fp8_scale)
+    q_scale = None
+    if fp8_queries:
+        qv = (q.astype(np.uint32) << 16).view(np.float32)
+        q_scale = float(np.float32(float(np.max(np.abs(qv))) / E4M3_MAX))
     return Case(name=name, B=B, T=T, Hq=Hq, Hkv=Hkv, d_qk=d_qk, d_v=d_v, page_size=page_size,
                 kv_dtype=kv_dtype, mla=mla, causal=T > 1, scale=scale, k_scale=k_scale,
                 v_scale=v_scale, out_fp32=out_fp32, seq_lens=seq_lens, block_table=bt, q=q,
-                k_cache=k_cache, v_cache=v_cache, seed=seed)
+                k_cache=k_cache, v_cache=v_cache, seed=seed, q_scale=q_scale)
 
 
 def tiny_gqa(L: int = 256, seed: int = 1001) -> Case:
@@ -239,14 +247,15 @@ def fp8_batched(B: int = 8, L: int = 32000, seed: int = 1003, fp8_scale=None) ->
 
 
 def mla_decode(L: int = 2048, seed: int = 1004, T: int = 6, Hq: int = 128,
-               kv_dtype: str = KV_BF16) -> Case:
+               kv_dtype: str = KV_BF16, fp8_queries: bool = False) -> Case:
     """MLA decode: 6 causal query tokens, 128 heads, one 576-wide latent head (V = first 512).
 
     kv_dtype e4m3 stores the latent cache as FP8 codes with one per-tensor
-    scale (keys and values share it, being the same rows)."""
-    return make_case("mla" if kv_dtype == KV_BF16 else "mla-fp8", B=1, T=T, Hq=Hq, Hkv=1, d_qk=576,
-                     d_v=512, seq_lens=[L], page_size=64, mla=True, std=0.5, seed=seed,
-                     kv_dtype=kv_dtype)
+    scale (keys and values share it, being the same rows); fp8_queries (e4m3
+    cache only) adds a query scale for e4m3 queries."""
+    name = "mla" if kv_dtype == KV_BF16 else ("mla-fp8q" if fp8_queries else "mla-fp8")
+    return make_case(name, B=1, T=T, Hq=Hq, Hkv=1, d_qk=576, d_v=512, seq_lens=[L], page_size=64,
+                     mla=True, std=0.5, seed=seed, kv_dtype=kv_dtype, fp8_queries=fp8_queries)
 
 
 def ragged(B: int = 32, seed: int = 1005, hi: int = 131072, seq_lens=None) -> Case:

@@ -31,7 +31,7 @@ def session_for(case, requested_splits=0, max_splits=64, layout="HND", q_pad_hea
                          seq_lens=case.seq_lens, scale=case.scale, k_scale=case.k_scale,
                          v_scale=case.v_scale, mla=case.mla, requested_splits=requested_splits,
                          max_splits=max_splits, out_fp32=case.out_fp32, debug=debug,
-                         num_cus=num_cus), t
+                         num_cus=num_cus, q_scale=case.q_scale), t
 
 
 def to_np(x):

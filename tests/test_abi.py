@@ -208,6 +208,29 @@ def test_mla_shape_errors_without_device():
     assert lib.splitkv_decode(ctypes.byref(a), 5, None) == sk.SPLITKV_ERR_INVALID_ARG
 
 
+@pytest.mark.parametrize("over,code", [
+    (dict(q_dtype=7), sk.SPLITKV_ERR_INVALID_ARG),
+    (dict(q_dtype=1, q_scale=0.0), sk.SPLITKV_ERR_INVALID_ARG),
+    (dict(q_dtype=1, q_scale=float("inf")), sk.SPLITKV_ERR_INVALID_ARG),
+    (dict(q_dtype=1, q_scale=0.01, kv_dtype=0), sk.SPLITKV_ERR_UNSUPPORTED),
+])
+def test_e4m3_query_errors_without_device(over, code):
+    # an MLA-shaped call over an e4m3 cache; the workspace is also too small,
+    # so no case here can get past validation
+    lib = _lib()
+    base = dict(Hkv=1, Hq=128, T=6, d_qk=576, d_v=512, kv_dtype=1, q_stride_b=6 * 128 * 576,
+                q_stride_t=128 * 576, q_stride_h=576, k_stride_page=16 * 576, k_stride_head=16 * 576,
+                k_stride_tok=576, workspace_bytes=16)
+    base.update(over)
+    a = _args(**base)
+    assert lib.splitkv_mla_decode_partial(ctypes.byref(a), None) == code, sk.splitkv_last_error()
+    assert "q_" in sk.splitkv_last_error() or "e4m3 queries" in sk.splitkv_last_error()
+    # the grouped-query kernels take no e4m3 queries
+    a = _args(q_dtype=1, q_scale=0.01, workspace_bytes=16)
+    assert lib.splitkv_decode_partial(ctypes.byref(a), None) == sk.SPLITKV_ERR_UNSUPPORTED
+    assert "e4m3 queries" in sk.splitkv_last_error()
+
+
 def _append_args(**over):
     a = sk.splitkv_append_args()
     base = dict(k_new=0x1000, v_new=0x1800, k_new_stride_b=2 * 128, k_new_stride_t=2 * 128,

@@ -480,6 +480,69 @@ def test_mla_fp8_full_size_sampled():
 
 
 # ---------------------------------------------------------------------------
+# MLA with e4m3 queries over the e4m3 latent cache (the FP8 matrix path): the
+# oracle quantises the queries with the same per-tensor encoding and attends
+# exactly over the dequantised values; the kernel also rounds the softmax
+# weights to e4m3, which the FP8 bar (3e-2) covers.
+
+@pytest.mark.parametrize("n", [1, 4, 8])
+def test_mla_fp8q_small_full_compare(n):
+    _need_gpu()
+    case = synth.mla_decode(L=2048, kv_dtype=synth.KV_E4M3, fp8_queries=True)
+    log(f"mla e4m3 queries L=2048 n={n} q_scale={case.q_scale} k_scale={case.k_scale}")
+    sess, _ = session_for(case, requested_splits=n, debug=True)
+    sess.decode()
+    _check_full(case, sess, f"mla fp8q n={n}")
+    _check_debug(case, sess, 1, 12)
+
+
+def test_mla_fp8q_tiles_cut_by_ranges_and_pages():
+    _need_gpu()
+    case = synth.mla_decode(L=2000, seed=13, kv_dtype=synth.KV_E4M3, fp8_queries=True)
+    log("mla e4m3 queries L=2000 n=3 (partial sub-tiles and windows, sub-tiles across pages)")
+    sess, _ = session_for(case, requested_splits=3, debug=True)
+    sess.decode()
+    _check_full(case, sess, "mla fp8q L=2000 n=3")
+    _check_debug(case, sess, 1, 12)
+
+
+@pytest.mark.parametrize("n", [1, 4])
+def test_mla_fp8q_sequences_shorter_than_the_draft(n):
+    _need_gpu()
+    case = synth.make_case("mla-fp8q-short", B=3, T=6, Hq=128, Hkv=1, d_qk=576, d_v=512,
+                           seq_lens=[0, 3, 100], page_size=64, mla=True, std=0.5, seed=4,
+                           kv_dtype=synth.KV_E4M3, fp8_queries=True)
+    log(f"mla e4m3 queries seq_lens=[0,3,100] n={n}")
+    sess, _ = session_for(case, requested_splits=n, debug=True)
+    sess.decode()
+    _check_full(case, sess, f"mla fp8q short n={n}")
+    _check_debug(case, sess, 1, 12)
+
+
+@pytest.mark.parametrize("T,Hq,L,n", [(1, 128, 3000, 4), (2, 16, 777, 3), (3, 40, 1500, 0)])
+def test_mla_fp8q_other_shapes(T, Hq, L, n):
+    _need_gpu()
+    case = synth.mla_decode(L=L, seed=60 + T, T=T, Hq=Hq, kv_dtype=synth.KV_E4M3, fp8_queries=True)
+    log(f"mla e4m3 queries T={T} Hq={Hq} L={L} n={n}")
+    sess, _ = session_for(case, requested_splits=n, debug=True)
+    sess.decode()
+    _check_full(case, sess, f"mla fp8q T={T} Hq={Hq}")
+    _check_debug(case, sess, 1, -(-(T * Hq) // 64))
+
+
+def test_mla_fp8q_full_size_sampled():
+    _need_gpu()
+    case = synth.mla_decode(L=65536, kv_dtype=synth.KV_E4M3, fp8_queries=True)
+    log("mla e4m3 queries L=65536 auto plan, sampled rows")
+    sess, _ = session_for(case, requested_splits=0, max_splits=256)
+    sess.decode()
+    rng = np.random.default_rng(6)
+    rows = [(0, int(t), int(h)) for t, h in zip(rng.integers(0, 6, 24), rng.integers(0, 128, 24))]
+    rows += [(0, 0, 0), (0, 5, 127)]
+    _check_rows(case, sess, rows, "mla fp8q L=65536")
+
+
+# ---------------------------------------------------------------------------
 # MLA at other decode shapes: one token (no causal mask within the draft),
 # and head counts whose T*Hq rows leave the last 64-row block partly empty.
 

@@ -130,3 +130,28 @@ def test_wrong_slot_is_caught(monkeypatch):
         return orig(kc, vc, kn, vn, bt, np.asarray(pos) + 1, P, dt, k_scale, v_scale)
     monkeypatch.setattr(TAP, "append_kv", bad)
     _fails(TAP.test_append_writes_exactly_the_target_rows, "bf16", False)
+
+
+def test_query_scale_dropped_is_caught(monkeypatch):
+    import tests.test_oracle_queries as TQ
+    from oracle.append import quantise_bf16
+
+    def bad(case, b, t, h):
+        if case.q_scale is None:
+            return C.decode_bf16(case.q[b, t, h])
+        return C.decode_e4m3(quantise_bf16(case.q[b, t, h], case.q_scale))     # no x q_scale
+    monkeypatch.setattr(A, "dequant_q", bad)
+    monkeypatch.setattr(TQ, "dequant_q", bad)
+    _fails(TQ.test_representable_queries_are_unchanged_and_attention_matches)
+    _fails(TQ.test_queries_go_to_the_nearest_code)
+
+
+def test_unquantised_queries_are_caught(monkeypatch):
+    import tests.test_oracle_queries as TQ
+
+    def bad(case, b, t, h):
+        return C.decode_bf16(case.q[b, t, h])
+    monkeypatch.setattr(A, "dequant_q", bad)
+    monkeypatch.setattr(TQ, "dequant_q", bad)
+    _fails(TQ.test_queries_go_to_the_nearest_code)
+    _fails(TQ.test_queries_saturate_at_448_scales)
