@@ -269,16 +269,17 @@ def ragged(B: int = 32, seed: int = 1005, hi: int = 131072, seq_lens=None) -> Ca
 
 
 def ramp_keys(case: Case, steps, d0: int = 0, d1: Optional[int] = None) -> Case:
-    """Scale key features [d0, d1) of later tokens, in place (bf16 caches only).
+    """Scale key features [d0, d1) of later tokens, in place.
 
     ``steps`` is a list of (first_token, factor): logical token j of every
     sequence gets the factor of the last step with first_token <= j (1 before
     the first step).  Scaled values are re-rounded to bf16.  Scores then grow
     along the sequence, so a running softmax maximum jumps inside a split;
     with [d0, d1) inside the rope features of an MLA cache, the values (its
-    first d_v features) stay as drawn.
+    first d_v features) stay as drawn.  An e4m3 cache keeps its scale: the
+    scaled codes are re-rounded to e4m3 (clamped to +-448), so the case must
+    have been drawn with a scale that leaves room for the factors.
     """
-    assert case.kv_dtype == KV_BF16
     d1 = case.d_qk if d1 is None else d1
     P = case.page_size
     steps = sorted(steps)
@@ -292,8 +293,13 @@ def ramp_keys(case: Case, steps, d0: int = 0, d1: Optional[int] = None) -> Case:
                 continue
             page = case.block_table[b, j // P]
             codes = case.k_cache[page, :, j % P, d0:d1]
-            vals = (codes.astype(np.uint32) << 16).view(np.float32) * np.float32(f)
-            case.k_cache[page, :, j % P, d0:d1] = to_bf16_codes(vals)
+            if case.kv_dtype == KV_BF16:
+                vals = (codes.astype(np.uint32) << 16).view(np.float32) * np.float32(f)
+                case.k_cache[page, :, j % P, d0:d1] = to_bf16_codes(vals)
+            else:
+                torch = _torch()
+                vals = torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).float().numpy()
+                case.k_cache[page, :, j % P, d0:d1] = to_e4m3_codes(vals * np.float32(f))
     return case
 
 

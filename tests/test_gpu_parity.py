@@ -373,6 +373,16 @@ def ramped_mla():
     return synth.ramp_keys(case, [(700, 30.0), (1300, 100.0)], d0=512)
 
 
+def ramped_mla_e4m3(fp8_queries):
+    # the cache scale leaves room for the x100 rope features (2.65 is about
+    # the largest |x| of the N(0, 0.5) draw)
+    case = synth.make_case("mla-fp8-ramp", B=1, T=6, Hq=128, Hkv=1, d_qk=576, d_v=512,
+                           seq_lens=[2048], page_size=64, mla=True, std=0.5, seed=23,
+                           kv_dtype=synth.KV_E4M3, fp8_scale=100 * 2.65 / 448,
+                           fp8_queries=fp8_queries)
+    return synth.ramp_keys(case, [(700, 30.0), (1300, 100.0)], d0=512)
+
+
 def ramped_few_kv():
     case = synth.few_kv_long(L=2000, seed=22)
     return synth.ramp_keys(case, [(700, 4.0), (1300, 16.0)])
@@ -386,6 +396,18 @@ def test_mla_rescale_inside_split(n):
     sess, _ = session_for(case, requested_splits=n)
     sess.decode()
     _check_full(case, sess, f"mla ramp n={n}")
+
+
+@pytest.mark.parametrize("fp8_queries", [False, True])
+@pytest.mark.parametrize("n", [1, 4])
+def test_mla_e4m3_rescale_inside_split(n, fp8_queries):
+    _need_gpu()
+    case = ramped_mla_e4m3(fp8_queries)
+    log(f"mla e4m3 cache, {'e4m3' if fp8_queries else 'bf16'} queries, L=2048 rope keys ramped "
+        f"x30 at 700, x100 at 1300, n={n}")
+    sess, _ = session_for(case, requested_splits=n)
+    sess.decode()
+    _check_full(case, sess, f"mla e4m3 ramp n={n} q8={fp8_queries}")
 
 
 @pytest.mark.parametrize("n", [1, 4])

@@ -11,8 +11,9 @@ import math
 
 import numpy as np
 
+import oracle
 from oracle import plan as oplan
-from tests.test_gpu_parity import ramped_few_kv, ramped_mla
+from tests.test_gpu_parity import ramped_few_kv, ramped_mla, ramped_mla_e4m3
 
 
 def _decode(codes):
@@ -23,7 +24,10 @@ def _keys(case, hk):
     P = case.page_size
     L = int(case.seq_lens[0])
     pages = case.block_table[0, np.arange(L) // P]
-    return _decode(case.k_cache[pages, hk, np.arange(L) % P, :])      # [L, d_qk]
+    codes = case.k_cache[pages, hk, np.arange(L) % P, :]
+    if case.kv_dtype == "e4m3":
+        return oracle.decode_e4m3(codes) * case.k_scale                # [L, d_qk]
+    return _decode(codes)
 
 
 def _max_jump(case, split_ranges):
@@ -57,3 +61,7 @@ def test_mla_ramp_jumps_past_the_margin():
 
 def test_few_kv_ramp_jumps_past_the_margin():
     _check(ramped_few_kv())
+
+
+def test_mla_e4m3_ramp_jumps_past_the_margin():
+    _check(ramped_mla_e4m3(False))
