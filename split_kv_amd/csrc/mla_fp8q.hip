@@ -9,9 +9,9 @@
 // sum(q code x k code) x q_scale x k_scale x softmax scale.  The
 // probabilities enter P V as e4m3 too, as two terms: P (<= 2^8 against the
 // reference max, inside e4m3's range) = hi + lo + r with hi and lo e4m3 codes
-// and |r| <= 2^-8 P + 2^-10; one e4m3 term alone (3 mantissa bits, up to
-// 2^-4 relative per weight) moves an output that averages a few values of
-// comparable weight by several hundredths.
+// and |r| <= 2^-8 P + 2^-10 (the weight sum adds P itself); one e4m3 term
+// alone (3 mantissa bits, up to 2^-4 relative per weight) moves an output
+// that averages a few values of comparable weight by several hundredths.
 //
 // Work layout (same row blocks, pairs and epilogue as the bf16-query kernel):
 // a workgroup keeps 64 query rows, eight waves (two per SIMD) form four
@@ -323,8 +323,8 @@ __global__ __launch_bounds__(512) void mla_fp8q_partial_kernel(PartialParams p, 
   };
 
   // Window w (sub-tiles 4w .. 4w+3): online softmax over its 128 tokens in
-  // base 2 (lazily moved reference max), P rounded to e4m3, then
-  // O^T[d][row] += V^T P^T with one 128-deep product per 16 value features.
+  // base 2 (lazily moved reference max), P as two e4m3 terms, then
+  // O^T[d][row] += V^T P^T with two 128-deep products (hi, lo) per 16 value features.
   auto window = [&](int w) __attribute__((always_inline)) {
     float m32 = sv[0];
 #pragma unroll
