@@ -249,6 +249,18 @@ def measured_traffic():
         return None, f"counters unavailable: {e}"
 
 
+def monotonic(sweep, band=1.03):
+    """The target's check: no split count slower than one split (within a
+    3% run-to-run band), over the requested counts that were timed."""
+    one = [r["us_per_step"] for r in sweep if r["num_splits_requested"] == 1]
+    if not one:
+        return None
+    worst = max(sweep, key=lambda r: r["us_per_step"])
+    ratio = worst["us_per_step"] / one[0]
+    return {"ok": ratio <= band, "band": band, "worst_over_one_split": round(ratio, 4),
+            "worst_request": worst["num_splits_requested"]}
+
+
 def cpu_baseline(case, seconds):
     """Time the fp64 oracle (as it stands) on the same workload, repeated ~`seconds`."""
     import oracle
@@ -257,19 +269,33 @@ def cpu_baseline(case, seconds):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         cores = 1
-    t0 = time.perf_counter()
-    n = 0
-    while True:
-        oracle.attend(case)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
+
+    def timed(budget):
+        t0 = time.perf_counter()
+        n = 0
+        while True:
+            oracle.attend(case)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                return n, el
+
+    n, el = timed(seconds)
     per_step = el / n
-    return {"value": case.kv_bytes() / per_step / 1e9, "unit": "GB/s", "cores": int(cores),
-            "kind": "oracle",
-            "sample": f"{n} full oracle steps of the bench workload (fp64 numpy, {el:.1f} s); "
-                      f"{per_step * 1e6:.0f} us per step"}
+    rec = {"value": case.kv_bytes() / per_step / 1e9, "unit": "GB/s", "cores": int(cores),
+           "kind": "oracle",
+           "sample": f"{n} full oracle steps of the bench workload (fp64 numpy, {el:.1f} s); "
+                     f"{per_step * 1e6:.0f} us per step"}
+    # the same oracle with its BLAS held to one thread, half the time budget
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            n1, el1 = timed(seconds / 2)
+        rec["single_thread"] = {"value": case.kv_bytes() / (el1 / n1) / 1e9, "unit": "GB/s",
+                                "cores": 1, "sample": f"{n1} steps in {el1:.1f} s"}
+    except Exception as e:                    # threadpoolctl missing: report the one timing
+        rec["single_thread"] = f"not measured: {e}"
+    return rec
 
 
 def copy_calibration():
@@ -484,6 +510,7 @@ def main():
                    "kv_bytes_per_step": kv_bytes,
                    "plan_host_us": head["plan_host_us"]},
         "sweep": sweep,
+        "monotonic": monotonic(sweep),
         "roofline": roof,
     }
     if not headline:
