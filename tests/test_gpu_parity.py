@@ -552,6 +552,23 @@ def test_mla_fp8q_other_shapes(T, Hq, L, n):
     _check_debug(case, sess, 1, -(-(T * Hq) // 64))
 
 
+def test_mla_fp8q_saturating_scale_strided_query_nhd_cache():
+    # q_scale an eighth of amax|q| / 448: the largest query values saturate at
+    # +-448 codes (the oracle applies the same clamp); the query is a strided
+    # view (padded head dimension) and the latent cache is stored NHD
+    import dataclasses
+    _need_gpu()
+    case = synth.mla_decode(L=1000, seed=71, kv_dtype=synth.KV_E4M3, fp8_queries=True)
+    case = dataclasses.replace(case, q_scale=float(np.float32(case.q_scale / 8)))
+    qv = np.abs(oracle.decode_bf16(case.q)) / case.q_scale
+    log(f"mla e4m3 queries, q_scale={case.q_scale}: {int((qv > 448).sum())} query values saturate")
+    assert (qv > 448).sum() > 100
+    sess, _ = session_for(case, requested_splits=4, layout="NHD", q_pad_heads=3, debug=True)
+    sess.decode()
+    _check_full(case, sess, "mla fp8q saturating q_scale, NHD, strided q")
+    _check_debug(case, sess, 1, 12)
+
+
 def test_mla_fp8q_full_size_sampled():
     _need_gpu()
     case = synth.mla_decode(L=65536, kv_dtype=synth.KV_E4M3, fp8_queries=True)
