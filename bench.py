@@ -249,6 +249,20 @@ def measured_traffic():
         return None, f"counters unavailable: {e}"
 
 
+def step_bytes(case, num_splits):
+    """Bytes a step must move besides the KV (query in, output and LSE out),
+    and the method's own overhead: the fp32 partials (m, l, o) written by the
+    partial kernel and read back by the combine (sequences with one split
+    write their output directly and have none)."""
+    rows = case.B * case.T * case.Hq
+    q = rows * case.d_qk * 2
+    out = rows * case.d_v * (4 if case.out_fp32 else 2) + rows * 4
+    slots = int(sum(int(n) for n in num_splits if int(n) > 1))
+    partials = slots * case.T * case.Hq * (case.d_v + 2) * 4
+    return {"algorithmic_bytes_total": case.kv_bytes() + q + out,
+            "partial_bytes_written_and_read": 2 * partials}
+
+
 def monotonic(sweep, band=1.03):
     """The target's check: no split count slower than one split (within a
     3% run-to-run band), over the requested counts that were timed."""
@@ -508,6 +522,7 @@ def main():
                    "num_splits_requested": head["num_splits_requested"],
                    "step": "partial kernel, then combine kernel (skipped when every sequence has one split)",
                    "kv_bytes_per_step": kv_bytes,
+                   **step_bytes(case, head["sess"].num_splits_host),
                    "plan_host_us": head["plan_host_us"]},
         "sweep": sweep,
         "monotonic": monotonic(sweep),
