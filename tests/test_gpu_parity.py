@@ -569,6 +569,30 @@ def test_mla_fp8q_saturating_scale_strided_query_nhd_cache():
     _check_debug(case, sess, 1, 12)
 
 
+@pytest.mark.parametrize("mode", ["bf16", "e4m3", "e4m3-queries"])
+@pytest.mark.parametrize("seed", range(6))
+def test_mla_random_shapes(seed, mode):
+    # seeded draws of batch, draft length, head count, lengths (tiles, windows
+    # and sub-tiles cut anywhere), page size and split request, for each MLA path
+    _need_gpu()
+    rng = np.random.default_rng(900 + seed)
+    B = int(rng.integers(1, 4))
+    T = int(rng.integers(1, 7))
+    Hq = int(rng.choice([16, 40, 64, 128]))
+    lens = [int(x) for x in rng.integers(0, 2600, size=B)]
+    n = int(rng.choice([0, 1, 2, 5, 9]))
+    case = synth.make_case(f"mla-rand{seed}", B=B, T=T, Hq=Hq, Hkv=1, d_qk=576, d_v=512,
+                           seq_lens=lens, page_size=int(rng.choice([16, 64, 128])), mla=True,
+                           std=0.5, seed=910 + seed,
+                           kv_dtype=synth.KV_BF16 if mode == "bf16" else synth.KV_E4M3,
+                           fp8_queries=mode == "e4m3-queries")
+    log(f"mla {mode} random seed={seed}: B={B} T={T} Hq={Hq} L={lens} P={case.page_size} n={n}")
+    sess, _ = session_for(case, requested_splits=n, debug=True)
+    sess.decode()
+    _check_full(case, sess, f"mla {mode} random seed={seed}")
+    _check_debug(case, sess, 1, -(-(T * Hq) // 64))
+
+
 def test_mla_fp8q_full_size_sampled():
     _need_gpu()
     case = synth.mla_decode(L=65536, kv_dtype=synth.KV_E4M3, fp8_queries=True)
