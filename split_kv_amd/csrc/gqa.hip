@@ -280,7 +280,9 @@ __global__ __launch_bounds__(256) void gqa_partial_kernel(
     const bool bump = mx > m_ref + kRescaleMargin;
     if (__any(bump)) {
       const float m_new = bump ? mx : m_ref;
-      const float alpha = fast_exp2(m_ref - m_new);   // 0 on the first visible group
+      // a row that does not move keeps alpha = 1 exactly: computing it would
+      // give exp2(-inf - -inf) = NaN for a row with nothing visible yet
+      const float alpha = bump ? fast_exp2(m_ref - m_new) : 1.f;   // 0 on the first visible group
       l_run *= alpha;
 #pragma unroll
       for (int c = 0; c < NC * 8; ++c) oacc[c] *= alpha;

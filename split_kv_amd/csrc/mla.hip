@@ -348,7 +348,9 @@ __global__ __launch_bounds__(512) void mla_partial_kernel(PartialParams p, int p
     const bool bump = mx > m_ref + kRescaleMargin;
     if (__any(bump)) {
       const float m_new = bump ? mx : m_ref;
-      const float alpha = fast_exp2(m_ref - m_new);   // 0 on the first visible tile, 1 if unmoved
+      // a row that does not move keeps alpha = 1 exactly: computing it would
+      // give exp2(-inf - -inf) = NaN for a row with nothing visible yet
+      const float alpha = bump ? fast_exp2(m_ref - m_new) : 1.f;   // 0 on the first visible tile
       l_run *= alpha;
       m_ref = m_new;
 #pragma unroll

@@ -569,6 +569,62 @@ def test_mla_fp8q_saturating_scale_strided_query_nhd_cache():
     _check_debug(case, sess, 1, 12)
 
 
+@pytest.mark.parametrize("path", ["gqa-bf16", "gqa-e4m3", "mla-bf16", "mla-e4m3", "mla-e4m3-queries"])
+def test_rows_without_visible_keys_beside_visible_ones(path):
+    # The lazy rescale moves the rows of a 16-row block whose maximum jumped
+    # and must leave the others untouched, including rows that have seen no
+    # key yet (it once computed their factor as exp2(-inf + inf) = NaN).
+    # Grouped-query: T=4 x 4 heads per block; L=305 in 19 splits leaves a
+    # last split [288, 305) whose second group (another wave) holds token
+    # 304, seen only by the last draft token, so the other rows are empty in
+    # that wave but not in the workgroup.  MLA: T=3 x 40 heads puts draft
+    # tokens 0 and 1 in one block; with L=2 and one split, token 0's rows see
+    # nothing while token 1's see a key, and single-split rows are written
+    # straight to the output.
+    _need_gpu()
+    kv = synth.KV_BF16 if path.endswith("bf16") else synth.KV_E4M3
+    if path.startswith("gqa"):
+        case = synth.make_case("mixed-visibility", B=1, T=4, Hq=16, Hkv=4, d_qk=128, d_v=128,
+                               seq_lens=[305], page_size=16, kv_dtype=kv, seed=33)
+        n, blocks, hkv = 19, 1, 4
+    else:
+        case = synth.make_case("mixed-visibility-mla", B=2, T=3, Hq=40, Hkv=1, d_qk=576, d_v=512,
+                               seq_lens=[2, 300], page_size=64, mla=True, std=0.5, seed=34, kv_dtype=kv,
+                               fp8_queries=path.endswith("queries"))
+        n, blocks, hkv = 1, 2, 1
+    log(f"{path}: rows with and without visible keys in one block, n={n}")
+    sess, _ = session_for(case, requested_splits=n, debug=True)
+    sess.decode()
+    _check_full(case, sess, f"{path} mixed visibility")
+    _check_debug(case, sess, hkv, blocks)
+
+
+@pytest.mark.parametrize("kv", [synth.KV_BF16, synth.KV_E4M3])
+@pytest.mark.parametrize("seed", range(8))
+def test_gqa_random_shapes(seed, kv):
+    # seeded draws of batch, query tokens, head grouping, head dim, lengths,
+    # page size (any multiple of 16), cache layout and split request
+    _need_gpu()
+    rng = np.random.default_rng(800 + seed)
+    B = int(rng.integers(1, 5))
+    T = int(rng.integers(1, 5))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    g = int(rng.choice([1, 2, 4, 8, 16]))
+    d = int(rng.choice([128, 256]))
+    lens = [int(x) for x in rng.integers(0, 3000, size=B)]
+    P = int(rng.choice([16, 32, 48, 64, 256]))
+    layout = str(rng.choice(["HND", "NHD"]))
+    n = int(rng.choice([0, 1, 3, 8, 40]))
+    case = synth.make_case(f"gqa-rand{seed}", B=B, T=T, Hq=g * Hkv, Hkv=Hkv, d_qk=d, d_v=d,
+                           seq_lens=lens, page_size=P, kv_dtype=kv, seed=810 + seed)
+    log(f"gqa {kv} random seed={seed}: B={B} T={T} Hq={g * Hkv} Hkv={Hkv} d={d} L={lens} P={P} "
+        f"{layout} n={n}")
+    sess, _ = session_for(case, requested_splits=n, layout=layout, debug=True)
+    sess.decode()
+    _check_full(case, sess, f"gqa {kv} random seed={seed}")
+    _check_debug(case, sess, Hkv, -(-(T * g) // 16))
+
+
 @pytest.mark.parametrize("mode", ["bf16", "e4m3", "e4m3-queries"])
 @pytest.mark.parametrize("seed", range(6))
 def test_mla_random_shapes(seed, mode):
