@@ -234,10 +234,10 @@ splitkv_status splitkv_decode_partial_fp8(const splitkv_args* args, void* stream
  * each bf16 query value is quantised to the e4m3 code of q / q_scale (fp32
  * division, saturated to +-448, nearest code, ties to even -- the encoding of
  * splitkv_append_kv) and the scores and P V run on the FP8 matrix path with
- * the softmax weights rounded to e4m3 (each to within 2^-4 of itself; the
- * weight sum adds the rounded weights).  The result approximates attention
- * over the dequantised queries, keys and values.  q_scale must be positive
- * and finite.
+ * each softmax weight entered as two e4m3 terms (hi + lo, within 2^-8 of
+ * the weight plus 2^-10; the weight sum adds the weights themselves).  The
+ * result approximates attention over the dequantised queries, keys and
+ * values.  q_scale must be positive and finite.
  */
 splitkv_status splitkv_mla_decode_partial(const splitkv_args* args, void* stream);
 
