@@ -18,7 +18,9 @@
  *     memory and keeps no per-call state: the caller owns every buffer,
  *     including the workspace (per-call buffer allocation inside attention
  *     backends was flagged as a memory hazard in "Xqa decode kernels",
- *     review comments).
+ *     review comments).  The one exception is splitkv_decode_noalloc, whose
+ *     partials live in a fixed module-scope device array that is loaded with
+ *     the library, never allocated per call.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Launches are asynchronous; device faults surface at the caller's next
  *     synchronisation.
@@ -90,6 +92,7 @@ typedef int32_t splitkv_status;
 #define SPLITKV_ROWS_PER_WG_GQA 16     /* query rows (g*T) one GQA workgroup covers */
 #define SPLITKV_ROWS_PER_WG_MLA 64     /* query rows (T*Hq) one MLA workgroup covers */
 #define SPLITKV_DEBUG_INTS 8
+#define SPLITKV_NOALLOC_SCRATCH_BYTES 67108864  /* library-owned partials of splitkv_decode_noalloc, per device */
 
 enum { SPLITKV_KV_BF16 = 0, SPLITKV_KV_E4M3 = 1 };
 enum { SPLITKV_KERNEL_GQA = 0, SPLITKV_KERNEL_MLA = 1 };
@@ -259,6 +262,24 @@ splitkv_status splitkv_combine(const splitkv_args* args, void* stream);
  * `kernel` is SPLITKV_KERNEL_GQA or SPLITKV_KERNEL_MLA.
  */
 splitkv_status splitkv_decode(const splitkv_args* args, int32_t kernel, void* stream);
+
+/*
+ * splitkv_decode_noalloc -- splitkv_decode for callers that cannot allocate
+ * device memory or hand in a workspace: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  The same kernels run; the
+ * partials go to a buffer the library owns (SPLITKV_NOALLOC_SCRATCH_BYTES =
+ * 64 MiB, one copy per device, held until the process ends) instead of
+ * args->workspace, which is ignored together with args->workspace_bytes.
+ * A plan whose partials need more (splitkv_workspace_bytes(total_slots, T,
+ * Hq, d_v) > SPLITKV_NOALLOC_SCRATCH_BYTES) fails with SPLITKV_ERR_WORKSPACE
+ * before anything is launched.  Nothing in the buffer has to start at zero:
+ * every partial the combine reads is written by the partial kernel of the
+ * same call.  Every call on one device shares that device's buffer, so calls
+ * that overlap on one device (streams without an ordering between them)
+ * race; calls ordered on one stream do not.  The call itself allocates
+ * nothing (no hipMalloc, no allocating library routine).
+ */
+splitkv_status splitkv_decode_noalloc(const splitkv_args* args, int32_t kernel, void* stream);
 
 /* Arguments of splitkv_append_kv. */
 typedef struct {

@@ -38,6 +38,7 @@ SPLITKV_MAX_SPLITS_LIMIT = 256
 SPLITKV_ROWS_PER_WG_GQA = 16
 SPLITKV_ROWS_PER_WG_MLA = 64
 SPLITKV_DEBUG_INTS = 8
+SPLITKV_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 SPLITKV_KV_BF16 = 0
 SPLITKV_KV_E4M3 = 1
@@ -121,6 +122,7 @@ def load():
             "splitkv_mla_decode_partial": (c_i32, [P(splitkv_args), c_vp]),
             "splitkv_combine": (c_i32, [P(splitkv_args), c_vp]),
             "splitkv_decode": (c_i32, [P(splitkv_args), c_i32, c_vp]),
+            "splitkv_decode_noalloc": (c_i32, [P(splitkv_args), c_i32, c_vp]),
             "splitkv_validate_block_table": (c_i32, [c_vp, c_vp, c_i32, c_i64, c_i32, c_i32]),
             "splitkv_e4m3_to_bf16": (c_i32, [c_vp, c_vp, c_i64, c_vp]),
             "splitkv_append_kv": (c_i32, [P(splitkv_append_args), c_vp]),
@@ -144,7 +146,7 @@ def load():
 
 EXPORTED = ("splitkv_plan", "splitkv_split_range", "splitkv_workspace_bytes",
             "splitkv_decode_partial", "splitkv_decode_partial_fp8", "splitkv_mla_decode_partial",
-            "splitkv_combine", "splitkv_decode", "splitkv_validate_block_table",
+            "splitkv_combine", "splitkv_decode", "splitkv_decode_noalloc", "splitkv_validate_block_table",
             "splitkv_e4m3_to_bf16", "splitkv_append_kv", "splitkv_last_error", "splitkv_version",
             "splitkv_args_size", "splitkv_plan_args_size", "splitkv_append_args_size")
 
@@ -212,6 +214,11 @@ def splitkv_combine(args: splitkv_args, stream: int = 0):
 
 def splitkv_decode(args: splitkv_args, kernel: int, stream: int = 0):
     _check("splitkv_decode", load().splitkv_decode(ctypes.byref(args), kernel, stream))
+
+
+def splitkv_decode_noalloc(args: splitkv_args, kernel: int, stream: int = 0):
+    """splitkv_decode with the partials in the library's own buffer (args.workspace is ignored)."""
+    _check("splitkv_decode_noalloc", load().splitkv_decode_noalloc(ctypes.byref(args), kernel, stream))
 
 
 def splitkv_validate_block_table(block_table, seq_lens, page_size: int, num_pages: int):

@@ -284,6 +284,33 @@ splitkv_status run_combine(const splitkv_args* a, bool skip_single, void* stream
   return SPLITKV_OK;
 }
 
+// Partials buffer of splitkv_decode_noalloc: a module-scope device array, one
+// copy per device, held until the process ends.  In host code its name only
+// stands in for the symbol; the device address comes from hipGetSymbolAddress,
+// once per device with that device current, and only that address is handed
+// to the kernels.
+static __device__ __align__(256) uint8_t scratch[SPLITKV_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+splitkv_status scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(SPLITKV_ERR_DEVICE, "hipGetDevice failed");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    const hipError_t err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess || !p)
+      return fail(SPLITKV_ERR_DEVICE, "hipGetSymbolAddress of the partials buffer failed on device %d: %s",
+                  dev, hipGetErrorString(err));
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return SPLITKV_OK;
+}
+
 }  // namespace
 }  // namespace splitkv
 
@@ -332,6 +359,27 @@ splitkv_status splitkv_decode(const splitkv_args* args, int32_t kernel, void* st
   splitkv_status st = run_partial(args, kind, true, stream, "splitkv_decode");
   if (st != SPLITKV_OK || args->total_slots == args->B) return st;
   return run_combine(args, true, stream, "splitkv_decode");
+}
+
+splitkv_status splitkv_decode_noalloc(const splitkv_args* args, int32_t kernel, void* stream) {
+  const char* fn = "splitkv_decode_noalloc";
+  if (!args) return fail(SPLITKV_ERR_INVALID_ARG, "%s: null args", fn);
+  // size check first: a plan that does not fit is refused before any device call
+  const size_t need = splitkv_workspace_bytes(args->total_slots, args->T, args->Hq, args->d_v);
+  if (need > size_t(SPLITKV_NOALLOC_SCRATCH_BYTES))
+    return fail(SPLITKV_ERR_WORKSPACE,
+                "%s: the plan's partials need %zu bytes; the library buffer holds %d "
+                "(use fewer splits, or splitkv_decode with a workspace)",
+                fn, need, SPLITKV_NOALLOC_SCRATCH_BYTES);
+  splitkv_status st = check_device(nullptr);
+  if (st != SPLITKV_OK) return st;
+  void* buf = nullptr;
+  st = scratch_address(&buf);
+  if (st != SPLITKV_OK) return st;
+  splitkv_args a = *args;
+  a.workspace = static_cast<float*>(buf);
+  a.workspace_bytes = size_t(SPLITKV_NOALLOC_SCRATCH_BYTES);
+  return splitkv_decode(&a, kernel, stream);
 }
 
 splitkv_status splitkv_e4m3_to_bf16(const uint8_t* in, uint16_t* out, int64_t n, void* stream) {

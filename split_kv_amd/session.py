@@ -14,7 +14,7 @@ import numpy as np
 from . import (SPLITKV_KERNEL_GQA, SPLITKV_KERNEL_MLA, SPLITKV_KV_BF16, SPLITKV_KV_E4M3,
                SPLITKV_MAX_SPLITS_LIMIT, SPLITKV_OUT_BF16, SPLITKV_OUT_F32, SPLITKV_Q_BF16, SPLITKV_Q_E4M3,
                SPLITKV_ROWS_PER_WG_GQA, SPLITKV_ROWS_PER_WG_MLA,
-               splitkv_args, splitkv_combine, splitkv_decode, splitkv_decode_partial,
+               splitkv_args, splitkv_combine, splitkv_decode, splitkv_decode_noalloc, splitkv_decode_partial,
                splitkv_decode_partial_fp8, splitkv_mla_decode_partial, splitkv_plan,
                splitkv_plan_args, splitkv_workspace_bytes)
 
@@ -143,6 +143,11 @@ class DecodeSession:
     def decode(self):
         """The whole decode step: partial kernel, then the combine where needed."""
         splitkv_decode(self.args, self.kernel, self._stream())
+        return self.out, self.lse
+
+    def decode_noalloc(self):
+        """The whole decode step with the partials in the library's own buffer."""
+        splitkv_decode_noalloc(self.args, self.kernel, self._stream())
         return self.out, self.lse
 
     def partial(self):

@@ -272,3 +272,15 @@ def test_append_argument_errors_without_device(over, code):
 def test_version_string():
     _lib()
     assert sk.splitkv_version()
+
+
+def test_noalloc_refuses_an_oversized_plan_without_a_device():
+    # 256 MLA slots of 768 rows need ~404 MB of partials, more than the
+    # library's 64 MiB buffer: refused on the host, before any device call
+    lib = _lib()
+    a = sk.splitkv_args()
+    a.B, a.T, a.Hq, a.Hkv, a.d_qk, a.d_v, a.total_slots = 1, 6, 128, 1, 576, 512, 256
+    assert sk.splitkv_workspace_bytes(256, 6, 128, 512) > sk.SPLITKV_NOALLOC_SCRATCH_BYTES
+    st = lib.splitkv_decode_noalloc(ctypes.byref(a), sk.SPLITKV_KERNEL_MLA, None)
+    assert st == sk.SPLITKV_ERR_WORKSPACE
+    assert "library buffer" in sk.splitkv_last_error()
