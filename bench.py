@@ -1,21 +1,31 @@
 #!/usr/bin/env python3
 """Split-KV decode-attention benchmark on one MI355X.
 
-Workload (default): few-KV-head long-context decode, B=1, one query token,
-Hq=16, Hkv=2, D=256, L=5900 cached tokens, bf16, paged KV with page size 16
-and a seeded random page permutation.  One step is one pass of the whole hot
-path through the C ABI (splitkv_decode: the partial kernel, then the
+Workload of the bench line: few-KV-head long-context decode, B=1, one query
+token, Hq=16, Hkv=2, D=256, L=5900 cached tokens, bf16, paged KV with page
+size 16 and a seeded random page permutation.  One step is one pass of the
+whole hot path through the C ABI (splitkv_decode: the partial kernel, then the
 log-sum-exp combine when a sequence has more than one split); the host plan is
 made once per split count, outside the timed region, and its cost is reported
 separately.
 
-Cold cache: the page pool is replicated until the copies total >= 1 GiB and
-step k reads copy k mod R through a block table offset by copy, so every step
-streams its KV from HBM and not from L2 or MALL.  Outputs are bit-identical
-across copies.
+Cold cache: the page pool is replicated until the copies total >= 1 GiB, and
+every launch the bench makes -- eager or captured, warm-up or timed -- takes
+the next copy of one rotation over all of them.  A copy is therefore read
+again only after every other copy (>= 1 GiB, four times the 256 MB MALL) has
+been streamed, whatever --steps is.  Outputs are bit-identical across copies.
 
-Prints ONE JSON line: metric / value (KV GB/s at the auto plan) / ms_per_step
-/ the num_splits sweep / roofline of the dominant kernel / cpu_baseline.
+Timing: K steps are captured in a HIP graph and replayed once untimed; then
+five further graphs of K steps (each on the next K copies of the rotation) are
+replayed between two events on their launch stream, and the median of the
+five is reported.  The partial kernel alone is timed the same way for the
+roofline object.
+
+Prints ONE JSON line: metric / value (KV GB/s at the auto plan) /
+ms_per_step / the num_splits sweep / roofline of the dominant kernel / the
+floor (empty-kernel and plain-stream-read calibration) / cpu_baseline, plus an
+`extra` list with the auto plan, sweep, roofline and monotonic check of every
+other workload.
 """
 from __future__ import annotations
 
@@ -23,6 +33,7 @@ import argparse
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -33,10 +44,23 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 MFMA_FP8_PEAK_TFLOPS = 5000.0
 METRIC = "decode-attention µs/step and KV GB/s (% of HBM peak) vs num_splits"
+BATCHES = 5
+HEADLINE_SWEEP = "1,2,3,4,6,8,12,16,24,32,48,64,96,128,192,256"
 
-
-def parse_defaults():
-    return {"sweep": "1,2,3,4,6,8,12,16,24,32,48,64,96,128,192,256"}
+# The other workloads, each carried in the default run's `extra` list: (name, L, split counts;
+# 0 = the auto plan).
+EXTRA = [
+    ("tiny-gqa", 256, [0, 1, 2, 4]),
+    ("few-kv-long", 260, [0, 1, 2, 4, 8, 16, 32, 64]),
+    ("fp8-batched", None, [0, 1, 2, 4, 8, 16, 32]),
+    ("mla", 2048, [0, 1, 4, 8, 16]),
+    ("mla-fp8", 2048, [0, 1, 4, 8, 16]),
+    ("mla-fp8q", 2048, [0, 1, 4, 8, 16]),
+    ("mla", 65536, [0, 1, 4, 8]),
+    ("mla-fp8", 65536, [0, 1, 4, 8]),
+    ("mla-fp8q", 65536, [0, 1, 4, 8]),
+    ("ragged", None, [0, 1, 4, 16, 64]),
+]
 
 
 def parse():
@@ -49,11 +73,14 @@ def parse():
                              "tiny-gqa"],
                     help="few-kv-long is the headline; the others are extra measurements")
     ap.add_argument("--L", type=int, default=None, help="sequence length (few-kv-long, mla, mla-fp8, mla-fp8q, tiny-gqa)")
-    ap.add_argument("--sweep", type=str, default="1,2,3,4,6,8,12,16,24,32,48,64,96,128,192,256",
-                    help="comma-separated num_splits to sweep ('' to skip); the workload's own "
+    ap.add_argument("--sweep", type=str, default=None,
+                    help="comma-separated num_splits to sweep ('' to skip); the headline's own "
                          "sweep is 1..64, larger counts are extra points")
     ap.add_argument("--only", type=int, default=None,
                     help="time one split count only (0 = auto); for profiler runs")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
+    ap.add_argument("--extra-steps", type=int, default=50,
+                    help="steps per timed batch of the other workloads (at most --steps)")
     ap.add_argument("--warm-cache", action="store_true", help="reuse one page pool copy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -100,122 +127,102 @@ def describe(case, name):
             "fp32 out")
 
 
-def cold_copies(case, device, warm):
-    """Replicate the page pool R times (>= 1 GiB total) with per-copy block tables."""
-    import numpy as np
+class Pool:
+    """The workload's page pool replicated R times (>= 1 GiB in total), with one
+    rotation shared by every launch: take(n) hands out the next n copies."""
+
+    def __init__(self, case, device, warm):
+        import numpy as np
+        import torch
+        import synth
+        t = synth.to_torch(case, device)
+        pool = case.k_cache.nbytes + (case.v_cache.nbytes if case.v_cache is not None else 0)
+        R = 1 if warm else max(1, math.ceil((1 << 30) / pool))
+        self.q = t["q"]
+        self.k = t["k_cache"].repeat(R, 1, 1, 1) if R > 1 else t["k_cache"]
+        v = t["v_cache"]
+        self.v = v.repeat(R, 1, 1, 1) if (v is not None and R > 1) else v
+        bt = case.block_table
+        valid = bt != synth.INT32_MAX
+        tables = []
+        for r in range(R):
+            b = bt.copy()
+            b[valid] += r * case.num_pages
+            tables.append(b)
+        self.bts = torch.from_numpy(np.stack(tables)).to(device)
+        self.R = R
+        self.pool_bytes = pool
+        self.i = 0
+
+    def take(self, n):
+        idx = [(self.i + j) % self.R for j in range(n)]
+        self.i = (self.i + n) % self.R
+        return idx
+
+
+def _events():
     import torch
-    import synth
-    t = synth.to_torch(case, device)
-    pool = case.k_cache.nbytes + (case.v_cache.nbytes if case.v_cache is not None else 0)
-    R = 1 if warm else max(1, math.ceil((1 << 30) / pool))
-    k = t["k_cache"].repeat(R, 1, 1, 1) if R > 1 else t["k_cache"]
-    v = t["v_cache"]
-    if v is not None and R > 1:
-        v = v.repeat(R, 1, 1, 1)
-    bt = case.block_table
-    valid = bt != synth.INT32_MAX
-    tables = []
-    for r in range(R):
-        b = bt.copy()
-        b[valid] += r * case.num_pages
-        tables.append(b)
-    bts = torch.from_numpy(np.stack(tables)).to(device)
-    return t["q"], k, v, bts, R
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
 
-def time_steps(sess, bts, R, steps, warmup, stream):
+def capture(sess, pool, n, fn, stream):
+    """A HIP graph of n launches of fn, launch i reading the next copy of the rotation."""
     import torch
-    for i in range(warmup):
-        sess.set_block_table(bts[i % R])
-        sess.decode()
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for i in range(steps):
-        sess.set_block_table(bts[(warmup + i) % R])
-        sess.decode()
-    end.record(stream)
-    torch.cuda.synchronize()
-    return start.elapsed_time(end) * 1e3 / steps      # us per step
-
-
-_SIDE = None
-
-
-def time_steps_graph(sess, bts, R, steps, warmup, check=True):
-    """Exactly `steps` decode steps replayed from one captured HIP graph.
-
-    This is how a serving engine runs decode steps: the whole step sequence is
-    captured once and replayed, so no host launch sits between kernels.  Step
-    i of the graph reads page-pool copy i mod R.  The graph is replayed once
-    untimed, then once timed.  With `check`, its output must equal the eager
-    step's bit for bit.  Returns us per step.
-    """
-    import torch
-    global _SIDE
-    if _SIDE is None:
-        _SIDE = torch.cuda.Stream()     # one warm-up stream for every capture
-    side = _SIDE
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        for i in range(max(1, warmup)):
-            sess.set_block_table(bts[i % R])
-            sess.decode()
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    ref = sess.out.clone()
     g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for i in range(steps):
-            sess.set_block_table(bts[i % R])
-            sess.decode()
-    g.replay()
-    torch.cuda.synchronize()
-    if check:
-        assert torch.equal(sess.out, ref), "graph replay output differs from the eager step"
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    g.replay()
-    end.record()
-    torch.cuda.synchronize()
-    if check:
-        assert torch.equal(sess.out, ref), "graph replay output differs from the eager step"
-    del g
-    return start.elapsed_time(end) * 1e3 / steps
+    with torch.cuda.graph(g, stream=stream):
+        for c in pool.take(n):
+            sess.set_block_table(pool.bts[c])
+            fn()
+    return g
 
 
-def time_partial_kernel(sess, bts, R, steps, stream):
-    """Average duration of the dominant kernel, the partial kernel.
-
-    `steps` launches (launch i reads page-pool copy i mod R) are captured in
-    one HIP graph on `stream` and replayed once untimed, then once between two
-    events recorded on that same stream; the result is the replay time divided
-    by `steps`.  Back-to-back graph nodes leave only the dispatch gap between
-    kernels, so this tracks the kernel-trace duration.
-    """
+def timed_graphs(sess, pool, fn, steps, stream, check=None):
+    """us per launch of fn: one untimed replay, then the median of BATCHES
+    replays of freshly captured graphs, each between two events recorded on
+    the stream the graph runs on (every graph reads the next `steps` copies of
+    the rotation)."""
     import torch
-    launch = sess.partial
     with torch.cuda.stream(stream):
-        for i in range(3):
-            sess.set_block_table(bts[i % R])
-            launch()
+        for c in pool.take(3):                # eager warm-up on the launch stream
+            sess.set_block_table(pool.bts[c])
+            fn()
     torch.cuda.synchronize()
-    cap = torch.cuda.Stream()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=cap):
-        for i in range(steps):
-            sess.set_block_table(bts[i % R])
-            launch()
-    with torch.cuda.stream(cap):
+    g = capture(sess, pool, steps, fn, stream)
+    with torch.cuda.stream(stream):
         g.replay()
-        torch.cuda.synchronize()
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        start.record(cap)
-        g.replay()
-        end.record(cap)
     torch.cuda.synchronize()
     del g
-    return start.elapsed_time(end) * 1e3 / steps
+    if check:
+        check()
+    times = []
+    for _ in range(BATCHES):
+        g = capture(sess, pool, steps, fn, stream)
+        e0, e1 = _events()
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3 / steps)
+        del g
+        if check:
+            check()
+    return statistics.median(times), times
+
+
+def time_eager(sess, pool, steps, stream):
+    """us per step with one host launch per kernel (no graph)."""
+    import torch
+    torch.cuda.synchronize()
+    e0, e1 = _events()
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for c in pool.take(steps):
+            sess.set_block_table(pool.bts[c])
+            sess.decode()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / steps
 
 
 COUNTERS = os.path.join(ROOT, "profiles", "gqa_partial_fewkv_L5900_counters.md")
@@ -275,40 +282,196 @@ def monotonic(sweep, band=1.03):
             "worst_request": worst["num_splits_requested"]}
 
 
-def cpu_baseline(case, seconds):
-    """Time the fp64 oracle (as it stands) on the same workload, repeated ~`seconds`."""
-    import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        cores = 1
+def partial_kernel_name(case):
+    if case.mla:
+        if case.q_scale:
+            return "mla_fp8q_partial_kernel"
+        return "mla_partial_kernel<%s>" % ("e4m3" if case.kv_dtype == "e4m3" else "bf16")
+    return "gqa_partial_kernel<%d,%s>" % (case.d_qk, "e4m3" if case.kv_dtype == "e4m3" else "bf16")
 
-    def timed(budget):
+
+def partial_grid(case, sess):
+    """Workgroups of one partial-kernel launch."""
+    if case.mla:
+        rows = case.T * case.Hq
+        return sess.total_slots * -(-rows // 64)
+    return sess.total_slots * case.Hkv * -(-(case.g * case.T) // 16)
+
+
+def roofline(case, part_us):
+    if case.mla:
+        flops = 2 * case.T * case.Hq * (case.d_qk + case.d_v) * int(case.seq_lens.sum())
+        # e4m3 queries put the products on the FP8 matrix path: its own peak
+        peak = MFMA_FP8_PEAK_TFLOPS if case.q_scale else MFMA_BF16_PEAK_TFLOPS
+        return {"bound": "mfma", "kernel": partial_kernel_name(case),
+                "achieved": round(flops / part_us / 1e6, 1), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(flops / part_us / 1e6 / peak, 4),
+                "traffic": None, "kernel_us": round(part_us, 3), "flops_per_launch": flops}
+    kv = case.kv_bytes()
+    achieved = kv / part_us / 1e3
+    return {"bound": "hbm", "kernel": partial_kernel_name(case), "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None, "kernel_us": round(part_us, 3), "bytes_per_launch": kv}
+
+
+def measure(case, pool, counts, steps, stream, eager=True, log_prefix=""):
+    """Sweep the split counts: us/step from graph replays (median of BATCHES),
+    plus the partial kernel alone at the first count.  Returns (sweep, head)."""
+    import torch
+    from split_kv_amd.session import DecodeSession
+    kv_bytes = case.kv_bytes()
+
+    def session(n):
+        t0 = time.perf_counter()
+        s = DecodeSession(q=pool.q, k_cache=pool.k, v_cache=pool.v, block_table=pool.bts[0],
+                          seq_lens=case.seq_lens, scale=case.scale, k_scale=case.k_scale,
+                          v_scale=case.v_scale, mla=case.mla, requested_splits=n, max_splits=256,
+                          out_fp32=case.out_fp32, q_scale=case.q_scale)
+        return s, (time.perf_counter() - t0) * 1e6
+
+    sweep, head = [], None
+    for n in counts:
+        sess, plan_us = session(n)
+        eager_us = time_eager(sess, pool, steps, stream) if eager else None
+        ref = {}
+
+        def check():
+            # every replayed step writes the same bits as the first eager step
+            if not ref:
+                ref["out"] = sess.out.clone()
+            assert torch.equal(sess.out, ref["out"]), "graph replay output differs from the eager step"
+
+        sess.set_block_table(pool.bts[pool.take(1)[0]])
+        with torch.cuda.stream(stream):
+            sess.decode()
+        torch.cuda.synchronize()
+        check()
+        us, batches = timed_graphs(sess, pool, sess.decode, steps, stream, check=check)
+        rec = {"num_splits_requested": n, "num_splits": int(sess.num_splits_host.max()),
+               "total_slots": sess.total_slots,
+               "us_per_step": round(us, 3), "kv_GBps": round(kv_bytes / us / 1e3, 1),
+               "pct_hbm_peak": round(100 * kv_bytes / us / 1e3 / HBM_PEAK_GBS, 2),
+               "batches_us": [round(x, 3) for x in batches]}
+        if eager_us is not None:
+            rec["eager_us_per_step"] = round(eager_us, 3)
+        if n == counts[0]:
+            part_us, part_batches = timed_graphs(sess, pool, sess.partial, steps, stream)
+            head = dict(rec, plan_host_us=round(plan_us, 1), partial_kernel_us=round(part_us, 3),
+                        partial_batches_us=[round(x, 3) for x in part_batches],
+                        partial_workgroups=partial_grid(case, sess),
+                        num_splits_host=sess.num_splits_host.copy())
+        sweep.append(rec)
+        print(f"# {log_prefix}n={n} -> {rec}", file=sys.stderr, flush=True)
+        del sess
+    return sweep, head
+
+
+def floor_measurement(kv_bytes, grids, steps, stream):
+    """Floors of a decode step on this GPU, measured with the library's
+    calibration kernels from captured graphs: one empty kernel per node, a
+    step of two empty kernels (the partial + combine shape), and a plain
+    streaming read of the step's KV bytes with the given workgroup counts
+    (each launch on the next chunk of a 1 GiB rotation, so from HBM), plus a
+    1 GiB read with 4096 workgroups (the stream peak)."""
+    import torch
+    import split_kv_amd as sk
+    dev = torch.device("cuda:0")
+    gib = 1 << 30
+    buf = torch.ones(gib // 4, dtype=torch.float32, device=dev)
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device=dev)
+    base = buf.data_ptr()
+    chunk = -(-kv_bytes // (1 << 18)) * (1 << 18)
+    nchunks = max(1, (gib - kv_bytes) // chunk)
+    rot = {"i": 0}
+
+    def graph_time(body, n_launch, reps=BATCHES):
+        times = []
+        for r in range(reps + 1):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for _ in range(n_launch):
+                    body()
+            e0, e1 = _events()
+            with torch.cuda.stream(stream):
+                e0.record(stream)
+                g.replay()
+                e1.record(stream)
+            torch.cuda.synchronize()
+            if r:
+                times.append(e0.elapsed_time(e1) * 1e3 / n_launch)
+            del g
+        return statistics.median(times)
+
+    def empty():
+        sk.splitkv_calib_empty(torch.cuda.current_stream().cuda_stream)
+
+    def two_empty():
+        empty()
+        empty()
+
+    out = {"empty_kernel_graph_us": round(graph_time(empty, steps), 3),
+           "empty_two_kernel_step_us": round(graph_time(two_empty, steps), 3)}
+    reads = []
+    for wgs in grids:
+        def read(wgs=wgs):
+            off = (rot["i"] % nchunks) * chunk
+            rot["i"] += 1
+            sk.splitkv_calib_stream_read(base + off, kv_bytes, wgs, sink.data_ptr(),
+                                         torch.cuda.current_stream().cuda_stream)
+        us = graph_time(read, steps)
+        reads.append({"workgroups": wgs, "bytes": kv_bytes, "us": round(us, 3),
+                      "GBps": round(kv_bytes / us / 1e3, 1)})
+
+    def read_all():
+        sk.splitkv_calib_stream_read(base, gib, 4096, sink.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    us = graph_time(read_all, 4)
+    reads.append({"workgroups": 4096, "bytes": gib, "us": round(us, 3), "GBps": round(gib / us / 1e3, 1)})
+    out["stream_read"] = reads
+    del buf, sink
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(case, seconds):
+    """Time the fp64 oracle (as it stands) on the same workload, repeated ~`seconds`,
+    with its BLAS held to one thread (its per-row loops use one core either way)."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):
         t0 = time.perf_counter()
         n = 0
         while True:
             oracle.attend(case)
             n += 1
             el = time.perf_counter() - t0
-            if el >= budget:
-                return n, el
-
-    n, el = timed(seconds)
+            if el >= seconds:
+                break
     per_step = el / n
-    rec = {"value": case.kv_bytes() / per_step / 1e9, "unit": "GB/s", "cores": int(cores),
-           "kind": "oracle",
-           "sample": f"{n} full oracle steps of the bench workload (fp64 numpy, {el:.1f} s); "
-                     f"{per_step * 1e6:.0f} us per step"}
-    # the same oracle with its BLAS held to one thread, half the time budget
-    try:
-        from threadpoolctl import threadpool_limits
-        with threadpool_limits(limits=1):
-            n1, el1 = timed(seconds / 2)
-        rec["single_thread"] = {"value": case.kv_bytes() / (el1 / n1) / 1e9, "unit": "GB/s",
-                                "cores": 1, "sample": f"{n1} steps in {el1:.1f} s"}
-    except Exception as e:                    # threadpoolctl missing: report the one timing
-        rec["single_thread"] = f"not measured: {e}"
+    return {"value": round(case.kv_bytes() / per_step / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{n} full oracle steps of the bench workload (fp64 numpy, one thread, "
+                      f"{el:.1f} s); {per_step * 1e6:.0f} us per step"}
+
+
+def extra_record(name, L, counts, steps, stream, dev):
+    import torch
+    case = make_workload(name, L)
+    pool = Pool(case, dev, False)
+    sweep, head = measure(case, pool, counts, steps, stream, eager=False, log_prefix=f"{name} L={L} ")
+    roof = roofline(case, head["partial_kernel_us"])
+    rec = {"workload": describe(case, name),
+           "kv_bytes_per_step": case.kv_bytes(),
+           "cold_copies": pool.R,
+           "auto": {"num_splits": head["num_splits"], "total_slots": head["total_slots"],
+                    "us_per_step": head["us_per_step"], "kv_GBps": head["kv_GBps"],
+                    "pct_hbm_peak": head["pct_hbm_peak"], "plan_host_us": head["plan_host_us"],
+                    **step_bytes(case, head["num_splits_host"])},
+           "sweep": [{"n_req": r["num_splits_requested"], "n": r["num_splits"], "slots": r["total_slots"],
+                      "us": r["us_per_step"], "GBps": r["kv_GBps"]} for r in sweep],
+           "monotonic": monotonic(sweep),
+           "roofline": roof}
+    del pool
+    torch.cuda.empty_cache()
     return rec
 
 
@@ -383,7 +546,7 @@ def append_measurement(steps, warmup):
                 sk.splitkv_append_kv(a, torch.cuda.current_stream().cuda_stream)
         g.replay()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0, e1 = _events()
         e0.record()
         g.replay()
         e1.record()
@@ -415,88 +578,46 @@ def main():
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "multi-GPU sharding is described in DESIGN.md, not run.", file=sys.stderr)
         sys.exit(2)
-    import numpy as np
     import torch
-    import synth
     import split_kv_amd
-    from split_kv_amd.session import DecodeSession
 
     split_kv_amd.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    stream = torch.cuda.current_stream()
+    stream = torch.cuda.Stream()          # every timed launch and its events live on this stream
     case = make_workload(args.workload, args.L)
-    headline = args.workload == "few-kv-long"
-    q, k, v, bts, R = cold_copies(case, dev, args.warm_cache)
+    headline = args.workload == "few-kv-long" and args.L is None
+    pool = Pool(case, dev, args.warm_cache)
     kv_bytes = case.kv_bytes()
-
-    def session(n):
-        t0 = time.perf_counter()
-        s = DecodeSession(q=q, k_cache=k, v_cache=v, block_table=bts[0], seq_lens=case.seq_lens,
-                          scale=case.scale, k_scale=case.k_scale, v_scale=case.v_scale,
-                          mla=case.mla, requested_splits=n, max_splits=256,
-                          out_fp32=case.out_fp32, q_scale=case.q_scale)
-        return s, (time.perf_counter() - t0) * 1e6
 
     if args.only is not None:
         counts = [args.only]
-    elif not headline and args.sweep == parse_defaults()["sweep"]:
-        counts = [0, 1, 4, 8, 16]
-    else:
+    elif args.sweep is not None:
         counts = [0] + [int(x) for x in args.sweep.split(",") if x.strip()]
-    # Warm-up: about two seconds of eager steps of the first configuration,
-    # then one rehearsal of the whole measurement of that configuration whose
-    # results are discarded (the first captured-graph timing of a process
-    # reads 1-8% slow; every later timing of the same plan agrees).
-    sess, _ = session(counts[0])
-    t_end = time.perf_counter() + 2.0
-    while time.perf_counter() < t_end:
-        time_steps(sess, bts, R, 20, 0, stream)
-    time_steps(sess, bts, R, args.steps, args.warmup, stream)
-    time_steps_graph(sess, bts, R, args.steps, args.warmup)
-    time_partial_kernel(sess, bts, R, args.steps, stream)
-    del sess
-    sweep = []
-    head = None
-    for n in counts:
-        sess, plan_us = session(n)
-        eager_us = time_steps(sess, bts, R, args.steps, args.warmup, stream)
-        us = time_steps_graph(sess, bts, R, args.steps, args.warmup)
-        rec = {"num_splits_requested": n, "num_splits": int(sess.num_splits_host.max()),
-               "total_slots": sess.total_slots,
-               "us_per_step": round(us, 3), "kv_GBps": round(kv_bytes / us / 1e3, 1),
-               "pct_hbm_peak": round(100 * kv_bytes / us / 1e3 / HBM_PEAK_GBS, 2),
-               "eager_us_per_step": round(eager_us, 3),
-               "eager_kv_GBps": round(kv_bytes / eager_us / 1e3, 1)}
-        if n == counts[0]:
-            part_us = time_partial_kernel(sess, bts, R, args.steps, stream)
-            head = dict(rec, plan_host_us=round(plan_us, 1), partial_kernel_us=round(part_us, 3),
-                        sess=sess)
-        sweep.append(rec)
-        print(f"# n={n} -> {rec}", file=sys.stderr, flush=True)
+    elif args.workload == "few-kv-long":
+        counts = [0] + [int(x) for x in HEADLINE_SWEEP.split(",")]
+    else:
+        counts = [0, 1, 4, 8, 16]
+    # Warm-up: W eager steps and one discarded rehearsal of the first
+    # configuration's measurement (the first captured-graph timing of a
+    # process reads a few percent slow).
+    from split_kv_amd.session import DecodeSession
+    s0 = DecodeSession(q=pool.q, k_cache=pool.k, v_cache=pool.v, block_table=pool.bts[0],
+                       seq_lens=case.seq_lens, scale=case.scale, k_scale=case.k_scale,
+                       v_scale=case.v_scale, mla=case.mla, requested_splits=counts[0], max_splits=256,
+                       out_fp32=case.out_fp32, q_scale=case.q_scale)
+    time_eager(s0, pool, max(1, args.warmup), stream)
+    timed_graphs(s0, pool, s0.decode, args.steps, stream)
+    del s0
+    sweep, head = measure(case, pool, counts, args.steps, stream)
 
     us = head["us_per_step"]
-    part_us = head["partial_kernel_us"]
-    if case.mla:
-        flops = 2 * case.T * case.Hq * (case.d_qk + case.d_v) * int(case.seq_lens.sum())
-        # e4m3 queries put the products on the FP8 matrix path: its own peak
-        peak = MFMA_FP8_PEAK_TFLOPS if case.q_scale else MFMA_BF16_PEAK_TFLOPS
-        roof = {"bound": "mfma",
-                "kernel": "mla_fp8q_partial_kernel" if case.q_scale else "mla_partial_kernel",
-                "achieved": round(flops / part_us / 1e6, 1), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(flops / part_us / 1e6 / peak, 4),
-                "traffic": None, "kernel_us": part_us, "flops_per_launch": flops}
-    else:
-        kname = ("gqa_partial_kernel<%d,%s>" % (case.d_qk, "e4m3" if case.kv_dtype == "e4m3" else "bf16"))
-        achieved = kv_bytes / part_us / 1e3
-        roof = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel_us": part_us, "bytes_per_launch": kv_bytes}
-        # counters were taken for the headline workload at the auto plan
-        if headline and head["num_splits_requested"] == 0 and not args.warm_cache and args.L is None:
-            traffic, detail = measured_traffic()
-            roof["traffic"] = traffic
-            roof["traffic_detail"] = detail
+    roof = roofline(case, head["partial_kernel_us"])
+    if headline and head["num_splits_requested"] == 0 and not args.warm_cache:
+        traffic, detail = measured_traffic()
+        roof["traffic"] = traffic
+        roof["traffic_detail"] = detail
+    timed_bytes = args.steps * kv_bytes
     line = {
         "metric": METRIC,
         "value": head["kv_GBps"],
@@ -507,29 +628,55 @@ def main():
         "ms_per_step": round(us / 1e3, 6),
         "us_per_step": us,
         "pct_hbm_peak": head["pct_hbm_peak"],
-        "timing": f"{args.steps} steps replayed from one captured HIP graph (step i reads "
-                  f"page-pool copy i mod {R}), events around the replay, after ~2 s of warm-up "
-                  f"steps and one discarded rehearsal of the first configuration's measurement; "
-                  f"eager (one host launch per kernel): {head['eager_us_per_step']} us/step",
+        "timing": f"median of {BATCHES} timed batches; each batch is {args.steps} steps replayed "
+                  f"from one freshly captured HIP graph between two events on its launch stream; "
+                  f"every launch of the run reads the next page-pool copy of one rotation over "
+                  f"{pool.R} copies, so a copy is re-read only after >= 1 GiB of other copies; "
+                  f"batches: {head['batches_us']} us/step; eager (one host launch per kernel): "
+                  f"{head['eager_us_per_step']} us/step",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": ("e4m3" if case.q_scale else "e4m3-kv/bf16") if case.kv_dtype == "e4m3" else "bf16",
         "data": "synthetic",
         "config": {"workload": f"{describe(case, args.workload)}, "
-                               f"{'warm' if args.warm_cache else 'cold'} cache ({R} pool copies)",
+                               f"{'warm' if args.warm_cache else 'cold'} cache ({pool.R} pool copies)",
                    "num_splits": head["num_splits"],
                    "num_splits_requested": head["num_splits_requested"],
                    "step": "partial kernel, then combine kernel (skipped when every sequence has one split)",
                    "kv_bytes_per_step": kv_bytes,
-                   **step_bytes(case, head["sess"].num_splits_host),
+                   "timed_batch_kv_bytes": timed_bytes,
+                   "pool_copy_bytes": pool.pool_bytes,
+                   **step_bytes(case, head["num_splits_host"]),
                    "plan_host_us": head["plan_host_us"]},
         "sweep": sweep,
         "monotonic": monotonic(sweep),
         "roofline": roof,
     }
+    if not args.no_extra or headline:
+        fl = floor_measurement(kv_bytes, sorted({head["partial_workgroups"], 256, 1024}), args.steps, stream)
+        same = [r for r in fl["stream_read"] if r["workgroups"] == head["partial_workgroups"]][0]
+        peak = fl["stream_read"][-1]
+        fl["partial_pct_of_stream_same_grid"] = round(100 * roof["achieved"] / same["GBps"], 1) \
+            if roof["unit"] == "GB/s" else None
+        fl["step_pct_of_stream_peak"] = round(100 * head["kv_GBps"] / peak["GBps"], 1)
+        fl["partial_workgroups"] = head["partial_workgroups"]
+        line["floor"] = fl
     if not headline:
-        line["note"] = "extra measurement; the bench line is the few-kv-long workload"
+        line["note"] = "extra measurement; the bench line is the few-kv-long workload at L=5900"
+    if headline and not args.no_extra and args.only is None:
+        steps_x = max(1, min(args.steps, args.extra_steps))
+        extra = []
+        del pool
+        torch.cuda.empty_cache()
+        for name, L, cnts in EXTRA:
+            t0 = time.perf_counter()
+            rec = extra_record(name, L, cnts, steps_x, stream, dev)
+            rec["steps_per_batch"] = steps_x
+            extra.append(rec)
+            print(f"# extra {name} L={L}: auto {rec['auto']['us_per_step']} us/step "
+                  f"({time.perf_counter() - t0:.1f} s)", file=sys.stderr, flush=True)
+        line["extra"] = extra
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -334,6 +334,27 @@ splitkv_status splitkv_validate_block_table(const int32_t* block_table_host,
  */
 splitkv_status splitkv_e4m3_to_bf16(const uint8_t* in, uint16_t* out, int64_t n, void* stream);
 
+/*
+ * Measurement helpers (the benchmark's floors).  What a decode kernel reaches
+ * is judged against what a plain read-only kernel of the same grid reaches
+ * and against the cost of a kernel that does nothing ("vLLM 0.30.0 FA4 SplitKV
+ * Bug ...", section "The kernel profile isolates one operation": the same
+ * grid, thread count and shared memory separate launch and occupancy effects
+ * from useful work).
+ *
+ * splitkv_calib_empty -- launch one empty kernel (one wave) on `stream`.
+ *
+ * splitkv_calib_stream_read -- read `bytes` (a multiple of 16) of device
+ * memory at `src` (16-byte aligned) with `workgroups` workgroups of 256
+ * threads, each reading one contiguous share with 16-byte loads, thirty-two
+ * in flight per thread; workgroup w stores the XOR of what it read to sink[w]
+ * (`sink` holds `workgroups` uint32 values).  Bad arguments give
+ * SPLITKV_ERR_INVALID_ARG.
+ */
+splitkv_status splitkv_calib_empty(void* stream);
+splitkv_status splitkv_calib_stream_read(const void* src, size_t bytes, int32_t workgroups, uint32_t* sink,
+                                         void* stream);
+
 const char* splitkv_last_error(void);   /* thread-local message of the last failure */
 const char* splitkv_version(void);      /* source revision the library was built from */
 size_t splitkv_args_size(void);         /* sizeof(splitkv_args), for binding checks */

@@ -127,6 +127,8 @@ def load():
             "splitkv_e4m3_to_bf16": (c_i32, [c_vp, c_vp, c_i64, c_vp]),
             "splitkv_append_kv": (c_i32, [P(splitkv_append_args), c_vp]),
             "splitkv_append_args_size": (c_sz, []),
+            "splitkv_calib_empty": (c_i32, [c_vp]),
+            "splitkv_calib_stream_read": (c_i32, [c_vp, c_sz, c_i32, c_vp, c_vp]),
             "splitkv_last_error": (ctypes.c_char_p, []),
             "splitkv_version": (ctypes.c_char_p, []),
             "splitkv_args_size": (c_sz, []),
@@ -148,7 +150,8 @@ EXPORTED = ("splitkv_plan", "splitkv_split_range", "splitkv_workspace_bytes",
             "splitkv_decode_partial", "splitkv_decode_partial_fp8", "splitkv_mla_decode_partial",
             "splitkv_combine", "splitkv_decode", "splitkv_decode_noalloc", "splitkv_validate_block_table",
             "splitkv_e4m3_to_bf16", "splitkv_append_kv", "splitkv_last_error", "splitkv_version",
-            "splitkv_args_size", "splitkv_plan_args_size", "splitkv_append_args_size")
+            "splitkv_args_size", "splitkv_plan_args_size", "splitkv_append_args_size",
+            "splitkv_calib_empty", "splitkv_calib_stream_read")
 
 
 def _check(fn, status):
@@ -235,3 +238,11 @@ def splitkv_e4m3_to_bf16(src: int, dst: int, n: int, stream: int = 0):
 
 def splitkv_append_kv(args: splitkv_append_args, stream: int = 0):
     _check("splitkv_append_kv", load().splitkv_append_kv(ctypes.byref(args), stream))
+
+
+def splitkv_calib_empty(stream: int = 0):
+    _check("splitkv_calib_empty", load().splitkv_calib_empty(stream))
+
+
+def splitkv_calib_stream_read(src: int, nbytes: int, workgroups: int, sink: int, stream: int = 0):
+    _check("splitkv_calib_stream_read", load().splitkv_calib_stream_read(src, nbytes, workgroups, sink, stream))
