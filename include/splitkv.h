@@ -51,13 +51,18 @@
  *   out          [B][T][Hq][d_v], bf16 or fp32 (out_dtype), contiguous.
  *   lse          fp32 [B][T][Hq] natural-log log-sum-exp of the scaled
  *                scores; may be NULL.
- *   workspace    fp32; layout (S = total_slots, R = T*Hq):
- *                  part_m [S][R]   max of scale*q.k over the split (natural
- *                                  log units; -inf if the row sees nothing)
- *                  part_l [S][R]   sum of exp(s - m)
- *                  part_o [S][R][d_v]  sum of exp(s - m) * v (v dequantised)
+ *   workspace    layout (S = total_slots, R = T*Hq):
+ *                  part_m [S][R]   fp32: max of scale*q.k over the split
+ *                                  (natural log units; -inf if the row sees
+ *                                  nothing)
+ *                  part_l [S][R]   fp32: sum of exp(s - m)
+ *                  part_o [S][R][d_v]  bf16 (round to nearest even): sum of
+ *                                  exp(s - m) * v (v dequantised)
  *                part_o starts at the first 256-byte boundary after part_l;
- *                splitkv_workspace_bytes() gives the total.
+ *                splitkv_workspace_bytes() gives the total.  The output is
+ *                bf16 itself; a bf16 part_o adds at most 2^-9 of the split
+ *                outputs' magnitude to it and halves the bytes the partial
+ *                kernel writes and the merge reads.
  *   debug        optional int32 [S][Hkv][row_blocks][8] records
  *                (b, i, hk, s, e, groups, xor_phys, sum_phys mod 2^31) over
  *                the 16-token groups of the split's range; row_blocks =
@@ -161,7 +166,7 @@ splitkv_status splitkv_plan(const splitkv_plan_args* args, const int32_t* seq_le
 /* Token range [*s, *e) of split i of n for a sequence of L tokens (host; same formula as the kernels). */
 splitkv_status splitkv_split_range(int32_t L, int32_t n, int32_t i, int32_t* s, int32_t* e);
 
-/* Bytes of fp32 workspace the partials of S slots need. */
+/* Bytes of workspace the partials of S slots need (fp32 m, l; bf16 o). */
 size_t splitkv_workspace_bytes(int32_t total_slots, int32_t T, int32_t Hq, int32_t d_v);
 
 /* Arguments of the decode entry points. */
@@ -198,6 +203,9 @@ typedef struct {
                                       over an e4m3 cache only: q quantised to e4m3 codes of
                                       q / q_scale inside the kernel) */
   float q_scale;                   /* per-tensor query scale for SPLITKV_Q_E4M3 (ignored for bf16) */
+  int32_t max_seq_splits;          /* > 0: the largest num_splits[b] of the plan, which sizes the
+                                      merge's launch (a smaller value than the truth is slower,
+                                      never wrong); 0: not given */
 } splitkv_args;
 
 /*

@@ -74,6 +74,7 @@ class splitkv_args(ctypes.Structure):
         ("out", c_vp), ("out_dtype", c_i32), ("lse", c_vp), ("debug", c_vp),
         ("uniform_splits", c_i32),
         ("q_dtype", c_i32), ("q_scale", c_f32),
+        ("max_seq_splits", c_i32),
     ]
 
 

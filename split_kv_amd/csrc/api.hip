@@ -64,7 +64,7 @@ enum class Kind { GqaBf16, GqaFp8, Mla };
 struct Layout {
   float* m;
   float* l;
-  float* o;
+  uint16_t* o;   // bf16 codes
 };
 
 Layout workspace_layout(const splitkv_args& a) {
@@ -74,7 +74,7 @@ Layout workspace_layout(const splitkv_args& a) {
   Layout w;
   w.m = a.workspace;
   w.l = a.workspace ? a.workspace + rows : nullptr;
-  w.o = a.workspace ? reinterpret_cast<float*>(reinterpret_cast<char*>(a.workspace) + ml) : nullptr;
+  w.o = a.workspace ? reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(a.workspace) + ml) : nullptr;
   return w;
 }
 
@@ -251,8 +251,8 @@ splitkv_status run_partial(const splitkv_args* a, Kind kind, bool direct, void* 
 splitkv_status run_combine(const splitkv_args* a, bool skip_single, void* stream, const char* fn) {
   splitkv_status st = check_common(a, fn);
   if (st != SPLITKV_OK) return st;
-  if (a->d_v != 128 && a->d_v != 256 && a->d_v != 512)
-    return fail(SPLITKV_ERR_UNSUPPORTED, "%s: d_v=%d; built for 128, 256, 512", fn, a->d_v);
+  if (a->d_v != 64 && a->d_v != 128 && a->d_v != 256 && a->d_v != 512)
+    return fail(SPLITKV_ERR_UNSUPPORTED, "%s: d_v=%d; built for 64, 128, 256, 512", fn, a->d_v);
   if (!a->out || !aligned(a->out, 16)) return fail(SPLITKV_ERR_INVALID_ARG, "%s: out null or misaligned", fn);
   const size_t need = splitkv_workspace_bytes(a->total_slots, a->T, a->Hq, a->d_v);
   if (!a->workspace || !aligned(a->workspace, 16) || a->workspace_bytes < need)
@@ -262,6 +262,9 @@ splitkv_status run_combine(const splitkv_args* a, bool skip_single, void* stream
       (a->uniform_splits > 0 && int64_t(a->uniform_splits) * a->B != a->total_slots))
     return fail(SPLITKV_ERR_INVALID_ARG, "%s: uniform_splits=%d inconsistent with B=%d, total_slots=%d",
                 fn, a->uniform_splits, a->B, a->total_slots);
+  if (a->max_seq_splits < 0 || a->max_seq_splits > SPLITKV_MAX_SPLITS_LIMIT)
+    return fail(SPLITKV_ERR_INVALID_ARG, "%s: max_seq_splits=%d outside [0, %d]", fn, a->max_seq_splits,
+                SPLITKV_MAX_SPLITS_LIMIT);
   st = check_device(nullptr);
   if (st != SPLITKV_OK) return st;
   const Layout w = workspace_layout(*a);
@@ -279,6 +282,7 @@ splitkv_status run_combine(const splitkv_args* a, bool skip_single, void* stream
   p.d_v = a->d_v;
   p.skip_single = skip_single ? 1 : 0;
   p.uniform_splits = a->uniform_splits;
+  p.max_seq_splits = a->max_seq_splits;
   const hipError_t err = launch_combine(p, static_cast<hipStream_t>(stream));
   if (err != hipSuccess) return fail(SPLITKV_ERR_LAUNCH, "%s: launch failed: %s", fn, hipGetErrorString(err));
   return SPLITKV_OK;

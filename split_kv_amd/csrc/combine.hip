@@ -7,28 +7,29 @@
 // gives the right answer ("vLLM 0.30.0 FA4 SplitKV Bug: H100 Decode Can Be 48%
 // Slower", section "Why the result is still correct").  Its cost grows with
 // the split count ("Shipped: 484.5 tok/s on one GB300 ...", section "Why 8
-// splits lost"): it reads S * rows * (d_v + 2) * 4 bytes of partials.
+// splits lost"): it reads S * rows * (2 * d_v + 8) bytes of partials (fp32
+// m and l, bf16 o).
 //
-// A row's d_v features are split over workgroups of 64 features each, and a
-// workgroup's 256 threads are 16 float4 columns x 16 groups over splits, so
-// that at decode sizes every load of the row is in flight at once (the kernel
-// is latency-bound): each thread loads m, l and one float4 of o for each of
-// its splits, up to eight at a time (as many as the row's split count needs:
-// a pass issues no load it would only mask away), merges them against its
-// own running max, and
-// the groups are merged through LDS (the same rescaling as across splits).
+// A workgroup merges one row's partials over C float4 columns (4C features)
+// with G groups of threads over the splits: thread (g, c) takes splits g,
+// g + G, g + 2G, ... of the row for column c, issuing the loads of up to U
+// splits (m, l and a float4 of o each) before merging any, and the G groups
+// meet in LDS (the same rescaling as across splits).  The host picks G for
+// the plan's largest split count so that a thread has at most eight splits
+// (G = 1 needs no LDS step at all); C is 256 / G columns, or the whole row
+// when that is narrower, so a row of the six-token MLA shape (512 features,
+// ~21 splits) is two workgroups of 4 x 64 threads and a row of the few-KV
+// shape (256 features, ~62 splits) two of 8 x 32.  Every load of a row is
+// in flight at once: at decode sizes the merge is latency-bound.
 #include "device.h"
 
 namespace splitkv {
 
-constexpr int kCombineCols = 16;                // float4 columns per workgroup (64 features)
-constexpr int kCombineGroups = 256 / kCombineCols;
-
 // One thread's share of a row's splits: splits g, g+G, g+2G, ... of the n,
 // U loads in flight per pass, merged into the running (M2, lam, acc) in base 2.
-template <int U, int G>
-__device__ __forceinline__ void merge_splits(const float* part_m, const float* part_l, const float* po,
-                                             int64_t step, int R, int rix, int base, int n, int g,
+template <int U>
+__device__ __forceinline__ void merge_splits(const float* part_m, const float* part_l, const uint16_t* po,
+                                             int64_t step, int R, int rix, int base, int n, int g, int G,
                                              float& M2, float& lam, f32x4& acc) {
   for (int i0 = g; i0 < n; i0 += U * G) {
     float mi[U], li[U];
@@ -39,7 +40,9 @@ __device__ __forceinline__ void merge_splits(const float* part_m, const float* p
       const int64_t sl = base + (i < n ? i : i0);   // past the end: reread a valid slot, weight 0
       mi[u] = part_m[sl * R + rix];
       li[u] = part_l[sl * R + rix];
-      oi[u] = *reinterpret_cast<const f32x4*>(po + sl * step);
+      const u32x2 w = *reinterpret_cast<const u32x2*>(po + sl * step);   // four bf16 codes
+      oi[u] = f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                    __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
       if (i >= n) mi[u] = -INFINITY;
     }
 #pragma unroll
@@ -56,27 +59,29 @@ __device__ __forceinline__ void merge_splits(const float* part_m, const float* p
   }
 }
 
-// All fourteen argument dwords (workspace, plan, output and log-sum-exp
-// pointers, the row geometry and flags) are preloaded into scalar registers
-// at wave launch, so the two plan reads of the row's sequence are the first
-// memory accesses, issued together, and the stores need no argument load.
-// part_l and part_o follow part_m in the workspace: part_l at SR floats
-// (SR = total_slots * rows per sequence), part_o at the next 256-byte
-// boundary after 2 * SR floats.  The merge runs in base 2 on the hardware
-// exponential (every argument is <= 0: a difference from the running max).
+// All argument dwords (workspace, plan, output and log-sum-exp pointers, the
+// row geometry and flags) are preloaded into scalar registers at wave launch,
+// so the two plan reads of the row's sequence are the first memory accesses,
+// issued together, and the stores need no argument load.  part_l and part_o
+// follow part_m in the workspace: part_l at SR floats (SR = total_slots *
+// rows per sequence), part_o at the next 256-byte boundary after 2 * SR
+// floats.  The merge runs in base 2 on the hardware exponential (every
+// argument is <= 0: a difference from the running max).
 // flags: d_v (bits 0-15) | skip rows of single-split sequences (bit 16) |
 // fp32 output (bit 17) | uniform split count (bits 18-26; 0: read the plan).
 // With a uniform count the row's plan is n = that count and base = b * n, so
-// the partial loads are the first memory accesses.
+// the partial loads are the first memory accesses.  The workgroup has C * G
+// threads (C = blockDim.x / G float4 columns).
+template <int G>
 __global__ __launch_bounds__(256) void combine_kernel(const float* part_m, const int32_t* num_splits,
                                                       const int32_t* slot_offset, void* out,
                                                       float* lse, int32_t R, int32_t dsplit,
                                                       int32_t flags, int32_t SR) {
-  constexpr int CH = kCombineCols, G = kCombineGroups;
-  __shared__ float red_m[G][CH], red_l[G][CH];
-  __shared__ f32x4 red_o[G][CH];
+  __shared__ float red_m[256], red_l[256];
+  __shared__ f32x4 red_o[256];
 
   const int tid = threadIdx.x;
+  const int C = int(blockDim.x) / G;
   const int row = int(blockIdx.x) / dsplit;
   const int part = int(blockIdx.x) - row * dsplit;
   const int b = row / R;
@@ -93,70 +98,95 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* part_m, const
   }
   if ((flags & (1 << 16)) && n == 1) return;
   const int DV = flags & 0xffff;
-  const int c = tid % CH, g = tid / CH;
+  const int c = tid % C, g = tid / C;
   const float* part_l = part_m + SR;
-  const float* part_o = part_m + (int64_t(2) * SR * 4 + 255) / 256 * 64;
+  const uint16_t* part_o =
+      reinterpret_cast<const uint16_t*>(part_m + (int64_t(2) * SR * 4 + 255) / 256 * 64);
 
   // running state in base 2: M2 = max of m_i * log2(e)
   float M2 = -INFINITY, lam = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  const float* po = part_o + int64_t(rix) * DV + 64 * part + 4 * c;
+  const int f0 = 4 * (C * part + c);                  // this thread's first feature
+  const uint16_t* po = part_o + int64_t(rix) * DV + f0;
   const int64_t step = int64_t(R) * DV;
   // loads per thread and pass: just enough for the row's splits (uniform
   // across the workgroup), so no pass issues loads it only masks away
   const int per = (n + G - 1) / G;
   if (per <= 1)
-    merge_splits<1, G>(part_m, part_l, po, step, R, rix, base, n, g, M2, lam, acc);
+    merge_splits<1>(part_m, part_l, po, step, R, rix, base, n, g, G, M2, lam, acc);
   else if (per <= 2)
-    merge_splits<2, G>(part_m, part_l, po, step, R, rix, base, n, g, M2, lam, acc);
+    merge_splits<2>(part_m, part_l, po, step, R, rix, base, n, g, G, M2, lam, acc);
   else if (per <= 4)
-    merge_splits<4, G>(part_m, part_l, po, step, R, rix, base, n, g, M2, lam, acc);
+    merge_splits<4>(part_m, part_l, po, step, R, rix, base, n, g, G, M2, lam, acc);
   else
-    merge_splits<8, G>(part_m, part_l, po, step, R, rix, base, n, g, M2, lam, acc);
-  red_m[g][c] = M2;
-  red_l[g][c] = lam;
-  red_o[g][c] = acc;
-  __syncthreads();
-  if (g == 0) {
-    float Mt = red_m[0][c];
+    merge_splits<8>(part_m, part_l, po, step, R, rix, base, n, g, G, M2, lam, acc);
+  if constexpr (G > 1) {
+    red_m[tid] = M2;
+    red_l[tid] = lam;
+    red_o[tid] = acc;
+    __syncthreads();
+    if (g != 0) return;
+    float Mt = M2;
 #pragma unroll
-    for (int k = 1; k < G; ++k) Mt = fmaxf(Mt, red_m[k][c]);
+    for (int k = 1; k < G; ++k) Mt = fmaxf(Mt, red_m[k * C + c]);
     float lt = 0.f;
     f32x4 ot = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < G; ++k) {
-      const float mk = red_m[k][c];
+      const float mk = red_m[k * C + c];
       const float w = mk == -INFINITY ? 0.f : fast_exp2(mk - Mt);
-      lt += w * red_l[k][c];
-      ot += w * red_o[k][c];
+      lt += w * red_l[k * C + c];
+      ot += w * red_o[k * C + c];
     }
-    const bool ok = Mt != -INFINITY && lt > 0.f;
-    ot *= ok ? 1.f / lt : 0.f;
-    const int64_t o = int64_t(row) * DV + 64 * part + 4 * c;
-    if (flags & (1 << 17)) {
-      *reinterpret_cast<f32x4*>(static_cast<float*>(out) + o) = ot;
-    } else {
-      u32x2 pk = {pack_bf16x2(ot[0], ot[1]), pack_bf16x2(ot[2], ot[3])};
-      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + o) = pk;
-    }
-    if (lse && part == 0 && c == 0) lse[row] = ok ? (Mt + log2f(lt)) * kLn2 : -INFINITY;
+    M2 = Mt;
+    lam = lt;
+    acc = ot;
   }
+  const bool ok = M2 != -INFINITY && lam > 0.f;
+  acc *= ok ? 1.f / lam : 0.f;
+  const int64_t o = int64_t(row) * DV + f0;
+  if (flags & (1 << 17)) {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(out) + o) = acc;
+  } else {
+    u32x2 pk = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + o) = pk;
+  }
+  if (lse && part == 0 && c == 0) lse[row] = ok ? (M2 + log2f(lam)) * kLn2 : -INFINITY;
 }
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
-  if (p.d_v % 64 != 0 || p.d_v > 0xffff || p.uniform_splits < 0 || p.uniform_splits > 0x1ff)
+  if (p.d_v % 4 != 0 || p.d_v > 0xffff || p.uniform_splits < 0 || p.uniform_splits > 0x1ff)
     return hipErrorInvalidValue;
-  const int dsplit = p.d_v / 64;
+  // splits per row the launch is sized for: the plan's largest count when
+  // known, else the most any plan can hold
+  const int nmax = p.uniform_splits > 0 ? p.uniform_splits
+                                        : (p.max_seq_splits > 0 ? p.max_seq_splits : SPLITKV_MAX_SPLITS_LIMIT);
+  int G = 1;
+  while (G < 16 && (nmax + G - 1) / G > 8) G *= 2;
+  const int cols = p.d_v / 4;                       // float4 columns of a row
+  int C = 256 / G;
+  while (C > cols) C /= 2;
+  if (cols % C != 0) return hipErrorInvalidValue;   // d_v a multiple of 4 * C
+  const int dsplit = cols / C;
   const int64_t wgs = int64_t(p.B) * p.R * dsplit;
   const int64_t SR = p.part_l - p.part_m;
   if (wgs > INT32_MAX || SR > INT32_MAX / 8 ||
-      p.part_o != p.part_m + (2 * SR * 4 + 255) / 256 * 64)
+      p.part_o != reinterpret_cast<const uint16_t*>(p.part_m + (2 * SR * 4 + 255) / 256 * 64))
     return hipErrorInvalidValue;
-  const dim3 grid(static_cast<unsigned>(wgs)), block(256);
+  const dim3 grid(static_cast<unsigned>(wgs)), block(unsigned(C * G));
   const int32_t flags = p.d_v | (p.skip_single ? 1 << 16 : 0) | (p.out_f32 ? 1 << 17 : 0) |
                        (p.uniform_splits << 18);
-  hipLaunchKernelGGL(combine_kernel, grid, block, 0, stream, p.part_m, p.num_splits, p.slot_offset,
-                     p.out, p.lse, p.R, dsplit, flags, int32_t(SR));
+#define SPLITKV_COMBINE(GG)                                                                             \
+  hipLaunchKernelGGL(combine_kernel<GG>, grid, block, 0, stream, p.part_m, p.num_splits, p.slot_offset, \
+                     p.out, p.lse, p.R, dsplit, flags, int32_t(SR))
+  switch (G) {
+    case 1: SPLITKV_COMBINE(1); break;
+    case 2: SPLITKV_COMBINE(2); break;
+    case 4: SPLITKV_COMBINE(4); break;
+    case 8: SPLITKV_COMBINE(8); break;
+    default: SPLITKV_COMBINE(16); break;
+  }
+#undef SPLITKV_COMBINE
   return hipGetLastError();
 }
 

@@ -43,7 +43,7 @@ struct PartialParams {
   float v_scale;
   float* part_m;                // [S][T*Hq]
   float* part_l;
-  float* part_o;                // [S][T*Hq][d_v]
+  uint16_t* part_o;             // [S][T*Hq][d_v] bf16 codes
   void* out;
   int32_t out_f32;
   float* lse;
@@ -56,13 +56,14 @@ struct CombineParams {
   const int32_t* slot_offset;
   const float* part_m;
   const float* part_l;
-  const float* part_o;
+  const uint16_t* part_o;       // bf16 codes
   void* out;
   int32_t out_f32;
   float* lse;
   int32_t B, R, d_v;            // R = T * Hq rows per sequence
   int32_t skip_single;          // rows of single-split sequences were written by the partial kernel
   int32_t uniform_splits;       // > 0: every sequence has this many splits (no plan reads)
+  int32_t max_seq_splits;       // > 0: no sequence has more splits (sizes the launch); 0: unknown
 };
 
 // Parameters of the KV append kernel (index 0: keys, 1: values).

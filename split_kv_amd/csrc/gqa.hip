@@ -59,7 +59,7 @@ struct GqaRest {
   const int32_t* seq_lens;
   float* part_m;
   float* part_l;
-  float* part_o;
+  uint16_t* part_o;               // bf16 codes
   void* out;
   float* lse;
   int32_t* debug;
@@ -446,15 +446,12 @@ __global__ __launch_bounds__(256) void gqa_partial_kernel(
         for (int w = 1; w < 4; ++w) acc += wgt[w] * ov[w][q];
         acc *= mul;
         const int64_t o = obase + 4 * (cl + TPR * q);
-        if (direct) {
-          if (a.out_f32) {
-            *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + o) = acc;
-          } else {
-            u32x2 pk = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
-            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + o) = pk;
-          }
+        if (direct && a.out_f32) {
+          *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + o) = acc;
         } else {
-          *reinterpret_cast<f32x4*>(a.part_o + o) = acc;
+          // the bf16 output, or the partial o (bf16 in the workspace)
+          u32x2 pk = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+          *reinterpret_cast<u32x2*>((direct ? static_cast<uint16_t*>(a.out) : a.part_o) + o) = pk;
         }
       }
       if (cl == 0) {

@@ -77,6 +77,7 @@ static_assert((kF8LoadsPerWave - 1) * kWaves < kF8TileLoads && kF8LoadsPerWave *
 constexpr int kQk = kMlaDqk / 32 / 2;            // 9 k-steps of 32 key features per half
 constexpr int kPv = kMlaDv / 128 / 2;            // 2 chunks of 128 value features per half
 static_assert(kSlotBytes == kTileChunks * 16 && kTileChunks % 64 == 0, "slot holds a tile");
+static_assert(kStageBytes <= kPoolBytes, "the epilogue's staging fits the tile pool");
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -141,10 +142,8 @@ __global__ __launch_bounds__(512) void mla_partial_kernel(PartialParams p, int p
 #pragma unroll
     for (int it = 0; it < kQk; ++it) q[it] = *reinterpret_cast<const bf16x8*>(qrow + 64 * it);
   }
-  // The query has landed before the first tile fill is issued: the compiler
-  // would otherwise wait for it inside the tile loop with load counts that,
-  // not knowing about the fills, would also drain the fills in flight.
-  __builtin_amdgcn_s_waitcnt(0x0F70);                      // vmcnt(0)
+  // The query's loads stay in flight while the first tile fills are issued
+  // (below); the wait for all of them comes before the tile loop.
 
   // Tiles that end at or before full_end need no mask: every token is in the
   // range and visible to every row of the wave (its first row has the
@@ -432,6 +431,13 @@ __global__ __launch_bounds__(512) void mla_partial_kernel(PartialParams p, int p
     tile_pages(2, pa, pb);
     fill(2, fill_slot(2), pa, pb);
     tile_pages(3, pa, pb);
+    // Wait here for the query (and with it, loads completing in order, the
+    // three fills): the compiler does not see the fills, and a wait for the
+    // query placed inside the tile loop would drain the fills in flight there.
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0x0F70);                    // vmcnt(0)
+#pragma unroll
+    for (int it = 0; it < kQk; ++it) asm volatile("" ::"v"(q[it]));
     if constexpr (FP8) {
       // tile 0 widened before the loop (tile k+1 is widened in step k)
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -445,7 +451,7 @@ __global__ __launch_bounds__(512) void mla_partial_kernel(PartialParams p, int p
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0x0F70);                      // vmcnt(0)
 
-  store_rows(p, o, rowv, qg, hf, b, slot, nsplit, m_ref, m_true, l_run);
+  store_rows(p, o, rowv, qg, hf, b, slot, nsplit, m_ref, m_true, l_run, pool);
 
   if (p.debug && tid == 0) store_debug(p, slot, rb, b, split, s, e, dbg_groups, dbg_xor, dbg_sum);
 }

@@ -44,34 +44,61 @@ __device__ __forceinline__ void lds_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Row pitch (floats) of the epilogue's LDS staging: 256 features plus 8, so
+// that the sixteen rows of a 16-byte write land in distinct banks.
+constexpr int kStagePitch = 264;
+constexpr int kStageBytes = kWaves * 16 * kStagePitch * 4;    // 135168
+
 // Epilogue of one wave: lane (n16, qg) of wave half hf holds
 // O[row][256 hf + 16 e + 4 qg + i] in o[e][i] (unnormalised, relative to the
 // reference max m_ref), the running true max m_true and its part of the
 // weight sum l_run (the row's four qg lanes hold parts that add up).  Both
 // waves of a pair hold the same (m, l); the hf == 0 wave writes them.
+// The rows go out through LDS (`stage`, kStageBytes of the kernel's tile
+// pool, free once every wave has left the tile loop): written there in the
+// MFMA layout, read back a row at a time, so that each store instruction
+// writes one row's 256 contiguous features -- in register layout a store
+// would cover sixteen rows with 64 bytes each, which halves the store rate.
+// Must be reached by every wave of the workgroup (it holds a barrier).
 __device__ __forceinline__ void store_rows(const PartialParams& p, const f32x4 (&o)[16], int rowv,
                                            int qg, int hf, int b, int slot, int nsplit, float m_ref,
-                                           float m_true, float l_run) {
+                                           float m_true, float l_run, uint8_t* stage) {
   const bool direct = p.direct && nsplit == 1;
   const int64_t R = int64_t(p.T) * p.Hq;
   // bring (l, o) from the reference max to the true max of the row
   const float f = (m_ref == -INFINITY) ? 0.f : fast_exp2(m_ref - m_true);
   const float m_run = m_true;
   const float l_tot = column_sum4(l_run * f);
-  const int row = min(rowv, p.rows - 1);
   const bool real = rowv < p.rows;
-  const int t = row / p.Hq, h = row % p.Hq;
-  const int64_t rix = int64_t(t) * p.Hq + h;
+  const int64_t rix = rowv;              // row (t, h) of the sequence is t * Hq + h
   float mul = p.v_scale * f;
   if (direct) mul = l_tot > 0.f ? p.v_scale * f / l_tot : 0.f;
+  const int lane = int(threadIdx.x & 63);
+  const int wave = int(threadIdx.x >> 6);
+  const int n16 = lane & 15;
+  float* st = reinterpret_cast<float*>(stage) + wave * 16 * kStagePitch;
+  __syncthreads();                       // every wave is done with the tile pool
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
-    const int d = 256 * hf + 16 * e + 4 * qg;
     f32x4 v4 = o[e];
     v4 *= mul;
-    if (!real) continue;
+    *reinterpret_cast<f32x4*>(st + n16 * kStagePitch + 16 * e + 4 * qg) = v4;
+  }
+  // each wave reads back only what it wrote (no barrier; the LDS waits
+  // suffice), all sixteen rows before the first store; rows are in (t, h)
+  // order, so a row's index within the sequence is the row number itself
+  const int row0 = rowv - n16;           // the wave's first row
+  f32x4 rv4[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) rv4[r] = *reinterpret_cast<const f32x4*>(st + r * kStagePitch + 4 * lane);
+  const int d = 256 * hf + 4 * lane;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int64_t rr = row0 + r;
+    if (rr >= p.rows) continue;
+    const f32x4 v4 = rv4[r];
     if (direct) {
-      const int64_t oo = (int64_t(b) * R + rix) * kDv + d;
+      const int64_t oo = (int64_t(b) * R + rr) * kDv + d;
       if (p.out_f32) {
         *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + oo) = v4;
       } else {
@@ -79,7 +106,8 @@ __device__ __forceinline__ void store_rows(const PartialParams& p, const f32x4 (
         *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + oo) = pk;
       }
     } else {
-      *reinterpret_cast<f32x4*>(p.part_o + (int64_t(slot) * R + rix) * kDv + d) = v4;
+      u32x2 pk = {pack_bf16x2(v4[0], v4[1]), pack_bf16x2(v4[2], v4[3])};
+      *reinterpret_cast<u32x2*>(p.part_o + (int64_t(slot) * R + rr) * kDv + d) = pk;
     }
   }
   if (real && qg == 0 && hf == 0) {

@@ -64,6 +64,7 @@ static_assert((kLPW - 1) * kWaves < kSlotLoads && kLPW * kWaves >= kSlotLoads,
 static_assert(kRing * kSlotBytes + kWaves * 2 * 64 * 16 == 160 * 1024, "ring and exchange fill the LDS");
 static_assert(kChunks % 4 == 0, "the swizzle permutes aligned groups of four chunks");
 static_assert(kRing == 2 * kAhead && kAhead == kWin, "one window computed while the next is filled");
+static_assert(kStageBytes <= kRing * kSlotBytes, "the epilogue's staging fits the sub-tile ring");
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
@@ -420,7 +421,7 @@ __global__ __launch_bounds__(512) void mla_fp8q_partial_kernel(PartialParams p, 
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0x0F70);                      // vmcnt(0)
 
-  store_rows(p, o, rowv, qg, hf, b, slot, nsplit, m_ref, m_true, l_run);
+  store_rows(p, o, rowv, qg, hf, b, slot, nsplit, m_ref, m_true, l_run, ring);
   if (p.debug && tid == 0) store_debug(p, slot, rb, b, split, s, e, dbg_groups, dbg_xor, dbg_sum);
 }
 

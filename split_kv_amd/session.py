@@ -128,6 +128,7 @@ class DecodeSession:
         a.debug = self.debug.data_ptr() if self.debug is not None else None
         ns = self.num_splits_host
         a.uniform_splits = int(ns[0]) if len(ns) and (ns == ns[0]).all() else 0
+        a.max_seq_splits = int(ns.max()) if len(ns) else 0
         self.args = a
 
     def set_block_table(self, block_table):
@@ -164,11 +165,12 @@ class DecodeSession:
         return self.out, self.lse
 
     def partials(self):
-        """Views (part_m [S,T,Hq], part_l [S,T,Hq], part_o [S,T,Hq,d_v]) of the workspace."""
+        """Views (part_m [S,T,Hq] fp32, part_l [S,T,Hq] fp32, part_o [S,T,Hq,d_v] bf16) of
+        the workspace."""
         s = self.shape
         S, T, Hq, dv = self.total_slots, s["T"], s["Hq"], s["d_v"]
         rows = S * T * Hq
         ml = -(-(2 * rows * 4) // 256) * 256 // 4
         w = self.workspace
-        return (w[:rows].view(S, T, Hq), w[rows:2 * rows].view(S, T, Hq),
-                w[ml:ml + rows * dv].view(S, T, Hq, dv))
+        po = w[ml:ml + (rows * dv + 1) // 2].view(self.torch.bfloat16)[:rows * dv]
+        return (w[:rows].view(S, T, Hq), w[rows:2 * rows].view(S, T, Hq), po.view(S, T, Hq, dv))

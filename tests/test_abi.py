@@ -142,7 +142,7 @@ def test_workspace_bytes():
     S, T, Hq, dv = 13, 2, 16, 256
     rows = S * T * Hq
     ml = -(-(2 * rows * 4) // 256) * 256
-    assert sk.splitkv_workspace_bytes(S, T, Hq, dv) == ml + rows * dv * 4
+    assert sk.splitkv_workspace_bytes(S, T, Hq, dv) == ml + rows * dv * 2     # bf16 part_o
 
 
 def test_validate_block_table():
@@ -198,6 +198,14 @@ def test_uniform_splits_must_match_the_slot_count():
     assert "uniform_splits" in sk.splitkv_last_error()
     a = _args(uniform_splits=-1)
     assert lib.splitkv_combine(ctypes.byref(a), None) == sk.SPLITKV_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("m", [-1, 257])
+def test_max_seq_splits_hint_range(m):
+    lib = _lib()
+    a = _args(max_seq_splits=m)
+    assert lib.splitkv_combine(ctypes.byref(a), None) == sk.SPLITKV_ERR_INVALID_ARG
+    assert "max_seq_splits" in sk.splitkv_last_error()
 
 
 def test_mla_shape_errors_without_device():
@@ -275,7 +283,7 @@ def test_version_string():
 
 
 def test_noalloc_refuses_an_oversized_plan_without_a_device():
-    # 256 MLA slots of 768 rows need ~404 MB of partials, more than the
+    # 256 MLA slots of 768 rows need ~202 MB of partials, more than the
     # library's 64 MiB buffer: refused on the host, before any device call
     lib = _lib()
     a = sk.splitkv_args()

@@ -153,15 +153,64 @@ def test_combine_alone_against_oracle_combine():
     o[np.isinf(m)] = 0
     gm.copy_(torch.from_numpy(m))
     gl.copy_(torch.from_numpy(l))
-    go.copy_(torch.from_numpy(o))
+    go.copy_(torch.from_numpy(o))                       # rounded to the workspace's bf16
+    o = to_np(go)
     log("combine alone, random partials with -inf rows")
     sess.combine()
     torch.cuda.synchronize()
-    Oref, Lref = oracle.combine(m.astype(np.float64), l.astype(np.float64), o.astype(np.float64),
+    Oref, Lref = oracle.combine(m.astype(np.float64), l.astype(np.float64), o,
                                 sess.num_splits_host, sess.slot_offset_host)
     assert_close(to_np(sess.out), Oref, 1e-6, 1e-5, "combine out")
     assert_close(to_np(sess.lse), Lref, 1e-6, 1e-5, "combine lse")
     assert (to_np(sess.out)[0, 0, 3] == 0).all() and np.isneginf(to_np(sess.lse)[0, 0, 3])
+
+
+@pytest.mark.parametrize("hint", ["exact", "unknown", "low"])
+@pytest.mark.parametrize("splits", [[1], [3], [9, 1, 21], [62], [130, 2]])
+@pytest.mark.parametrize("d_v,T,Hq", [(64, 1, 8), (128, 1, 32), (256, 1, 16), (512, 6, 16)])
+def test_combine_launch_shapes(d_v, T, Hq, splits, hint):
+    # The merge sizes its launch (split groups per row, columns per
+    # workgroup) from the plan's largest split count; a missing or too-small
+    # hint must only cost time.  Random partials with empty splits, merged
+    # through the C ABI, against the oracle's fp64 merge.
+    _need_gpu()
+    import torch
+    import split_kv_amd as sk
+    rng = np.random.default_rng(1000 + d_v + sum(splits))
+    B, R = len(splits), T * Hq
+    ns = np.array(splits, dtype=np.int32)
+    off = np.concatenate([[0], np.cumsum(ns)]).astype(np.int32)
+    S = int(off[-1])
+    m = rng.normal(0, 3, size=(S, T, Hq)).astype(np.float32)
+    m[rng.random(m.shape) < 0.25] = -np.inf
+    l = np.where(np.isinf(m), 0, rng.uniform(0.5, 20, size=m.shape)).astype(np.float32)
+    o = (rng.normal(size=(S, T, Hq, d_v)) * l[..., None]).astype(np.float32)
+    o[np.isinf(m)] = 0
+    nbytes = sk.splitkv_workspace_bytes(S, T, Hq, d_v)
+    ws = torch.full(((nbytes + 3) // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    lo = -(-(2 * S * R * 4) // 256) * 256 // 4
+    ws[:S * R] = torch.from_numpy(m.reshape(-1)).cuda()
+    ws[S * R:2 * S * R] = torch.from_numpy(l.reshape(-1)).cuda()
+    ob = torch.from_numpy(o.reshape(-1)).to(torch.bfloat16)           # part_o is bf16
+    ws[lo:lo + (S * R * d_v) // 2] = ob.view(torch.float32).cuda()
+    o = ob.to(torch.float64).numpy().reshape(o.shape)
+    out = torch.full((B, T, Hq, d_v), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((B, T, Hq), float("nan"), dtype=torch.float32, device="cuda")
+    nsd, offd = torch.from_numpy(ns).cuda(), torch.from_numpy(off).cuda()
+    lens = torch.full((B,), 16 * 256, dtype=torch.int32, device="cuda")     # not read by the merge
+    a = sk.splitkv_args()
+    a.num_splits, a.slot_offset, a.total_slots = nsd.data_ptr(), offd.data_ptr(), S
+    a.seq_lens = lens.data_ptr()
+    a.B, a.T, a.Hq, a.Hkv, a.d_qk, a.d_v = B, T, Hq, 1, d_v, d_v
+    a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel() * 4
+    a.out, a.out_dtype, a.lse = out.data_ptr(), sk.SPLITKV_OUT_F32, lse.data_ptr()
+    a.max_seq_splits = {"exact": int(ns.max()), "unknown": 0, "low": 1}[hint]
+    log(f"combine d_v={d_v} T={T} Hq={Hq} splits={splits} hint={hint}")
+    sk.splitkv_combine(a, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    Oref, Lref = oracle.combine(m.astype(np.float64), l.astype(np.float64), o, ns, off)
+    assert_close(to_np(out), Oref, 1e-6, 1e-5, "combine out")
+    assert_close(to_np(lse), Lref, 1e-6, 1e-5, "combine lse")
 
 
 def test_uniform_plan_promise_changes_nothing():

@@ -67,7 +67,7 @@ def test_noalloc_refuses_plans_beyond_its_buffer():
     _need_gpu()
     import split_kv_amd as sk
     case = synth.mla_decode(L=65536)
-    sess, _ = session_for(case, requested_splits=64, max_splits=256)
+    sess, _ = session_for(case, requested_splits=128, max_splits=256)
     need = sk.splitkv_workspace_bytes(sess.total_slots, case.T, case.Hq, case.d_v)
     assert need > sk.SPLITKV_NOALLOC_SCRATCH_BYTES
     with pytest.raises(sk.SplitKVError) as ei:
