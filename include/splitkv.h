@@ -51,18 +51,13 @@
  *   out          [B][T][Hq][d_v], bf16 or fp32 (out_dtype), contiguous.
  *   lse          fp32 [B][T][Hq] natural-log log-sum-exp of the scaled
  *                scores; may be NULL.
- *   workspace    layout (S = total_slots, R = T*Hq):
- *                  part_m [S][R]   fp32: max of scale*q.k over the split
- *                                  (natural log units; -inf if the row sees
- *                                  nothing)
- *                  part_l [S][R]   fp32: sum of exp(s - m)
- *                  part_o [S][R][d_v]  bf16 (round to nearest even): sum of
- *                                  exp(s - m) * v (v dequantised)
+ *   workspace    fp32; layout (S = total_slots, R = T*Hq):
+ *                  part_m [S][R]   max of scale*q.k over the split (natural
+ *                                  log units; -inf if the row sees nothing)
+ *                  part_l [S][R]   sum of exp(s - m)
+ *                  part_o [S][R][d_v]  sum of exp(s - m) * v (v dequantised)
  *                part_o starts at the first 256-byte boundary after part_l;
- *                splitkv_workspace_bytes() gives the total.  The output is
- *                bf16 itself; a bf16 part_o adds at most 2^-9 of the split
- *                outputs' magnitude to it and halves the bytes the partial
- *                kernel writes and the merge reads.
+ *                splitkv_workspace_bytes() gives the total.
  *   debug        optional int32 [S][Hkv][row_blocks][8] records
  *                (b, i, hk, s, e, groups, xor_phys, sum_phys mod 2^31) over
  *                the 16-token groups of the split's range; row_blocks =
@@ -166,7 +161,7 @@ splitkv_status splitkv_plan(const splitkv_plan_args* args, const int32_t* seq_le
 /* Token range [*s, *e) of split i of n for a sequence of L tokens (host; same formula as the kernels). */
 splitkv_status splitkv_split_range(int32_t L, int32_t n, int32_t i, int32_t* s, int32_t* e);
 
-/* Bytes of workspace the partials of S slots need (fp32 m, l; bf16 o). */
+/* Bytes of fp32 workspace the partials of S slots need. */
 size_t splitkv_workspace_bytes(int32_t total_slots, int32_t T, int32_t Hq, int32_t d_v);
 
 /* Arguments of the decode entry points. */
@@ -206,6 +201,10 @@ typedef struct {
   int32_t max_seq_splits;          /* > 0: the largest num_splits[b] of the plan, which sizes the
                                       merge's launch (a smaller value than the truth is slower,
                                       never wrong); 0: not given */
+  int32_t* tickets;                /* splitkv_decode_single_launch only: int32 [B][Hkv][row_blocks]
+                                      arrival counters (row_blocks = ceil(g*T / 16)), all zero
+                                      before the first call; every completed call leaves them
+                                      zero.  Ignored (may be NULL) elsewhere */
 } splitkv_args;
 
 /*
@@ -213,7 +212,7 @@ typedef struct {
  * One workgroup per (slot, KV head, block of 16 query rows) writes the
  * partial (m, l, o) of its split ("vLLM 0.30.0 FA4 SplitKV Bug ...", section
  * "What SplitKV is trying to do": each split computes a partial attention
- * result).  Requires kv_dtype == BF16, d_qk == d_v in {128, 256},
+ * result).  Requires kv_dtype == BF16, d_qk == d_v in {64, 128, 256},
  * page_size % 16 == 0, 16-byte aligned q / caches / strides.
  */
 splitkv_status splitkv_decode_partial(const splitkv_args* args, void* stream);
@@ -224,7 +223,7 @@ splitkv_status splitkv_decode_partial(const splitkv_args* args, void* stream);
  * FP8 KV cache).  Codes widen exactly to bf16; k_scale multiplies the scores,
  * v_scale the output.  The query is never quantised and takes no scale of its
  * own (same page, timeline: no q_scale for model-dtype queries over an FP8
- * cache).  Requires kv_dtype == E4M3, d_qk == d_v in {128, 256}.
+ * cache).  Requires kv_dtype == E4M3, d_qk == d_v in {64, 128, 256}.
  */
 splitkv_status splitkv_decode_partial_fp8(const splitkv_args* args, void* stream);
 
@@ -270,6 +269,20 @@ splitkv_status splitkv_combine(const splitkv_args* args, void* stream);
  * `kernel` is SPLITKV_KERNEL_GQA or SPLITKV_KERNEL_MLA.
  */
 splitkv_status splitkv_decode(const splitkv_args* args, int32_t kernel, void* stream);
+
+/*
+ * splitkv_decode_single_launch -- the whole grouped-query decode step in one
+ * kernel: the workgroups of one (sequence, KV head, row block) take a ticket
+ * in args->tickets when their partial is stored, and the last to arrive
+ * merges the sequence's partials into out/lse (the same log-sum-exp merge as
+ * splitkv_combine), so the merge costs no second launch ("Shipped: 484.5
+ * tok/s on one GB300 ...", section "Why 8 splits lost": the merge can eat the
+ * gain of more splits).  The partials still go through args->workspace.
+ * `kernel` must be SPLITKV_KERNEL_GQA (else SPLITKV_ERR_UNSUPPORTED); the
+ * tickets array must be given when any sequence has several splits.  Calls
+ * that share a tickets array must not overlap.
+ */
+splitkv_status splitkv_decode_single_launch(const splitkv_args* args, int32_t kernel, void* stream);
 
 /*
  * splitkv_decode_noalloc -- splitkv_decode for callers that cannot allocate

@@ -75,6 +75,7 @@ class splitkv_args(ctypes.Structure):
         ("uniform_splits", c_i32),
         ("q_dtype", c_i32), ("q_scale", c_f32),
         ("max_seq_splits", c_i32),
+        ("tickets", c_vp),
     ]
 
 
@@ -124,6 +125,7 @@ def load():
             "splitkv_combine": (c_i32, [P(splitkv_args), c_vp]),
             "splitkv_decode": (c_i32, [P(splitkv_args), c_i32, c_vp]),
             "splitkv_decode_noalloc": (c_i32, [P(splitkv_args), c_i32, c_vp]),
+            "splitkv_decode_single_launch": (c_i32, [P(splitkv_args), c_i32, c_vp]),
             "splitkv_validate_block_table": (c_i32, [c_vp, c_vp, c_i32, c_i64, c_i32, c_i32]),
             "splitkv_e4m3_to_bf16": (c_i32, [c_vp, c_vp, c_i64, c_vp]),
             "splitkv_append_kv": (c_i32, [P(splitkv_append_args), c_vp]),
@@ -149,7 +151,8 @@ def load():
 
 EXPORTED = ("splitkv_plan", "splitkv_split_range", "splitkv_workspace_bytes",
             "splitkv_decode_partial", "splitkv_decode_partial_fp8", "splitkv_mla_decode_partial",
-            "splitkv_combine", "splitkv_decode", "splitkv_decode_noalloc", "splitkv_validate_block_table",
+            "splitkv_combine", "splitkv_decode", "splitkv_decode_noalloc", "splitkv_decode_single_launch",
+            "splitkv_validate_block_table",
             "splitkv_e4m3_to_bf16", "splitkv_append_kv", "splitkv_last_error", "splitkv_version",
             "splitkv_args_size", "splitkv_plan_args_size", "splitkv_append_args_size",
             "splitkv_calib_empty", "splitkv_calib_stream_read")
@@ -218,6 +221,11 @@ def splitkv_combine(args: splitkv_args, stream: int = 0):
 
 def splitkv_decode(args: splitkv_args, kernel: int, stream: int = 0):
     _check("splitkv_decode", load().splitkv_decode(ctypes.byref(args), kernel, stream))
+
+
+def splitkv_decode_single_launch(args: splitkv_args, kernel: int, stream: int = 0):
+    _check("splitkv_decode_single_launch",
+           load().splitkv_decode_single_launch(ctypes.byref(args), kernel, stream))
 
 
 def splitkv_decode_noalloc(args: splitkv_args, kernel: int, stream: int = 0):

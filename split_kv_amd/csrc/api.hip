@@ -13,7 +13,7 @@
 
 namespace splitkv {
 
-hipError_t launch_gqa_partial(const PartialParams& p, int D, bool fp8, hipStream_t stream);
+hipError_t launch_gqa_partial(const PartialParams& p, int D, bool fp8, bool fused, hipStream_t stream);
 hipError_t launch_mla_partial(const PartialParams& p, bool fp8, hipStream_t stream);
 hipError_t launch_mla_fp8q_partial(const PartialParams& p, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
@@ -64,7 +64,7 @@ enum class Kind { GqaBf16, GqaFp8, Mla };
 struct Layout {
   float* m;
   float* l;
-  uint16_t* o;   // bf16 codes
+  float* o;
 };
 
 Layout workspace_layout(const splitkv_args& a) {
@@ -74,7 +74,7 @@ Layout workspace_layout(const splitkv_args& a) {
   Layout w;
   w.m = a.workspace;
   w.l = a.workspace ? a.workspace + rows : nullptr;
-  w.o = a.workspace ? reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(a.workspace) + ml) : nullptr;
+  w.o = a.workspace ? reinterpret_cast<float*>(reinterpret_cast<char*>(a.workspace) + ml) : nullptr;
   return w;
 }
 
@@ -120,8 +120,8 @@ splitkv_status check_partial(const splitkv_args* a, Kind kind, bool need_ws, con
                   a->page_size);
     if (a->k_stride_page * 2 > INT32_MAX || a->k_stride_tok * 2 > INT32_MAX)
       return fail(SPLITKV_ERR_UNSUPPORTED, "%s: MLA cache strides must fit 31 bits", fn);
-  } else if (a->d_qk != a->d_v || (a->d_qk != 128 && a->d_qk != 256)) {
-    return fail(SPLITKV_ERR_UNSUPPORTED, "%s: head dims d_qk=%d d_v=%d; built for 128 and 256", fn,
+  } else if (a->d_qk != a->d_v || (a->d_qk != 64 && a->d_qk != 128 && a->d_qk != 256)) {
+    return fail(SPLITKV_ERR_UNSUPPORTED, "%s: head dims d_qk=%d d_v=%d; built for 64, 128 and 256", fn,
                 a->d_qk, a->d_v);
   }
   if (!(a->scale > 0.f) || !(a->k_scale > 0.f) || !(a->v_scale > 0.f))
@@ -222,24 +222,27 @@ PartialParams make_partial_params(const splitkv_args& a, Kind kind, int row_bloc
   p.out_f32 = a.out_dtype == SPLITKV_OUT_F32;
   p.lse = a.lse;
   p.debug = a.debug;
+  p.tickets = a.tickets;
   p.direct = direct ? 1 : 0;
   return p;
 }
 
 splitkv_status run_partial(const splitkv_args* a, Kind kind, bool direct, void* stream,
-                           const char* fn) {
+                           const char* fn, bool fused = false) {
   int row_blocks = 0;
   // Direct mode only needs the workspace when some sequence has several splits.
   const bool need_ws = !direct || (a && a->total_slots > a->B);
   splitkv_status st = check_partial(a, kind, need_ws, fn, &row_blocks);
   if (st != SPLITKV_OK) return st;
+  if (fused && need_ws && (!a->tickets || !aligned(a->tickets, 4)))
+    return fail(SPLITKV_ERR_INVALID_ARG, "%s: the single launch needs the tickets array", fn);
   st = check_device(nullptr);
   if (st != SPLITKV_OK) return st;
   const PartialParams p = make_partial_params(*a, kind, row_blocks, direct);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t err;
   if (kind != Kind::Mla)
-    err = launch_gqa_partial(p, a->d_qk, kind == Kind::GqaFp8, s);
+    err = launch_gqa_partial(p, a->d_qk, kind == Kind::GqaFp8, fused, s);
   else if (a->q_dtype == SPLITKV_Q_E4M3)
     err = launch_mla_fp8q_partial(p, s);
   else
@@ -363,6 +366,15 @@ splitkv_status splitkv_decode(const splitkv_args* args, int32_t kernel, void* st
   splitkv_status st = run_partial(args, kind, true, stream, "splitkv_decode");
   if (st != SPLITKV_OK || args->total_slots == args->B) return st;
   return run_combine(args, true, stream, "splitkv_decode");
+}
+
+splitkv_status splitkv_decode_single_launch(const splitkv_args* args, int32_t kernel, void* stream) {
+  const char* fn = "splitkv_decode_single_launch";
+  if (!args) return fail(SPLITKV_ERR_INVALID_ARG, "%s: null args", fn);
+  if (kernel != SPLITKV_KERNEL_GQA)
+    return fail(SPLITKV_ERR_UNSUPPORTED, "%s: built for the grouped-query kernels only", fn);
+  const Kind kind = args->kv_dtype == SPLITKV_KV_E4M3 ? Kind::GqaFp8 : Kind::GqaBf16;
+  return run_partial(args, kind, true, stream, fn, true);
 }
 
 splitkv_status splitkv_decode_noalloc(const splitkv_args* args, int32_t kernel, void* stream) {

@@ -7,8 +7,7 @@
 // gives the right answer ("vLLM 0.30.0 FA4 SplitKV Bug: H100 Decode Can Be 48%
 // Slower", section "Why the result is still correct").  Its cost grows with
 // the split count ("Shipped: 484.5 tok/s on one GB300 ...", section "Why 8
-// splits lost"): it reads S * rows * (2 * d_v + 8) bytes of partials (fp32
-// m and l, bf16 o).
+// splits lost"): it reads S * rows * (d_v + 2) * 4 bytes of partials.
 //
 // A workgroup merges one row's partials over C float4 columns (4C features)
 // with G groups of threads over the splits: thread (g, c) takes splits g,
@@ -28,7 +27,7 @@ namespace splitkv {
 // One thread's share of a row's splits: splits g, g+G, g+2G, ... of the n,
 // U loads in flight per pass, merged into the running (M2, lam, acc) in base 2.
 template <int U>
-__device__ __forceinline__ void merge_splits(const float* part_m, const float* part_l, const uint16_t* po,
+__device__ __forceinline__ void merge_splits(const float* part_m, const float* part_l, const float* po,
                                              int64_t step, int R, int rix, int base, int n, int g, int G,
                                              float& M2, float& lam, f32x4& acc) {
   for (int i0 = g; i0 < n; i0 += U * G) {
@@ -40,9 +39,7 @@ __device__ __forceinline__ void merge_splits(const float* part_m, const float* p
       const int64_t sl = base + (i < n ? i : i0);   // past the end: reread a valid slot, weight 0
       mi[u] = part_m[sl * R + rix];
       li[u] = part_l[sl * R + rix];
-      const u32x2 w = *reinterpret_cast<const u32x2*>(po + sl * step);   // four bf16 codes
-      oi[u] = f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
-                    __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
+      oi[u] = *reinterpret_cast<const f32x4*>(po + sl * step);
       if (i >= n) mi[u] = -INFINITY;
     }
 #pragma unroll
@@ -100,14 +97,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* part_m, const
   const int DV = flags & 0xffff;
   const int c = tid % C, g = tid / C;
   const float* part_l = part_m + SR;
-  const uint16_t* part_o =
-      reinterpret_cast<const uint16_t*>(part_m + (int64_t(2) * SR * 4 + 255) / 256 * 64);
+  const float* part_o = part_m + (int64_t(2) * SR * 4 + 255) / 256 * 64;
 
   // running state in base 2: M2 = max of m_i * log2(e)
   float M2 = -INFINITY, lam = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   const int f0 = 4 * (C * part + c);                  // this thread's first feature
-  const uint16_t* po = part_o + int64_t(rix) * DV + f0;
+  const float* po = part_o + int64_t(rix) * DV + f0;
   const int64_t step = int64_t(R) * DV;
   // loads per thread and pass: just enough for the row's splits (uniform
   // across the workgroup), so no pass issues loads it only masks away
@@ -171,7 +167,7 @@ hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
   const int64_t wgs = int64_t(p.B) * p.R * dsplit;
   const int64_t SR = p.part_l - p.part_m;
   if (wgs > INT32_MAX || SR > INT32_MAX / 8 ||
-      p.part_o != reinterpret_cast<const uint16_t*>(p.part_m + (2 * SR * 4 + 255) / 256 * 64))
+      p.part_o != p.part_m + (2 * SR * 4 + 255) / 256 * 64)
     return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(wgs)), block(unsigned(C * G));
   const int32_t flags = p.d_v | (p.skip_single ? 1 << 16 : 0) | (p.out_f32 ? 1 << 17 : 0) |

@@ -43,11 +43,12 @@ struct PartialParams {
   float v_scale;
   float* part_m;                // [S][T*Hq]
   float* part_l;
-  uint16_t* part_o;             // [S][T*Hq][d_v] bf16 codes
+  float* part_o;                // [S][T*Hq][d_v]
   void* out;
   int32_t out_f32;
   float* lse;
   int32_t* debug;
+  int32_t* tickets;             // single launch: arrival counters per (sequence, KV head, row block)
   int32_t direct;               // single-split sequences write out/lse directly
 };
 
@@ -56,7 +57,7 @@ struct CombineParams {
   const int32_t* slot_offset;
   const float* part_m;
   const float* part_l;
-  const uint16_t* part_o;       // bf16 codes
+  const float* part_o;
   void* out;
   int32_t out_f32;
   float* lse;

@@ -59,10 +59,11 @@ struct GqaRest {
   const int32_t* seq_lens;
   float* part_m;
   float* part_l;
-  uint16_t* part_o;               // bf16 codes
+  float* part_o;
   void* out;
   float* lse;
   int32_t* debug;
+  int32_t* tickets;               // single launch: [B][Hkv][row blocks] arrival counters
   int32_t out_f32, direct;
 };
 
@@ -141,7 +142,7 @@ __device__ __forceinline__ void transpose4x8(const u32x4 (&w)[4], bf16x4 (&op)[8
 template <int D, bool FP8>
 struct GroupRegs {
   bf16x8 k[D / 32];
-  u32x4 v[D / 128][4];
+  u32x4 v[(D + 127) / 128][4];
 };
 
 
@@ -149,18 +150,19 @@ struct GroupRegs {
 
 // Launch geometry packed into one preloaded dword: Hkv (bits 0-15), row
 // blocks (16-23), log2(page size) + 1 (24-31; 0 when not a power of two).
-template <int D, bool FP8>
+template <int D, bool FP8, bool FUSED>
 __global__ __launch_bounds__(256) void gqa_partial_kernel(
     const int32_t* bt, const int32_t* slot_info, const uint16_t* q, const uint8_t* kc,
     const uint8_t* vc, int32_t bt_stride, int32_t geom, GqaRest a) {
   constexpr int NIT = D / 32;           // QK k-iterations
-  constexpr int NC = D / 128;           // V feature chunks of 128 per lane-row
+  constexpr int NC = (D + 127) / 128;   // V feature chunks of 128 per lane-row (D = 64: half of one)
   constexpr int ELEM = FP8 ? 1 : 2;
   constexpr int LDS_STRIDE = D + 4;     // floats; padding against bank conflicts
   constexpr float kRescaleMargin = 8.f; // base-2 growth of a row max before O is rescaled
   __shared__ float sm_o[4][16][LDS_STRIDE];
   __shared__ f32x4 sm_ml[4][16];      // per wave and row: true max, reference max, sum
   __shared__ int sm_dbg[4][3];
+  __shared__ int sm_last;
 
   const int lane = threadIdx.x & 63;
   const int wave = uniform(int(threadIdx.x >> 6));
@@ -179,7 +181,7 @@ __global__ __launch_bounds__(256) void gqa_partial_kernel(
   const int b = work.b, split = work.split, nsplit = work.nsplit, s = work.s, e = work.e;
 
   const int P = a.page_size;
-  const int32_t* bt_row = bt + b * bt_stride;
+  const int32_t* bt_row = bt + int64_t(b) * bt_stride;
   // groups of the range: wave w takes groups w, w+4, w+8, ...
   const int ngroups = (e - s + 15) >> 4;
   const int ngw = ngroups > wave ? (ngroups - wave + 3) >> 2 : 0;
@@ -207,7 +209,7 @@ __global__ __launch_bounds__(256) void gqa_partial_kernel(
   if (a.T > 1) limit = ((cint32*)a.seq_lens)[b] - a.T + t;
   bf16x8 qop[NIT];
   {
-    const uint16_t* qrow = q + int64_t(b) * a.qsb + t * a.qst + (hk * a.g + rc % a.g) * a.qsh;
+    const uint16_t* qrow = q + int64_t(b) * a.qsb + int64_t(t) * a.qst + int64_t(hk * a.g + rc % a.g) * a.qsh;
 #pragma unroll
     for (int it = 0; it < NIT; ++it)
       qop[it] = *reinterpret_cast<const bf16x8*>(qrow + q_chunk_d0<FP8>(it, qg));
@@ -229,9 +231,13 @@ __global__ __launch_bounds__(256) void gqa_partial_kernel(
   // load is a uniform (scalar) base plus one of them, so the loop needs no
   // per-iteration vector address arithmetic.
   const uint32_t koff = uint32_t(n16 * a.kst) + 16u * qg;
+  // lane n16 holds value features 8 n16 .. +7 of each 128; with D = 64 the
+  // lanes past the row read a copy of the first half (their output rows are
+  // never stored)
+  const int vl = D >= 128 ? n16 : (n16 & 7);
   uint32_t voff[4];
 #pragma unroll
-  for (int jt = 0; jt < 4; ++jt) voff[jt] = uint32_t((4 * qg + jt) * a.vst) + uint32_t(ELEM * 8 * n16);
+  for (int jt = 0; jt < 4; ++jt) voff[jt] = uint32_t((4 * qg + jt) * a.vst) + uint32_t(ELEM * 8 * vl);
 
   // Group j of this wave (j < ngw loads; later j only keep the counts static).
   auto load = [&](int j, int64_t pg, GroupRegs<D, FP8>& r) {
@@ -380,7 +386,7 @@ __global__ __launch_bounds__(256) void gqa_partial_kernel(
   l_run = column_sum4(l_run);
   const int nrow = min(16, a.rows - rb * 16);
   // lane (n16, qg) holds O[row n16][128c + 32qg + 8i + e8] in oacc[c*8+e8][i]
-  if (n16 < nrow) {
+  if (n16 < nrow && (D >= 128 || 32 * qg < D)) {
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
@@ -411,10 +417,10 @@ __global__ __launch_bounds__(256) void gqa_partial_kernel(
   // contiguous bytes at a time.
   auto merge = [&](auto rows_c) __attribute__((always_inline)) {
     constexpr int RR = decltype(rows_c)::value;
-    constexpr int TPR = 256 / RR;
+    constexpr int TPR = 256 / RR < D / 4 ? 256 / RR : D / 4;
     constexpr int NQ = D / 4 / TPR;        // float4 columns per thread
     const int t = threadIdx.x;
-    const int row = t / TPR, cl = t % TPR;
+    const int row = t / TPR, cl = t % TPR;   // threads past RR * TPR have row >= RR: no store
     f32x4 mlw[4];
     f32x4 ov[4][NQ];
 #pragma unroll
@@ -446,12 +452,15 @@ __global__ __launch_bounds__(256) void gqa_partial_kernel(
         for (int w = 1; w < 4; ++w) acc += wgt[w] * ov[w][q];
         acc *= mul;
         const int64_t o = obase + 4 * (cl + TPR * q);
-        if (direct && a.out_f32) {
-          *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + o) = acc;
+        if (direct) {
+          if (a.out_f32) {
+            *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + o) = acc;
+          } else {
+            u32x2 pk = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + o) = pk;
+          }
         } else {
-          // the bf16 output, or the partial o (bf16 in the workspace)
-          u32x2 pk = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
-          *reinterpret_cast<u32x2*>((direct ? static_cast<uint16_t*>(a.out) : a.part_o) + o) = pk;
+          *reinterpret_cast<f32x4*>(a.part_o + o) = acc;
         }
       }
       if (cl == 0) {
@@ -487,10 +496,85 @@ __global__ __launch_bounds__(256) void gqa_partial_kernel(
     rec[6] = x;
     rec[7] = int(sum & 0x7fffffffu);
   }
+  if constexpr (FUSED) {
+    if (nsplit > 1) {
+      // Single launch: the workgroups of one (sequence, KV head, row block)
+      // count their arrivals in a ticket; the one that arrives last merges
+      // the group's partials, so no second kernel is launched.  Each
+      // workgroup's partial stores complete before thread 0 releases them at
+      // device scope with the ticket increment (the partials of one group are
+      // written on every XCD, whose L2 caches are not coherent with each
+      // other); the last arriver acquires before it reads them.
+      __builtin_amdgcn_s_waitcnt(0x0F70);            // vmcnt(0): this wave's stores are done
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        int32_t* ctr = a.tickets + (int64_t(b) * Hkv + hk) * RB + rb;
+        const int arrived = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        const int last = arrived == nsplit - 1;
+        if (last) {
+          // every arrival of this call is in: the counter is left at zero for the next call
+          __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        }
+        sm_last = last;
+      }
+      __syncthreads();
+      if (sm_last) {
+        // log-sum-exp merge of the group's nsplit partials (slots slot - split
+        // .. of the sequence), in split order, eight loads in flight per thread;
+        // thread t takes (row, float4 column) pairs t, t + 256, ...
+        const int base = slot - split;
+        constexpr int NCOL = D / 4;
+        const int64_t R = a.R;
+        for (int pr = threadIdx.x; pr < nrow * NCOL; pr += 256) {
+          const int r = pr / NCOL, cq = pr - r * NCOL;
+          const int grow = rb * 16 + r;
+          const int tt = grow / a.g, hh = hk * a.g + grow - tt * a.g;
+          const int64_t rix = int64_t(tt) * a.Hq + hh;
+          float M2 = -INFINITY, lam = 0.f;
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          for (int i0 = 0; i0 < nsplit; i0 += 8) {
+            float mi[8], li[8];
+            f32x4 oi[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+              const int64_t sl = base + min(i0 + u, nsplit - 1);
+              mi[u] = a.part_m[sl * R + rix];
+              li[u] = a.part_l[sl * R + rix];
+              oi[u] = *reinterpret_cast<const f32x4*>(a.part_o + (sl * R + rix) * D + 4 * cq);
+              if (i0 + u >= nsplit) mi[u] = -INFINITY;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+              if (mi[u] == -INFINITY) continue;          // empty split: zero weight
+              const f32x4 ov = oi[u];
+              const float m2 = mi[u] * kLog2e;
+              const float Mn = fmaxf(M2, m2);
+              const float al = fast_exp2(M2 - Mn);
+              const float w = fast_exp2(m2 - Mn);
+              lam = lam * al + w * li[u];
+              acc = acc * al + w * ov;
+              M2 = Mn;
+            }
+          }
+          const bool ok = M2 != -INFINITY && lam > 0.f;
+          acc *= ok ? 1.f / lam : 0.f;
+          const int64_t o = (int64_t(b) * R + rix) * D + 4 * cq;
+          if (a.out_f32) {
+            *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + o) = acc;
+          } else {
+            u32x2 pk = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + o) = pk;
+          }
+          if (a.lse && cq == 0) a.lse[int64_t(b) * R + rix] = ok ? (M2 + log2f(lam)) * kLn2 : -INFINITY;
+        }
+      }
+    }
+  }
 }
 
 // Host launcher: grid = slots x KV heads x row blocks, 256 threads.
-hipError_t launch_gqa_partial(const PartialParams& p, int D, bool fp8, hipStream_t stream) {
+hipError_t launch_gqa_partial(const PartialParams& p, int D, bool fp8, bool fused, hipStream_t stream) {
   GqaRest a;
   a.qsb = int32_t(p.qsb);
   a.qst = int32_t(p.qst);
@@ -516,19 +600,27 @@ hipError_t launch_gqa_partial(const PartialParams& p, int D, bool fp8, hipStream
   a.out = p.out;
   a.lse = p.lse;
   a.debug = p.debug;
+  a.tickets = p.tickets;
   a.out_f32 = p.out_f32;
   a.direct = p.direct;
   const int32_t geom = (p.Hkv & 0xffff) | ((p.row_blocks & 0xff) << 16) | ((p.page_shift + 1) << 24);
   const int32_t bt_stride = int32_t(p.bt_stride);
   const dim3 grid(p.total_wg), block(256);
-#define SPLITKV_LAUNCH(DD, F8)                                                                     \
-  hipLaunchKernelGGL((gqa_partial_kernel<DD, F8>), grid, block, 0, stream, p.bt, p.slot_info, p.q, \
+#define SPLITKV_LAUNCH(DD, F8, FU)                                                                       \
+  hipLaunchKernelGGL((gqa_partial_kernel<DD, F8, FU>), grid, block, 0, stream, p.bt, p.slot_info, p.q, \
                      p.k, p.v, bt_stride, geom, a)
-  if (D == 128 && !fp8) SPLITKV_LAUNCH(128, false);
-  else if (D == 256 && !fp8) SPLITKV_LAUNCH(256, false);
-  else if (D == 128 && fp8) SPLITKV_LAUNCH(128, true);
-  else if (D == 256 && fp8) SPLITKV_LAUNCH(256, true);
+#define SPLITKV_LAUNCH_D(DD)                      \
+  do {                                            \
+    if (!fp8 && !fused) SPLITKV_LAUNCH(DD, false, false); \
+    else if (fp8 && !fused) SPLITKV_LAUNCH(DD, true, false); \
+    else if (!fp8) SPLITKV_LAUNCH(DD, false, true); \
+    else SPLITKV_LAUNCH(DD, true, true);          \
+  } while (0)
+  if (D == 64) SPLITKV_LAUNCH_D(64);
+  else if (D == 128) SPLITKV_LAUNCH_D(128);
+  else if (D == 256) SPLITKV_LAUNCH_D(256);
   else return hipErrorInvalidValue;
+#undef SPLITKV_LAUNCH_D
 #undef SPLITKV_LAUNCH
   return hipGetLastError();
 }

@@ -106,8 +106,7 @@ __device__ __forceinline__ void store_rows(const PartialParams& p, const f32x4 (
         *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + oo) = pk;
       }
     } else {
-      u32x2 pk = {pack_bf16x2(v4[0], v4[1]), pack_bf16x2(v4[2], v4[3])};
-      *reinterpret_cast<u32x2*>(p.part_o + (int64_t(slot) * R + rr) * kDv + d) = pk;
+      *reinterpret_cast<f32x4*>(p.part_o + (int64_t(slot) * R + rr) * kDv + d) = v4;
     }
   }
   if (real && qg == 0 && hf == 0) {

@@ -185,7 +185,7 @@ size_t splitkv_workspace_bytes(int32_t total_slots, int32_t T, int32_t Hq, int32
   const size_t rows = size_t(total_slots) * size_t(T) * size_t(Hq);
   size_t ml = 2 * rows * sizeof(float);
   ml = (ml + 255) / 256 * 256;
-  return ml + rows * size_t(d_v) * sizeof(uint16_t);   // part_o holds bf16
+  return ml + rows * size_t(d_v) * sizeof(float);
 }
 
 splitkv_status splitkv_validate_block_table(const int32_t* bt, const int32_t* seq_lens, int32_t B,

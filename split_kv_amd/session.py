@@ -14,7 +14,8 @@ import numpy as np
 from . import (SPLITKV_KERNEL_GQA, SPLITKV_KERNEL_MLA, SPLITKV_KV_BF16, SPLITKV_KV_E4M3,
                SPLITKV_MAX_SPLITS_LIMIT, SPLITKV_OUT_BF16, SPLITKV_OUT_F32, SPLITKV_Q_BF16, SPLITKV_Q_E4M3,
                SPLITKV_ROWS_PER_WG_GQA, SPLITKV_ROWS_PER_WG_MLA,
-               splitkv_args, splitkv_combine, splitkv_decode, splitkv_decode_noalloc, splitkv_decode_partial,
+               splitkv_args, splitkv_combine, splitkv_decode, splitkv_decode_noalloc,
+               splitkv_decode_partial, splitkv_decode_single_launch,
                splitkv_decode_partial_fp8, splitkv_mla_decode_partial, splitkv_plan,
                splitkv_plan_args, splitkv_workspace_bytes)
 
@@ -87,6 +88,12 @@ class DecodeSession:
         self.total_slots = int(off[-1])
         nbytes = splitkv_workspace_bytes(self.total_slots, s["T"], s["Hq"], s["d_v"])
         self.workspace = torch.empty((nbytes + 3) // 4, dtype=torch.float32, device=dev)
+        # arrival counters of the single-launch step (zero; each call leaves them zero)
+        if not self.mla:
+            rb = -(-((s["Hq"] // s["Hkv"]) * s["T"]) // SPLITKV_ROWS_PER_WG_GQA)
+            self.tickets = torch.zeros((s["B"], s["Hkv"], rb), dtype=torch.int32, device=dev)
+        else:
+            self.tickets = None
         if self.want_debug:
             rows = s["T"] * s["Hq"] if self.mla else (s["Hq"] // s["Hkv"]) * s["T"]
             rpw = SPLITKV_ROWS_PER_WG_MLA if self.mla else SPLITKV_ROWS_PER_WG_GQA
@@ -129,6 +136,7 @@ class DecodeSession:
         ns = self.num_splits_host
         a.uniform_splits = int(ns[0]) if len(ns) and (ns == ns[0]).all() else 0
         a.max_seq_splits = int(ns.max()) if len(ns) else 0
+        a.tickets = self.tickets.data_ptr() if self.tickets is not None else None
         self.args = a
 
     def set_block_table(self, block_table):
@@ -144,6 +152,11 @@ class DecodeSession:
     def decode(self):
         """The whole decode step: partial kernel, then the combine where needed."""
         splitkv_decode(self.args, self.kernel, self._stream())
+        return self.out, self.lse
+
+    def decode_single_launch(self):
+        """The whole grouped-query decode step in one kernel (ticketed last-arriver merge)."""
+        splitkv_decode_single_launch(self.args, self.kernel, self._stream())
         return self.out, self.lse
 
     def decode_noalloc(self):
@@ -165,12 +178,11 @@ class DecodeSession:
         return self.out, self.lse
 
     def partials(self):
-        """Views (part_m [S,T,Hq] fp32, part_l [S,T,Hq] fp32, part_o [S,T,Hq,d_v] bf16) of
-        the workspace."""
+        """Views (part_m [S,T,Hq], part_l [S,T,Hq], part_o [S,T,Hq,d_v]) of the workspace."""
         s = self.shape
         S, T, Hq, dv = self.total_slots, s["T"], s["Hq"], s["d_v"]
         rows = S * T * Hq
         ml = -(-(2 * rows * 4) // 256) * 256 // 4
         w = self.workspace
-        po = w[ml:ml + (rows * dv + 1) // 2].view(self.torch.bfloat16)[:rows * dv]
-        return (w[:rows].view(S, T, Hq), w[rows:2 * rows].view(S, T, Hq), po.view(S, T, Hq, dv))
+        return (w[:rows].view(S, T, Hq), w[rows:2 * rows].view(S, T, Hq),
+                w[ml:ml + rows * dv].view(S, T, Hq, dv))

@@ -80,9 +80,10 @@ def _oplan(lens, T, Hq, Hkv, kernel, req, mx, cus, d_qk=128, d_v=128, kv=sk.SPLI
 
 
 # (d_qk, d_v, kv dtype) per kernel: the configurations the kernels are built for
-HEADS = {sk.SPLITKV_KERNEL_GQA: [(128, 128, sk.SPLITKV_KV_BF16), (256, 256, sk.SPLITKV_KV_BF16),
-                                 (128, 128, sk.SPLITKV_KV_E4M3)],
-         sk.SPLITKV_KERNEL_MLA: [(576, 512, sk.SPLITKV_KV_BF16)]}
+HEADS = {sk.SPLITKV_KERNEL_GQA: [(64, 64, sk.SPLITKV_KV_BF16), (128, 128, sk.SPLITKV_KV_BF16),
+                                 (256, 256, sk.SPLITKV_KV_BF16), (64, 64, sk.SPLITKV_KV_E4M3),
+                                 (128, 128, sk.SPLITKV_KV_E4M3), (256, 256, sk.SPLITKV_KV_E4M3)],
+         sk.SPLITKV_KERNEL_MLA: [(576, 512, sk.SPLITKV_KV_BF16), (576, 512, sk.SPLITKV_KV_E4M3)]}
 
 
 @pytest.mark.parametrize("kernel", [sk.SPLITKV_KERNEL_GQA, sk.SPLITKV_KERNEL_MLA])
@@ -142,7 +143,7 @@ def test_workspace_bytes():
     S, T, Hq, dv = 13, 2, 16, 256
     rows = S * T * Hq
     ml = -(-(2 * rows * 4) // 256) * 256
-    assert sk.splitkv_workspace_bytes(S, T, Hq, dv) == ml + rows * dv * 2     # bf16 part_o
+    assert sk.splitkv_workspace_bytes(S, T, Hq, dv) == ml + rows * dv * 4
 
 
 def test_validate_block_table():
@@ -175,6 +176,7 @@ def _args(**over):
     (dict(q=None), sk.SPLITKV_ERR_INVALID_ARG),
     (dict(Hkv=3), sk.SPLITKV_ERR_INVALID_ARG),
     (dict(d_qk=96, d_v=96), sk.SPLITKV_ERR_UNSUPPORTED),
+    (dict(d_qk=64, d_v=128), sk.SPLITKV_ERR_UNSUPPORTED),
     (dict(page_size=24), sk.SPLITKV_ERR_UNSUPPORTED),
     (dict(q=0x1008), sk.SPLITKV_ERR_UNSUPPORTED),
     (dict(k_stride_tok=100), sk.SPLITKV_ERR_UNSUPPORTED),
@@ -283,7 +285,7 @@ def test_version_string():
 
 
 def test_noalloc_refuses_an_oversized_plan_without_a_device():
-    # 256 MLA slots of 768 rows need ~202 MB of partials, more than the
+    # 256 MLA slots of 768 rows need ~404 MB of partials, more than the
     # library's 64 MiB buffer: refused on the host, before any device call
     lib = _lib()
     a = sk.splitkv_args()
