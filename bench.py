@@ -360,6 +360,21 @@ def measure(case, pool, counts, steps, stream, eager=True, log_prefix=""):
                         partial_batches_us=[round(x, 3) for x in part_batches],
                         partial_workgroups=partial_grid(case, sess),
                         num_splits_host=sess.num_splits_host.copy())
+            if not case.mla:
+                # the whole step as one launch (ticketed last-arriver merge), for comparison;
+                # splitkv_decode takes it by itself only where it measured faster.  Its
+                # merge adds in another order, so its replays are checked against its own
+                # eager step.
+                sess.set_block_table(pool.bts[pool.take(1)[0]])
+                with torch.cuda.stream(stream):
+                    sess.decode_single_launch()
+                torch.cuda.synchronize()
+                ref1 = sess.out.clone()
+
+                def check1():
+                    assert torch.equal(sess.out, ref1), "single-launch replay differs from its eager step"
+                sl_us, _ = timed_graphs(sess, pool, sess.decode_single_launch, steps, stream, check=check1)
+                head["single_launch_us_per_step"] = round(sl_us, 3)
         sweep.append(rec)
         print(f"# {log_prefix}n={n} -> {rec}", file=sys.stderr, flush=True)
         del sess
@@ -464,6 +479,7 @@ def extra_record(name, L, counts, steps, stream, dev):
            "cold_copies": pool.R,
            "auto": {"num_splits": head["num_splits"], "total_slots": head["total_slots"],
                     "us_per_step": head["us_per_step"], "kv_GBps": head["kv_GBps"],
+                    "single_launch_us_per_step": head.get("single_launch_us_per_step"),
                     "pct_hbm_peak": head["pct_hbm_peak"], "plan_host_us": head["plan_host_us"],
                     **step_bytes(case, head["num_splits_host"])},
            "sweep": [{"n_req": r["num_splits_requested"], "n": r["num_splits"], "slots": r["total_slots"],
@@ -648,7 +664,8 @@ def main():
                    "timed_batch_kv_bytes": timed_bytes,
                    "pool_copy_bytes": pool.pool_bytes,
                    **step_bytes(case, head["num_splits_host"]),
-                   "plan_host_us": head["plan_host_us"]},
+                   "plan_host_us": head["plan_host_us"],
+                   "single_launch_us_per_step": head.get("single_launch_us_per_step")},
         "sweep": sweep,
         "monotonic": monotonic(sweep),
         "roofline": roof,

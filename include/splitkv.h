@@ -93,6 +93,7 @@ typedef int32_t splitkv_status;
 #define SPLITKV_ROWS_PER_WG_MLA 64     /* query rows (T*Hq) one MLA workgroup covers */
 #define SPLITKV_DEBUG_INTS 8
 #define SPLITKV_NOALLOC_SCRATCH_BYTES 67108864  /* library-owned partials of splitkv_decode_noalloc, per device */
+#define SPLITKV_SINGLE_LAUNCH_MAX_WORKGROUPS 64  /* splitkv_decode: one launch for grids up to this */
 
 enum { SPLITKV_KV_BF16 = 0, SPLITKV_KV_E4M3 = 1 };
 enum { SPLITKV_KERNEL_GQA = 0, SPLITKV_KERNEL_MLA = 1 };
@@ -139,7 +140,10 @@ typedef struct {
  *   4. each candidate's step is estimated by list scheduling its workgroups,
  *      in launch order (slot by slot, the units of a slot consecutively),
  *      onto num_cus identical compute units, a workgroup costing
- *      ceil(SPLITKV_AUTO_WG_OVERHEAD_BYTES / tb) + (end - start) tokens; the
+ *      ceil(SPLITKV_AUTO_WG_OVERHEAD_BYTES / tb) + (end - start) tokens, plus
+ *      ceil(2 * rw * (d_v + 2) * 4 / tb) tokens when its sequence has more
+ *      than one split: the fp32 partial (m, l, o) of its rw = min(rows_per_wg,
+ *      g*T (MLA: T*Hq)) rows, written and read back by the merge; the
  *      candidate whose busiest unit finishes first wins, A on a tie.
  *
  * Split i of n covers [16*floor(i*nblk/n), min(L, 16*floor((i+1)*nblk/n))).
@@ -266,7 +270,13 @@ splitkv_status splitkv_combine(const splitkv_args* args, void* stream);
  * and `kernel` select, then the combine.  Sequences with a single split
  * write out/lse directly from the partial kernel and are skipped by the
  * combine; when every sequence has one split the combine is not launched.
- * `kernel` is SPLITKV_KERNEL_GQA or SPLITKV_KERNEL_MLA.
+ * `kernel` is SPLITKV_KERNEL_GQA or SPLITKV_KERNEL_MLA.  A grouped-query step
+ * whose args carry tickets runs as one launch (see
+ * splitkv_decode_single_launch) when 1 < max_seq_splits <= 8, a row block's
+ * min(16, g*T) rows hold at most 256 float4 columns (rows x d_v / 4), and
+ * the partial kernel's grid has at most SPLITKV_SINGLE_LAUNCH_MAX_WORKGROUPS
+ * workgroups: there the last arriver merges in one round of loads and the
+ * step measured faster than two kernels.
  */
 splitkv_status splitkv_decode(const splitkv_args* args, int32_t kernel, void* stream);
 

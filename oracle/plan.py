@@ -36,9 +36,12 @@ two are compared bit for bit.
   - Each candidate is scored by greedy list scheduling: its workgroups, in
     launch order (slots in order, the units of a slot one after another),
     each go to whichever of num_cus compute units is free first, costing
-    ceil(AUTO_WG_OVERHEAD_BYTES / tb) + (end - start) tokens; the score is
-    the latest finish.  The balanced candidate is taken only if its score is
-    strictly lower.
+    ceil(AUTO_WG_OVERHEAD_BYTES / tb) + (end - start) tokens, plus, for a
+    sequence with more than one split, ceil(2 * rw * (d_v + 2) * 4 / tb)
+    tokens for the fp32 partial it writes and the merge reads back (rw =
+    min(rows_per_wg, query rows of a KV head: g*T, MLA T*Hq) rows of
+    (m, l, o)); the score is the latest finish.  The balanced candidate is
+    taken only if its score is strictly lower.
 * Split i of n covers [G*floor(i*nblk/n), min(L, G*floor((i+1)*nblk/n))).
   Because n <= nblk every range holds at least one token, the ranges are
   disjoint and contiguous and their union is [0, L).  L == 0 gives one empty
@@ -83,15 +86,16 @@ def clamp_request(L: int, n: int, max_splits: int) -> int:
     return max(1, min(int(n), cap))
 
 
-def _latest_finish(L, ns, units, num_cus, overhead):
+def _latest_finish(L, ns, units, num_cus, overhead, partial):
     """Greedy list scheduling of the plan's workgroups (in launch order) on num_cus units."""
     free = [0] * num_cus
     latest = 0
     for Lb, n in zip(L, ns):
+        extra = partial if n > 1 else 0      # a single split writes the output, no partial
         for i in range(n):
             s, e = split_range(Lb, n, i)
             for _ in range(units):
-                t = heapq.heappop(free) + overhead + (e - s)
+                t = heapq.heappop(free) + overhead + (e - s) + extra
                 latest = max(latest, t)
                 heapq.heappush(free, t)
     return latest
@@ -111,7 +115,9 @@ def _auto_counts(L, *, T, Hq, Hkv, max_splits, num_cus, rows_per_wg, d_qk, d_v, 
     one = [clamp_request(Lb, Lb // c1, max_splits) for Lb in L]
     bal = [clamp_request(Lb, _ceil_div(Lb, cb), max_splits) for Lb in L]
     ov = _ceil_div(AUTO_WG_OVERHEAD_BYTES, tb)
-    if _latest_finish(L, bal, units, num_cus, ov) < _latest_finish(L, one, units, num_cus, ov):
+    rw = min(rows_per_wg, T * Hq if mla else (Hq // Hkv) * T)
+    part = _ceil_div(2 * rw * (d_v + 2) * 4, tb)
+    if _latest_finish(L, bal, units, num_cus, ov, part) < _latest_finish(L, one, units, num_cus, ov, part):
         return bal
     return one
 

@@ -39,6 +39,7 @@ SPLITKV_ROWS_PER_WG_GQA = 16
 SPLITKV_ROWS_PER_WG_MLA = 64
 SPLITKV_DEBUG_INTS = 8
 SPLITKV_NOALLOC_SCRATCH_BYTES = 64 << 20
+SPLITKV_SINGLE_LAUNCH_MAX_WORKGROUPS = 64
 
 SPLITKV_KV_BF16 = 0
 SPLITKV_KV_E4M3 = 1

@@ -1,6 +1,7 @@
 // C ABI of the split-KV decode library: argument checks, the gfx950 gate and
 // dispatch to the kernels.  Every entry point returns a status and records a
 // message instead of asserting; the library allocates nothing.
+#include <algorithm>
 #include <cstring>
 #include <mutex>
 
@@ -363,6 +364,21 @@ splitkv_status splitkv_decode(const splitkv_args* args, int32_t kernel, void* st
   if (kernel == SPLITKV_KERNEL_MLA) kind = Kind::Mla;
   else if (kernel == SPLITKV_KERNEL_GQA) kind = args->kv_dtype == SPLITKV_KV_E4M3 ? Kind::GqaFp8 : Kind::GqaBf16;
   else return fail(SPLITKV_ERR_INVALID_ARG, "splitkv_decode: unknown kernel %d", kernel);
+  // The single launch (ticketed last-arriver merge) replaces the merge kernel
+  // for small steps: a grid of a few workgroups whose groups the last arriver
+  // merges in one round of loads (one float4 column of one row per thread,
+  // at most eight splits).  It measured faster than two kernels only there: a
+  // larger group is merged by one workgroup far more slowly than by the merge
+  // kernel's whole grid, and on a full grid every workgroup's device-scope
+  // release costs more than the second launch saves.
+  if (kind != Kind::Mla && args->tickets && args->max_seq_splits > 1 && args->Hkv > 0 && args->T > 0 &&
+      args->total_slots > args->B && args->max_seq_splits <= 8) {
+    const int64_t rw = std::min<int64_t>(SPLITKV_ROWS_PER_WG_GQA, int64_t(args->Hq / args->Hkv) * args->T);
+    const int64_t wgs = int64_t(args->total_slots) * args->Hkv *
+                        ceil_div(int64_t(args->Hq / args->Hkv) * args->T, SPLITKV_ROWS_PER_WG_GQA);
+    if (rw * (args->d_v / 4) <= 256 && wgs <= SPLITKV_SINGLE_LAUNCH_MAX_WORKGROUPS)
+      return run_partial(args, kind, true, stream, "splitkv_decode", true);
+  }
   splitkv_status st = run_partial(args, kind, true, stream, "splitkv_decode");
   if (st != SPLITKV_OK || args->total_slots == args->B) return st;
   return run_combine(args, true, stream, "splitkv_decode");

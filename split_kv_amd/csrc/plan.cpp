@@ -54,9 +54,11 @@ static int64_t isqrt64(int64_t x) {
 // Finish time of the busiest compute unit when the plan's workgroups are
 // handed out in launch order (slot by slot, the units of a slot one after
 // another), each to the unit that becomes free first; a workgroup costs
-// `overhead` plus its range length, in tokens.
+// `overhead` plus its range length, in tokens, plus `partial` when its
+// sequence has several splits (its fp32 partial, written and read back by the
+// merge; a single split writes the output directly).
 static int64_t list_schedule(const int32_t* seq_lens, const std::vector<int32_t>& ns,
-                             int64_t units, int32_t num_cus, int64_t overhead) {
+                             int64_t units, int32_t num_cus, int64_t overhead, int64_t partial) {
   std::priority_queue<int64_t, std::vector<int64_t>, std::greater<int64_t>> free_at;
   for (int32_t c = 0; c < num_cus; ++c) free_at.push(0);
   int64_t busiest = 0;
@@ -65,7 +67,7 @@ static int64_t list_schedule(const int32_t* seq_lens, const std::vector<int32_t>
       int64_t s, e;
       split_range(seq_lens[b], ns[b], i, &s, &e);
       for (int64_t u = 0; u < units; ++u) {
-        const int64_t t = free_at.top() + overhead + (e - s);
+        const int64_t t = free_at.top() + overhead + (e - s) + (ns[b] > 1 ? partial : 0);
         free_at.pop();
         free_at.push(t);
         busiest = std::max(busiest, t);
@@ -101,8 +103,13 @@ static void auto_splits(const splitkv_plan_args& a, int32_t num_cus, const int32
     bal[b] = clamp_request(L, ceil_div(L, c_bal), a.max_splits);
   }
   const int64_t overhead = ceil_div(int64_t(SPLITKV_AUTO_WG_OVERHEAD_BYTES), tb);
-  const bool take_bal = list_schedule(seq_lens, bal, units, num_cus, overhead) <
-                        list_schedule(seq_lens, one, units, num_cus, overhead);
+  // rows of (m, l, o) one workgroup writes, and the bytes of that partial
+  // written and read back, in tokens of streaming
+  const int64_t rows = a.kernel == SPLITKV_KERNEL_MLA ? int64_t(a.T) * a.Hq : int64_t(a.Hq / a.Hkv) * a.T;
+  const int64_t rw = std::min(rows_per_wg, rows);
+  const int64_t partial = ceil_div(2 * rw * (int64_t(a.d_v) + 2) * 4, tb);
+  const bool take_bal = list_schedule(seq_lens, bal, units, num_cus, overhead, partial) <
+                        list_schedule(seq_lens, one, units, num_cus, overhead, partial);
   std::copy((take_bal ? bal : one).begin(), (take_bal ? bal : one).end(), num_splits);
 }
 

@@ -38,6 +38,7 @@ def _check_full(case, sess, tag):
 def _check_rows(case, sess, rows, tag):
     import torch
     torch.cuda.synchronize()
+    rows = list(dict.fromkeys(tuple(r) for r in rows))     # each sampled row once
     O, L = oracle.attend(case, select=rows)
     out = to_np(sess.out)
     lse = to_np(sess.lse)
@@ -387,7 +388,10 @@ def test_fp8_full_size_sampled():
     sess, _ = session_for(case, requested_splits=0)
     log(f"  plan: splits {sess.num_splits_host.tolist()}")
     sess.decode()
-    rows = [(b, 0, h) for b in (0, 3, 7) for h in (0, 9, 31)]
+    # every (sequence, KV head) pair, each with a query head of its own group
+    rng = np.random.default_rng(3)
+    rows = [(b, 0, hk * case.g + int(rng.integers(case.g))) for b in range(case.B) for hk in range(case.Hkv)]
+    rows += [(b, 0, h) for b in (0, 3, 7) for h in (0, 9, 31)]
     _check_rows(case, sess, rows, "fp8 full")
 
 
@@ -399,6 +403,8 @@ def test_mla_full_size_sampled(n):
     sess, _ = session_for(case, requested_splits=n, max_splits=256)
     sess.decode()
     rows = [(0, t, h) for t in (0, 5) for h in (0, 77, 127)] + [(0, 3, 64)]
+    # one row in each of the twelve 64-row blocks (row = t * 128 + h)
+    rows += [(0, r // 128, r % 128) for r in range(7, 768, 64)]
     _check_rows(case, sess, rows, f"mla full n={n}")
 
 
@@ -412,6 +418,10 @@ def test_ragged_full_size_sampled():
     _check_debug(case, sess, case.Hkv, 1)
     bmax = int(np.argmax(case.seq_lens))
     rows = [(b, 0, h) for b in (0, 2, 4, bmax) for h in (0, 13, 31)]
+    # every KV head of the longest sequence and of the three shortest
+    order = np.argsort(case.seq_lens, kind="stable")
+    for b in [bmax] + [int(x) for x in order[:3]]:
+        rows += [(b, 0, hk * case.g + (b + hk) % case.g) for hk in range(case.Hkv)]
     _check_rows(case, sess, rows, "ragged full")
 
 

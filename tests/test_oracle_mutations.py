@@ -155,3 +155,10 @@ def test_unquantised_queries_are_caught(monkeypatch):
     monkeypatch.setattr(TQ, "dequant_q", bad)
     _fails(TQ.test_queries_go_to_the_nearest_code)
     _fails(TQ.test_queries_saturate_at_448_scales)
+
+
+def test_dropped_partial_term_is_caught(monkeypatch):
+    # the auto planner's schedule without the cost of the fp32 partials
+    orig = P._latest_finish
+    monkeypatch.setattr(P, "_latest_finish", lambda L, ns, u, c, ov, part: orig(L, ns, u, c, ov, 0))
+    _fails(TP.test_auto_plan_worked_examples)

@@ -100,8 +100,10 @@ def test_auto_plan_worked_examples():
     # Few-KV-head decode at L=5900, D=256 bf16 (tb = 1024, overhead 32 tokens):
     # c_lat = isqrt(8850) = 94 (94^2 = 8836); W = 11800 -> c = 94 for both.
     # one round: floor(5900/94) = 62 splits, ranges of 5 or 6 granules -> the
-    # longest workgroup costs 96 + 32 = 128; balanced: ceil(5900/94) = 63
-    # splits, also at most 6 granules -> 128.  A tie keeps one round.
+    # longest workgroup costs 96 + 32 + 17 = 145 (the partial term: 8 rows of
+    # (2 + 256) fp32 written and read, ceil(16512 / 1024) = 17); balanced:
+    # ceil(5900/94) = 63 splits, also at most 6 granules -> 145.  A tie keeps
+    # one round.
     assert _auto([5900]) == [62]
     # Eight e4m3 sequences of 32000, Hq=32, Hkv=4, D=128 (tb = 256, overhead
     # 128): units = 4, W = 1024000, c_lat = isqrt(48000) = 219.  One round:
@@ -120,6 +122,18 @@ def test_auto_plan_worked_examples():
     # c = ceil(7496/16) = 469 -> [9, 7, 1, 1], 18 workgroups costing 8648 in
     # total, none above 528, so list scheduling ends by 8648/4 + 528 < 3064.
     assert _auto([4096, 3000, 200, 200], Hq=1, Hkv=1, d=(128, 128), cus=4) == [9, 7, 1, 1]
+    # The partial term: an MLA-shaped sequence (T=6, 128 heads -> 12 row
+    # blocks; tb = 1152 B, overhead ceil(32768/1152) = 29 tokens) of 2048
+    # tokens on 8 units.  Each workgroup of a split sequence also pays
+    # ceil(2 * 64 * 514 * 4 / 1152) = 229 tokens for its fp32 partial written
+    # and read back.  One round: c = 24576 / 8 = 3072 > 2048 -> 1 split, 12
+    # workgroups of 29 + 2048 = 2077 -> two rounds end at 4154.  Balanced:
+    # c = 768 -> 3 splits of 672, 688, 688 tokens, 36 workgroups costing
+    # 930, 946, 946 -> 33864 in total, so no schedule on 8 units ends before
+    # 4233 > 4154: one round (no split) wins.  Without the partial term the
+    # same 36 workgroups total 25368 and would end near 3171, and the
+    # balanced plan would win.
+    assert _auto([2048], T=6, Hq=128, Hkv=1, d=(576, 512), rpw=64, cus=8) == [1]
     # max_splits caps the count; nblk caps short sequences
     assert _auto([5900], mx=16) == [16]
     assert _auto([0, 0]) == [1, 1]
