@@ -124,27 +124,30 @@ typedef struct {
  * ...", section "Why 8 splits lost").  With cap_b = min(max_splits,
  * max(nblk_b, 1)), units = Hkv * ceil(g*T / rows_per_wg) workgroups per split,
  * tb = bytes one workgroup streams per token ((d_qk + d_v) * elem for GQA,
- * d_qk * elem for MLA, whose V is the first d_v features of the same row;
- * elem = 2 for bf16, 1 for e4m3) and L_max the longest sequence:
+ * elem = 2 for bf16, 1 for e4m3; d_qk * 2 for MLA whatever the cache dtype:
+ * V is the first d_v features of the same row, and a token costs the matrix
+ * work on bf16 operands) and L_max the longest sequence:
  *   1. if L_max * tb < SPLITKV_AUTO_SPLIT_MIN_BYTES no sequence is split
  *      (the merge launch would cost more than it saves);
  *   2. c_lat = max(16, isqrt(L_max * SPLITKV_AUTO_LAT_NUM / SPLITKV_AUTO_LAT_DEN)),
  *      the tokens per split below which the merge of more partials costs
  *      more than the shorter split saves;  W = units * sum_b L_b;
- *   3. candidate A, one round: c = max(c_lat, ceil(W / num_cus)),
- *      n_b = clamp(floor(L_b / c), 1, cap_b) -- at most one workgroup per
+ *   3. candidate A, one round: c1 = max(c_lat, ceil(W / num_cus)),
+ *      n_b = clamp(floor(L_b / c1), 1, cap_b) -- at most one workgroup per
  *      compute unit when the batch allows it;
  *      candidate B, balanced: c = max(c_lat, ceil(W / (SPLITKV_AUTO_BALANCE *
  *      num_cus))), n_b = clamp(ceil(L_b / c), 1, cap_b) -- no workgroup
  *      longer than c, for batches of unequal lengths;
+ *      candidates C and D, fewer splits: as A with c = ceil(4 * c1 / 3) and
+ *      with c = 2 * c1;
  *   4. each candidate's step is estimated by list scheduling its workgroups,
  *      in launch order (slot by slot, the units of a slot consecutively),
  *      onto num_cus identical compute units, a workgroup costing
  *      ceil(SPLITKV_AUTO_WG_OVERHEAD_BYTES / tb) + (end - start) tokens, plus
- *      ceil(2 * rw * (d_v + 2) * 4 / tb) tokens when its sequence has more
- *      than one split: the fp32 partial (m, l, o) of its rw = min(rows_per_wg,
- *      g*T (MLA: T*Hq)) rows, written and read back by the merge; the
- *      candidate whose busiest unit finishes first wins, A on a tie.
+ *      the merge: ceil(Pb / (num_cus * tb)) tokens, Pb = 2 * sum over the
+ *      sequences with n_b > 1 of n_b * T * Hq * (d_v + 2) * 4, the fp32
+ *      partials written and read back, spread over every compute unit; the
+ *      lowest estimate wins, the earlier of A, B, C, D on a tie.
  *
  * Split i of n covers [16*floor(i*nblk/n), min(L, 16*floor((i+1)*nblk/n))).
  * L == 0 gives one empty split.

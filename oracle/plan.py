@@ -23,25 +23,29 @@ two are compared bit for bit.
   n_eff = clamp(n, 1, min(max_splits, max(nblk, 1))).
 * Auto mode (n == 0) weighs more splits against the merge they add and the
   start-up latency of every extra workgroup.  Per token a workgroup streams
-  tb = (d_qk + d_v) * elem bytes (MLA: d_qk * elem, V being part of the same
-  row); a split of a sequence is units = Hkv * ceil(g*T / rows_per_wg)
+  tb = (d_qk + d_v) * elem bytes; MLA counts tb = d_qk * 2 whatever the cache
+  dtype (V is part of the same row, and its cost per token is the matrix
+  work on bf16 operands, the same for an e4m3 cache); a split of a sequence is
+  units = Hkv * ceil(g*T / rows_per_wg)
   workgroups; cap_b = min(max_splits, max(nblk_b, 1)); L_max = max_b L_b.
   - If L_max * tb < AUTO_SPLIT_MIN_BYTES, every n_b = 1 (nothing to merge).
   - Latency floor c_lat = max(G, isqrt(L_max * AUTO_LAT_NUM // AUTO_LAT_DEN))
     tokens per split; W = units * sum_b L_b.
-  - Candidate "one round": c = max(c_lat, ceil(W / num_cus)),
-    n_b = clamp(floor(L_b / c), 1, cap_b).
+  - Candidate "one round": c1 = max(c_lat, ceil(W / num_cus)),
+    n_b = clamp(floor(L_b / c1), 1, cap_b).
   - Candidate "balanced": c = max(c_lat, ceil(W / (AUTO_BALANCE * num_cus))),
     n_b = clamp(ceil(L_b / c), 1, cap_b).
-  - Each candidate is scored by greedy list scheduling: its workgroups, in
-    launch order (slots in order, the units of a slot one after another),
-    each go to whichever of num_cus compute units is free first, costing
-    ceil(AUTO_WG_OVERHEAD_BYTES / tb) + (end - start) tokens, plus, for a
-    sequence with more than one split, ceil(2 * rw * (d_v + 2) * 4 / tb)
-    tokens for the fp32 partial it writes and the merge reads back (rw =
-    min(rows_per_wg, query rows of a KV head: g*T, MLA T*Hq) rows of
-    (m, l, o)); the score is the latest finish.  The balanced candidate is
-    taken only if its score is strictly lower.
+  - Candidates "fewer splits": one round with c = ceil(4 * c1 / 3) and with
+    c = 2 * c1 (floor as in one round).
+  - Each candidate is scored by greedy list scheduling plus its merge: its
+    workgroups, in launch order (slots in order, the units of a slot one
+    after another), each go to whichever of num_cus compute units is free
+    first, costing ceil(AUTO_WG_OVERHEAD_BYTES / tb) + (end - start) tokens;
+    to the latest finish is added ceil(Pb / (num_cus * tb)) tokens, Pb =
+    2 * sum over sequences with n_b > 1 of n_b * T * Hq * (d_v + 2) * 4, the
+    fp32 partials written and read back by the merge, spread over every
+    compute unit.  The lowest score wins; on a tie the earlier candidate in
+    the order one round, balanced, 4/3, 2.
 * Split i of n covers [G*floor(i*nblk/n), min(L, G*floor((i+1)*nblk/n))).
   Because n <= nblk every range holds at least one token, the ranges are
   disjoint and contiguous and their union is [0, L).  L == 0 gives one empty
@@ -86,24 +90,30 @@ def clamp_request(L: int, n: int, max_splits: int) -> int:
     return max(1, min(int(n), cap))
 
 
-def _latest_finish(L, ns, units, num_cus, overhead, partial):
+def _latest_finish(L, ns, units, num_cus, overhead):
     """Greedy list scheduling of the plan's workgroups (in launch order) on num_cus units."""
     free = [0] * num_cus
     latest = 0
     for Lb, n in zip(L, ns):
-        extra = partial if n > 1 else 0      # a single split writes the output, no partial
         for i in range(n):
             s, e = split_range(Lb, n, i)
             for _ in range(units):
-                t = heapq.heappop(free) + overhead + (e - s) + extra
+                t = heapq.heappop(free) + overhead + (e - s)
                 latest = max(latest, t)
                 heapq.heappush(free, t)
     return latest
 
 
+def _merge_tokens(ns, T, Hq, d_v, num_cus, tb):
+    """The fp32 partials a plan writes and the merge reads back, in tokens of
+    streaming spread over every compute unit (single-split sequences have none)."""
+    pb = 2 * sum(n for n in ns if n > 1) * T * Hq * (d_v + 2) * 4
+    return _ceil_div(pb, num_cus * tb)
+
+
 def _auto_counts(L, *, T, Hq, Hkv, max_splits, num_cus, rows_per_wg, d_qk, d_v, elem):
     mla = rows_per_wg == ROWS_PER_WG_MLA
-    tb = (d_qk if mla else d_qk + d_v) * elem
+    tb = d_qk * 2 if mla else (d_qk + d_v) * elem
     units = Hkv * _ceil_div((Hq // Hkv) * T, rows_per_wg)
     lmax = max(L)
     if lmax * tb < AUTO_SPLIT_MIN_BYTES:
@@ -114,12 +124,16 @@ def _auto_counts(L, *, T, Hq, Hkv, max_splits, num_cus, rows_per_wg, d_qk, d_v, 
     cb = max(c_lat, _ceil_div(W, AUTO_BALANCE * num_cus))
     one = [clamp_request(Lb, Lb // c1, max_splits) for Lb in L]
     bal = [clamp_request(Lb, _ceil_div(Lb, cb), max_splits) for Lb in L]
+    c43 = _ceil_div(4 * c1, 3)
+    few = [clamp_request(Lb, Lb // c43, max_splits) for Lb in L]
+    half = [clamp_request(Lb, Lb // (2 * c1), max_splits) for Lb in L]
     ov = _ceil_div(AUTO_WG_OVERHEAD_BYTES, tb)
-    rw = min(rows_per_wg, T * Hq if mla else (Hq // Hkv) * T)
-    part = _ceil_div(2 * rw * (d_v + 2) * 4, tb)
-    if _latest_finish(L, bal, units, num_cus, ov, part) < _latest_finish(L, one, units, num_cus, ov, part):
-        return bal
-    return one
+    best, best_score = None, None
+    for ns in (one, bal, few, half):
+        score = _latest_finish(L, ns, units, num_cus, ov) + _merge_tokens(ns, T, Hq, d_v, num_cus, tb)
+        if best_score is None or score < best_score:
+            best, best_score = ns, score
+    return best
 
 
 def make_plan(seq_lens, *, T: int, Hq: int, Hkv: int, requested: int, max_splits: int,

@@ -54,11 +54,9 @@ static int64_t isqrt64(int64_t x) {
 // Finish time of the busiest compute unit when the plan's workgroups are
 // handed out in launch order (slot by slot, the units of a slot one after
 // another), each to the unit that becomes free first; a workgroup costs
-// `overhead` plus its range length, in tokens, plus `partial` when its
-// sequence has several splits (its fp32 partial, written and read back by the
-// merge; a single split writes the output directly).
+// `overhead` plus its range length, in tokens.
 static int64_t list_schedule(const int32_t* seq_lens, const std::vector<int32_t>& ns,
-                             int64_t units, int32_t num_cus, int64_t overhead, int64_t partial) {
+                             int64_t units, int32_t num_cus, int64_t overhead) {
   std::priority_queue<int64_t, std::vector<int64_t>, std::greater<int64_t>> free_at;
   for (int32_t c = 0; c < num_cus; ++c) free_at.push(0);
   int64_t busiest = 0;
@@ -67,7 +65,7 @@ static int64_t list_schedule(const int32_t* seq_lens, const std::vector<int32_t>
       int64_t s, e;
       split_range(seq_lens[b], ns[b], i, &s, &e);
       for (int64_t u = 0; u < units; ++u) {
-        const int64_t t = free_at.top() + overhead + (e - s) + (ns[b] > 1 ? partial : 0);
+        const int64_t t = free_at.top() + overhead + (e - s);
         free_at.pop();
         free_at.push(t);
         busiest = std::max(busiest, t);
@@ -76,14 +74,26 @@ static int64_t list_schedule(const int32_t* seq_lens, const std::vector<int32_t>
   return busiest;
 }
 
+// The fp32 partials a plan writes and the merge reads back, in tokens of
+// streaming spread over every compute unit (a single split writes the output
+// directly and has none).
+static int64_t merge_tokens(const std::vector<int32_t>& ns, int64_t T, int64_t Hq, int64_t d_v,
+                            int32_t num_cus, int64_t tb) {
+  int64_t slots = 0;
+  for (int32_t n : ns)
+    if (n > 1) slots += n;
+  return ceil_div(2 * slots * T * Hq * (d_v + 2) * 4, int64_t(num_cus) * tb);
+}
+
 // Auto split counts (the rule documented at splitkv_plan).
 static void auto_splits(const splitkv_plan_args& a, int32_t num_cus, const int32_t* seq_lens,
                         int32_t* num_splits) {
-  const int64_t rows_per_wg =
-      a.kernel == SPLITKV_KERNEL_MLA ? SPLITKV_ROWS_PER_WG_MLA : SPLITKV_ROWS_PER_WG_GQA;
+  const bool mla = a.kernel == SPLITKV_KERNEL_MLA;
+  const int64_t rows_per_wg = mla ? SPLITKV_ROWS_PER_WG_MLA : SPLITKV_ROWS_PER_WG_GQA;
   const int64_t units = int64_t(a.Hkv) * ceil_div(int64_t(a.Hq / a.Hkv) * a.T, rows_per_wg);
   const int64_t elem = a.kv_dtype == SPLITKV_KV_E4M3 ? 1 : 2;
-  const int64_t tb = (a.kernel == SPLITKV_KERNEL_MLA ? int64_t(a.d_qk) : int64_t(a.d_qk) + a.d_v) * elem;
+  // MLA: the cost of a token is the matrix work on bf16 operands, whatever the cache dtype
+  const int64_t tb = mla ? int64_t(a.d_qk) * 2 : (int64_t(a.d_qk) + a.d_v) * elem;
   int64_t lmax = 0, sum_len = 0;
   for (int32_t b = 0; b < a.B; ++b) {
     lmax = std::max<int64_t>(lmax, seq_lens[b]);
@@ -96,21 +106,28 @@ static void auto_splits(const splitkv_plan_args& a, int32_t num_cus, const int32
   const int64_t work = sum_len > (INT64_MAX / 4) / units ? INT64_MAX / 4 : sum_len * units;
   const int64_t c_one = std::max(c_lat, ceil_div(work, int64_t(num_cus)));
   const int64_t c_bal = std::max(c_lat, ceil_div(work, int64_t(SPLITKV_AUTO_BALANCE) * num_cus));
-  std::vector<int32_t> one(a.B), bal(a.B);
+  const int64_t c_43 = ceil_div(4 * c_one, 3);
+  // candidates in tie-break order: one round, balanced, one round at 4/3 and at 2x the chunk
+  std::vector<std::vector<int32_t>> cand(4, std::vector<int32_t>(a.B));
   for (int32_t b = 0; b < a.B; ++b) {
     const int64_t L = seq_lens[b];
-    one[b] = clamp_request(L, L / c_one, a.max_splits);
-    bal[b] = clamp_request(L, ceil_div(L, c_bal), a.max_splits);
+    cand[0][b] = clamp_request(L, L / c_one, a.max_splits);
+    cand[1][b] = clamp_request(L, ceil_div(L, c_bal), a.max_splits);
+    cand[2][b] = clamp_request(L, L / c_43, a.max_splits);
+    cand[3][b] = clamp_request(L, L / (2 * c_one), a.max_splits);
   }
   const int64_t overhead = ceil_div(int64_t(SPLITKV_AUTO_WG_OVERHEAD_BYTES), tb);
-  // rows of (m, l, o) one workgroup writes, and the bytes of that partial
-  // written and read back, in tokens of streaming
-  const int64_t rows = a.kernel == SPLITKV_KERNEL_MLA ? int64_t(a.T) * a.Hq : int64_t(a.Hq / a.Hkv) * a.T;
-  const int64_t rw = std::min(rows_per_wg, rows);
-  const int64_t partial = ceil_div(2 * rw * (int64_t(a.d_v) + 2) * 4, tb);
-  const bool take_bal = list_schedule(seq_lens, bal, units, num_cus, overhead, partial) <
-                        list_schedule(seq_lens, one, units, num_cus, overhead, partial);
-  std::copy((take_bal ? bal : one).begin(), (take_bal ? bal : one).end(), num_splits);
+  size_t best = 0;
+  int64_t best_score = INT64_MAX;
+  for (size_t k = 0; k < cand.size(); ++k) {
+    const int64_t score = list_schedule(seq_lens, cand[k], units, num_cus, overhead) +
+                          merge_tokens(cand[k], a.T, a.Hq, a.d_v, num_cus, tb);
+    if (score < best_score) {
+      best = k;
+      best_score = score;
+    }
+  }
+  std::copy(cand[best].begin(), cand[best].end(), num_splits);
 }
 
 splitkv_status plan_host(const splitkv_plan_args& a, int32_t num_cus, const int32_t* seq_lens,

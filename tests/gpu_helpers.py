@@ -45,7 +45,7 @@ def guard_buffers(sess):
     """Move the session's output-side buffers into guarded allocations."""
     import torch
     sess._guards = []
-    for name in ("out", "lse", "workspace", "tickets", "debug"):
+    for name in ("out", "lse", "workspace", "workspace_alt", "tickets", "debug"):
         t = getattr(sess, name, None)
         if t is None:
             continue

@@ -157,8 +157,7 @@ def test_unquantised_queries_are_caught(monkeypatch):
     _fails(TQ.test_queries_saturate_at_448_scales)
 
 
-def test_dropped_partial_term_is_caught(monkeypatch):
-    # the auto planner's schedule without the cost of the fp32 partials
-    orig = P._latest_finish
-    monkeypatch.setattr(P, "_latest_finish", lambda L, ns, u, c, ov, part: orig(L, ns, u, c, ov, 0))
+def test_dropped_merge_term_is_caught(monkeypatch):
+    # the auto planner's estimate without the cost of the fp32 partials
+    monkeypatch.setattr(P, "_merge_tokens", lambda ns, T, Hq, d_v, cus, tb: 0)
     _fails(TP.test_auto_plan_worked_examples)

@@ -93,46 +93,58 @@ def test_auto_plan_worked_examples():
     # Below the byte threshold nothing is split: D=128 bf16 reads tb = 512 B per
     # token, and 383 * 512 = 196096 < 196608 <= 384 * 512.
     assert _auto([383], Hq=8, d=(128, 128)) == [1]
-    # L=384: c_lat = max(16, isqrt(576)) = 24, W = 384 * 2 = 768, so both
-    # candidates use c = 24: floor(384/24) = ceil(384/24) = 16 splits.
-    assert _auto([384], Hq=8, d=(128, 128)) == [16]
+    # L=384 (units 2, overhead 64): c_lat = max(16, isqrt(576)) = 24, W = 768.
+    # One round and balanced: c = 24, 16 splits of 1-2 granules -> 64 + 32 =
+    # 96, plus the merge: 2 * 16 * 8 rows * 130 * 4 B = 133120 B over 256 units
+    # of 512 B tokens -> 2, score 98.  Fewer splits (c = 32): 12 splits of two
+    # granules -> 96 + 1 (99840 B) = 97, the lowest.  Half (c = 48): 8 splits
+    # of three granules -> 112 + 1.
+    assert _auto([384], Hq=8, d=(128, 128)) == [12]
     assert _auto([256], Hq=8, d=(128, 128)) == [1]          # the tiny decode shape
     # Few-KV-head decode at L=5900, D=256 bf16 (tb = 1024, overhead 32 tokens):
-    # c_lat = isqrt(8850) = 94 (94^2 = 8836); W = 11800 -> c = 94 for both.
+    # c_lat = isqrt(8850) = 94 (94^2 = 8836); W = 11800 -> c1 = 94.
     # one round: floor(5900/94) = 62 splits, ranges of 5 or 6 granules -> the
-    # longest workgroup costs 96 + 32 + 17 = 145 (the partial term: 8 rows of
-    # (2 + 256) fp32 written and read, ceil(16512 / 1024) = 17); balanced:
-    # ceil(5900/94) = 63 splits, also at most 6 granules -> 145.  A tie keeps
-    # one round.
+    # longest workgroup costs 96 + 32 = 128, plus the merge of 62 partials of
+    # 16 rows x 258 fp32 written and read, 2047488 B over 256 x 1024 -> 8:
+    # 136; balanced: 63 splits, also at most 6 granules -> 128 + 8 = 136 (a
+    # tie keeps one round); 4/3 (c = 126): 46 splits of up to 9 granules ->
+    # 176 + 6; half (c = 188): 31 splits -> 224 + 4.
     assert _auto([5900]) == [62]
     # Eight e4m3 sequences of 32000, Hq=32, Hkv=4, D=128 (tb = 256, overhead
     # 128): units = 4, W = 1024000, c_lat = isqrt(48000) = 219.  One round:
-    # c = 4000 -> 8 splits, 256 workgroups of 4000 tokens -> 4128.  Balanced:
-    # c = 1000 -> 32 splits, 1024 workgroups of ~1000 tokens on 256 units ->
-    # four each, ~4512.  One round wins.
+    # c = 4000 -> 8 splits, 256 workgroups of 4000 tokens -> 4128 + merge 33.
+    # Balanced: c = 1000 -> 32 splits, 1024 workgroups of ~1000 tokens on 256
+    # units -> four each, ~4512 + 130.  4/3 and half: 5 and 4 splits, single
+    # workgroups of 6400 and 8000 tokens.  One round wins.
     assert _auto([32000] * 8, Hq=32, Hkv=4, d=(128, 128), elem=1) == [8] * 8
     # MLA decode at L=65536 (T=6, 128 heads -> units = 12, tb = 1152):
     # c_lat = isqrt(98304) = 313; one round: c = 786432/256 = 3072 -> 21
-    # splits, 252 workgroups; balanced: c = 768 -> 86 splits, 1032 workgroups,
-    # about four per unit.  One round wins.
+    # splits, 252 workgroups of up to 3136 tokens -> 3165 + merge 225 (21
+    # slots x 768 rows x 514 fp32 written and read, over 256 x 1152 B);
+    # balanced: c = 768 -> 86 splits, 1032 workgroups, about four per unit;
+    # 4/3: 16 splits of 4096 -> 4125 + 171.  One round wins.
     assert _auto([65536], T=6, Hq=128, Hkv=1, d=(576, 512), rpw=64) == [21]
+    # The same at L=2048, where the merge decides: one round, c = 96 -> 21
+    # splits of 96-112 tokens -> 141 + 225 = 366; 4/3, c = 128 -> 16 splits of
+    # 128 -> 157 + 172 = 329; half, c = 192 -> 10 splits of up to 208 -> 237 +
+    # 108 = 345; balanced, c = 55 -> 38 splits, 456 workgroups in two rounds.
+    # An e4m3 cache counts the same tb: a token costs the matrix work.
+    assert _auto([2048], T=6, Hq=128, Hkv=1, d=(576, 512), rpw=64) == [16]
+    assert _auto([2048], T=6, Hq=128, Hkv=1, d=(576, 512), rpw=64, elem=1) == [16]
     # Unequal lengths on 4 units (Hq = Hkv = 1 -> units = 1; D=128 bf16, overhead
     # 64): lens 4096, 3000, 200, 200, W = 7496, c_lat = 78.  One round: c = 1874
     # -> [2, 1, 1, 1]; the 3000-token workgroup alone costs 3064.  Balanced:
     # c = ceil(7496/16) = 469 -> [9, 7, 1, 1], 18 workgroups costing 8648 in
-    # total, none above 528, so list scheduling ends by 8648/4 + 528 < 3064.
+    # total, none above 528, so list scheduling ends by 8648/4 + 528 < 3064,
+    # and its merge (16 partials of 130 fp32, 16640 B over 4 x 512) adds 9.
+    # 4/3 and half leave every sequence whole: 4160.
     assert _auto([4096, 3000, 200, 200], Hq=1, Hkv=1, d=(128, 128), cus=4) == [9, 7, 1, 1]
-    # The partial term: an MLA-shaped sequence (T=6, 128 heads -> 12 row
-    # blocks; tb = 1152 B, overhead ceil(32768/1152) = 29 tokens) of 2048
-    # tokens on 8 units.  Each workgroup of a split sequence also pays
-    # ceil(2 * 64 * 514 * 4 / 1152) = 229 tokens for its fp32 partial written
-    # and read back.  One round: c = 24576 / 8 = 3072 > 2048 -> 1 split, 12
-    # workgroups of 29 + 2048 = 2077 -> two rounds end at 4154.  Balanced:
-    # c = 768 -> 3 splits of 672, 688, 688 tokens, 36 workgroups costing
-    # 930, 946, 946 -> 33864 in total, so no schedule on 8 units ends before
-    # 4233 > 4154: one round (no split) wins.  Without the partial term the
-    # same 36 workgroups total 25368 and would end near 3171, and the
-    # balanced plan would win.
+    # The merge term on 8 units: the MLA shape at 2048 tokens.  One round: c =
+    # 24576 / 8 = 3072 > 2048 -> 1 split, 12 workgroups of 29 + 2048 = 2077 ->
+    # two rounds end at 4154.  Balanced: c = 768 -> 3 splits, 36 workgroups of
+    # 701-717 tokens, four or five per unit (3553), and a merge of 3 x 768
+    # rows x 514 fp32 written and read over 8 x 1152 B: 1028 -> 4581.  No
+    # split wins; without the merge term balanced would.
     assert _auto([2048], T=6, Hq=128, Hkv=1, d=(576, 512), rpw=64, cus=8) == [1]
     # max_splits caps the count; nblk caps short sequences
     assert _auto([5900], mx=16) == [16]
