@@ -203,7 +203,7 @@ __global__ __launch_bounds__(512) void mla_partial_kernel(PartialParams p, int p
     pb = cbt[last >> psh];
   };
   auto fill = [&](int k, uint8_t* slotp, int pa, int pb) __attribute__((always_inline)) {
-    const int t0 = s + kTile * min(k, nt - 1);      // beyond the last tile: reload it
+    const int t0 = s + kTile * k;                   // k < nt
     if (t0 + kTile <= e) {
       // whole tile in the range: half 0 in page pa, half 1 in page pb
       const uint8_t* half0 = p.k + uint64_t(uint32_t(pa)) * ksp + uint32_t(t0 & pmask) * kst;
@@ -318,8 +318,8 @@ __global__ __launch_bounds__(512) void mla_partial_kernel(PartialParams p, int p
     // tile k+3's loads into the slot tile k-1 left (every wave finished tile
     // k-1 before the step barrier): issued here rather than at the step start,
     // so the tile's K reads and QK go first and the loads queue under the
-    // softmax and PV
-    fill(fill_k, fill_slot(fill_k), pa, pb);
+    // softmax and PV; past the range's last tile nothing is loaded
+    if (fill_k >= 0) fill(fill_k, fill_slot(fill_k), pa, pb);
     const int w2 = wave ^ 1;
     const f32x4 sc[2] = {s0 + xch[w2][0][lane], s1 + xch[w2][1][lane]};
     // ---- online softmax over the tile: lane (n16, qg) holds tokens
@@ -387,27 +387,43 @@ __global__ __launch_bounds__(512) void mla_partial_kernel(PartialParams p, int p
   };
 
   // Tile k: wait until this wave's loads of tile k are done (the loads of
-  // tiles k+1 and k+2 may still be in flight), then a barrier so every wave's
-  // part of the tile has landed -- which also means every wave has finished
-  // tile k-1 (its LDS reads and its partial exchange), so its slot can be
-  // refilled with tile k+3 (issued inside the tile, after the exchange) and
-  // the exchange buffer reused.  Tiles past the range reload the last tile
-  // (never computed), so the counts stay static.
+  // tiles k+1 and k+2, where the range has them, may still be in flight),
+  // then a barrier so every wave's part of the tile has landed -- which also
+  // means every wave has finished tile k-1 (its LDS reads and its partial
+  // exchange), so its slot can be refilled with tile k+3 (issued inside the
+  // tile, after the exchange) and the exchange buffer reused.  Tiles past the
+  // range are never loaded: the wait allows as many loads in flight as the
+  // range has tiles after k, up to two.
   // e4m3: the same three-ahead fills into the code ring; tile k+1 is widened
   // at the start of step k, so at step k this wave waits for its loads of
   // tile k+1 (those of tile k+2 may still be in flight) and the barrier makes
   // tile k's widened slot and tile k+1's codes visible (widening at the step
   // start measured faster than after the exchange or split around it).
-  auto step = [&](int k) __attribute__((always_inline)) {
+  // The steps of the loop's last three tiles (TAIL) take these counts from
+  // the range; the others, all but the last three, have two tiles in flight
+  // behind theirs and a tile to fill.
+  auto step = [&](int k, auto TAIL) __attribute__((always_inline)) {
+    constexpr bool tail = decltype(TAIL)::value;
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    if constexpr (FP8)
-      __builtin_amdgcn_s_waitcnt(0x0F70 | kLPW);           // vmcnt(3)
-    else
-      __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kLPW));     // vmcnt(10)
+    if constexpr (FP8) {
+      if (!tail || k + 2 < nt)
+        __builtin_amdgcn_s_waitcnt(0x0F70 | kLPW);         // vmcnt(3)
+      else
+        __builtin_amdgcn_s_waitcnt(0x0F70);                // vmcnt(0)
+    } else {
+      if (!tail || k + 2 < nt)
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kLPW));   // vmcnt(10)
+      else if (k + 1 < nt)
+        __builtin_amdgcn_s_waitcnt(0x0F70 | kLPW);         // vmcnt(5)
+      else
+        __builtin_amdgcn_s_waitcnt(0x0F70);                // vmcnt(0)
+    }
     lds_barrier();
-    fill_k = k + 3;
+    fill_k = tail ? -1 : k + 3;
     // e4m3: widen tile k+1 (its codes have landed) into the slot tile k-1 left
-    if constexpr (FP8) widen_tile(k + 1);
+    if constexpr (FP8) {
+      if (!tail || k + 1 < nt) widen_tile(k + 1);
+    }
     const uint8_t* cur = tile_slot(k);
     const int t0 = s + kTile * k;
     {
@@ -427,9 +443,9 @@ __global__ __launch_bounds__(512) void mla_partial_kernel(PartialParams p, int p
     tile_pages(0, pa, pb);
     fill(0, fill_slot(0), pa, pb);
     tile_pages(1, pa, pb);
-    fill(1, fill_slot(1), pa, pb);
+    if (nt > 1) fill(1, fill_slot(1), pa, pb);
     tile_pages(2, pa, pb);
-    fill(2, fill_slot(2), pa, pb);
+    if (nt > 2) fill(2, fill_slot(2), pa, pb);
     tile_pages(3, pa, pb);
     // Wait here for the query (and with it, loads completing in order, the
     // three fills): the compiler does not see the fills, and a wait for the
@@ -439,13 +455,14 @@ __global__ __launch_bounds__(512) void mla_partial_kernel(PartialParams p, int p
 #pragma unroll
     for (int it = 0; it < kQk; ++it) asm volatile("" ::"v"(q[it]));
     if constexpr (FP8) {
-      // tile 0 widened before the loop (tile k+1 is widened in step k)
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kLPW));     // vmcnt(6): tile 0 landed
+      // tile 0 (landed with the wait above) widened before the loop; tile
+      // k+1 is widened in step k
       lds_barrier();
       widen_tile(0);
     }
-    for (int k = 0; k < nt; ++k) step(k);
+    int k = 0;
+    for (; k + 3 < nt; ++k) step(k, std::false_type());
+    for (; k < nt; ++k) step(k, std::true_type());
   }
   // no wave leaves while loads it issued may still write LDS
   __atomic_signal_fence(__ATOMIC_SEQ_CST);

@@ -161,7 +161,8 @@ __global__ __launch_bounds__(512) void mla_fp8q_partial_kernel(PartialParams p, 
   // tokens 16-31; a 16-token half lies in one page, so a sub-tile inside the
   // range reads each half from a uniform page base plus a per-lane offset.
   // Tokens past the range end load the range's last token; sub-tiles past
-  // the range reload the last one (finite codes, never unmasked).
+  // the range but inside its last window reload the last one (finite codes,
+  // never unmasked); nothing past the last window is loaded.
   const int nt = (e - s + kSub - 1) / kSub;
   const bool third = wave + kWaves * (kLPW - 1) < kSlotLoads;   // waves 0 and 1
   auto load_index = [&](int u) __attribute__((always_inline)) {
@@ -248,17 +249,26 @@ __global__ __launch_bounds__(512) void mla_fp8q_partial_kernel(PartialParams p, 
 
   // Step k (sub-tile r = k mod 4 of its window): wait for this wave's loads of
   // sub-tile k (those of k+1..k+3, three or two per sub-tile, may still be in
-  // flight), then a barrier so
-  // every wave's part has landed -- which also means every wave has finished
-  // step k-1, so the exchange buffer can be reused, and the previous window's
-  // products, so its slots can be refilled.
-  auto step = [&](int k, auto R) __attribute__((always_inline)) {
+  // flight; in the last window only those up to its end, the last sub-tile
+  // loaded), then a barrier so every wave's part has landed -- which also
+  // means every wave has finished step k-1, so the exchange buffer can be
+  // reused, and the previous window's products, so its slots can be refilled.
+  auto step = [&](int k, auto R, auto LASTW) __attribute__((always_inline)) {
     constexpr int r = decltype(R)::value;
+    constexpr bool lastw = decltype(LASTW)::value;
+    constexpr int ahead_last = kWin - 1 - r;               // sub-tiles after k in the last window
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    if (third)
-      __builtin_amdgcn_s_waitcnt(0x0F70 | (3 * kLPW));     // vmcnt(9)
-    else
-      __builtin_amdgcn_s_waitcnt(0x0F70 | (3 * (kLPW - 1)));   // vmcnt(6)
+    if constexpr (!lastw) {
+      if (third)
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (3 * kLPW));         // vmcnt(9)
+      else
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (3 * (kLPW - 1)));   // vmcnt(6)
+    } else {
+      if (third)
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (ahead_last * kLPW));
+      else
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (ahead_last * (kLPW - 1)));
+    }
     lds_barrier();
     const uint8_t* cur = slot_ptr(k);
     const int t0 = s + kSub * k;
@@ -301,8 +311,8 @@ __global__ __launch_bounds__(512) void mla_fp8q_partial_kernel(PartialParams p, 
     xch[wave][1][lane] = s1;
     lds_barrier();
     // sub-tile k+4 into the slot sub-tile k-4 left (its window's products
-    // finished before this step's first barrier)
-    fill(k + kAhead, pa, pb);
+    // finished before this step's first barrier); the last window loads none
+    if constexpr (!lastw) fill(k + kAhead, pa, pb);
     const int w2 = wave ^ 1;
     const f32x4 sc[2] = {s0 + xch[w2][0][lane], s1 + xch[w2][1][lane]};
     if (t0 + kSub <= full_end) {
@@ -409,13 +419,15 @@ __global__ __launch_bounds__(512) void mla_fp8q_partial_kernel(PartialParams p, 
     }
     tile_pages(kAhead, pa, pb);
     const int nw = (nt + kWin - 1) / kWin;
-    for (int w = 0; w < nw; ++w) {
-      step(kWin * w + 0, std::integral_constant<int, 0>());
-      step(kWin * w + 1, std::integral_constant<int, 1>());
-      step(kWin * w + 2, std::integral_constant<int, 2>());
-      step(kWin * w + 3, std::integral_constant<int, 3>());
+    auto win_steps = [&](int w, auto LASTW) __attribute__((always_inline)) {
+      step(kWin * w + 0, std::integral_constant<int, 0>(), LASTW);
+      step(kWin * w + 1, std::integral_constant<int, 1>(), LASTW);
+      step(kWin * w + 2, std::integral_constant<int, 2>(), LASTW);
+      step(kWin * w + 3, std::integral_constant<int, 3>(), LASTW);
       window(w);
-    }
+    };
+    for (int w = 0; w + 1 < nw; ++w) win_steps(w, std::false_type());
+    win_steps(nw - 1, std::true_type());
   }
   // no wave leaves while loads it issued may still write LDS
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
