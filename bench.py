@@ -45,6 +45,12 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 MFMA_FP8_PEAK_TFLOPS = 5000.0
 METRIC = "decode-attention µs/step and KV GB/s (% of HBM peak) vs num_splits"
 BATCHES = 5
+# Before the timed batches of a measurement, its first captured graph is
+# replayed until this much GPU time has passed: a long kernel measured right
+# after an idle spell reads several percent slow in its first batches (the MLA
+# step at L=65536 gave 187.6, 178.8, 174.6, 172.0, 170.1 us over five batches
+# after a 4 ms warm-up).
+WARM_MS = 30.0
 HEADLINE_SWEEP = "1,2,3,4,6,8,12,16,24,32,48,64,96,128,192,256"
 
 # The other workloads, each carried in the default run's `extra` list: (name, L, split counts;
@@ -177,10 +183,10 @@ def capture(sess, pool, n, fn, stream):
 
 
 def timed_graphs(sess, pool, fn, steps, stream, check=None):
-    """us per launch of fn: one untimed replay, then the median of BATCHES
-    replays of freshly captured graphs, each between two events recorded on
-    the stream the graph runs on (every graph reads the next `steps` copies of
-    the rotation)."""
+    """us per launch of fn: untimed replays of one captured graph for at least
+    WARM_MS of GPU time, then the median of BATCHES replays of freshly captured
+    graphs, each between two events recorded on the stream the graph runs on
+    (every timed graph reads the next `steps` copies of the rotation)."""
     import torch
     with torch.cuda.stream(stream):
         for c in pool.take(3):                # eager warm-up on the launch stream
@@ -188,9 +194,16 @@ def timed_graphs(sess, pool, fn, steps, stream, check=None):
             fn()
     torch.cuda.synchronize()
     g = capture(sess, pool, steps, fn, stream)
-    with torch.cuda.stream(stream):
-        g.replay()
-    torch.cuda.synchronize()
+    warm_ms, replays = 0.0, 0
+    while warm_ms < WARM_MS and replays < 1000:
+        e0, e1 = _events()
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        warm_ms += e0.elapsed_time(e1)
+        replays += 1
     del g
     if check:
         check()
