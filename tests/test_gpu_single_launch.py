@@ -4,8 +4,9 @@ splitkv_decode_single_launch runs the grouped-query partial kernel with a
 ticketed last-arriver merge instead of a second (combine) kernel.  Its output
 must meet the oracle bound, agree with the two-kernel step, leave the ticket
 counters at zero after every call, and write nothing outside its buffers.
-Decode steps captured in a HIP graph must give, on every replay, the bits of
-the same step run eagerly.
+It must do so on grids larger than one round of the GPU too (the ragged
+batch's 1248 workgroups).  Decode steps captured in a HIP graph must give, on
+every replay, the bits of the same step run eagerly.
 """
 import numpy as np
 import pytest
@@ -67,6 +68,31 @@ def test_single_launch_matches_oracle_and_two_kernel_step(name):
         assert_close(to_np(sess.lse), to_np(two_lse), 2 * ATOL_LSE, 0.0, f"{name} lse vs two-kernel step")
         check_guards(sess)
         log(f"  call {call}: out max-abs {e[0]:.2e}; slots {sess.total_slots}")
+
+
+@pytest.mark.parametrize("which", ["fp8-batched", "ragged-full"])
+def test_single_launch_full_size_grids_match_two_kernel_step(which):
+    # 256 workgroups (FP8 batch, one per CU) and 1248 (the ragged batch: more
+    # than one round), at the auto plan: the single launch against the
+    # two-kernel step, every row.
+    _need_gpu()
+    import torch
+    case = synth.fp8_batched() if which == "fp8-batched" else synth.ragged()
+    log(f"single launch vs two kernels, full size: {which}")
+    sess, _ = session_for(case, requested_splits=0, max_splits=256)
+    sess.decode()
+    torch.cuda.synchronize()
+    two_out, two_lse = sess.out.clone(), sess.lse.clone()
+    atol, _ = tolerances(case)
+    for call in range(2):
+        sess.out.fill_(float("nan"))
+        sess.lse.fill_(float("nan"))
+        sess.decode_single_launch()
+        torch.cuda.synchronize()
+        assert_close(to_np(sess.out), to_np(two_out), 2 * atol, 0.0, f"{which} call {call} vs two-kernel")
+        assert_close(to_np(sess.lse), to_np(two_lse), 2 * ATOL_LSE, 0.0, f"{which} call {call} lse")
+        assert int(sess.tickets.abs().sum()) == 0, "counters not left at zero"
+    check_guards(sess)
 
 
 def test_single_launch_refuses_mla_and_missing_tickets():
