@@ -562,6 +562,8 @@ def test_mla_fp8_full_size_sampled():
     rng = np.random.default_rng(5)
     rows = [(0, int(t), int(h)) for t, h in zip(rng.integers(0, 6, 24), rng.integers(0, 128, 24))]
     rows += [(0, 0, 0), (0, 5, 127)]
+    # one row in each of the twelve 64-row blocks (row = t * 128 + h)
+    rows += [(0, r // 128, r % 128) for r in range(11, 768, 64)]
     _check_rows(case, sess, rows, "mla e4m3 L=65536")
 
 
@@ -746,6 +748,8 @@ def test_mla_fp8q_full_size_sampled():
     rng = np.random.default_rng(6)
     rows = [(0, int(t), int(h)) for t, h in zip(rng.integers(0, 6, 24), rng.integers(0, 128, 24))]
     rows += [(0, 0, 0), (0, 5, 127)]
+    # one row in each of the twelve 64-row blocks (row = t * 128 + h)
+    rows += [(0, r // 128, r % 128) for r in range(29, 768, 64)]
     _check_rows(case, sess, rows, "mla fp8q L=65536")
 
 
