@@ -604,8 +604,9 @@ def main():
         append_measurement(args.steps, args.warmup)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "multi-GPU sharding is described in DESIGN.md, not run.", file=sys.stderr)
+        print(f"bench.py: measures one GPU only (asked for --gpus {args.gpus}); the path would "
+              "shard by sequence or KV head, or by KV range with one exchange of the partials "
+              "before the combine, but no multi-GPU run is made.", file=sys.stderr)
         sys.exit(2)
     import torch
     import split_kv_amd

@@ -9,7 +9,7 @@ writes each new token there.  An FP8 cache is read as code x scale with one
 fp32 scale per tensor ("Xqa decode kernels", section "Purpose": bf16 queries
 over an FP8 KV cache; "Test Plan": the cache dtype fp8 with its dequant
 test).  The pages do not spell out the write side; the plainest reading,
-the inverse of that read, is taken here and stated in the design doc:
+the inverse of that read, is taken here:
 
     code = nearest e4m3 value of clamp(x / scale, -448, 448)   (fp32 division)
 
