@@ -51,13 +51,24 @@
  *   out          [B][T][Hq][d_v], bf16 or fp32 (out_dtype), contiguous.
  *   lse          fp32 [B][T][Hq] natural-log log-sum-exp of the scaled
  *                scores; may be NULL.
- *   workspace    fp32; layout (S = total_slots, R = T*Hq):
- *                  part_m [S][R]   max of scale*q.k over the split (natural
- *                                  log units; -inf if the row sees nothing)
- *                  part_l [S][R]   sum of exp(s - m)
- *                  part_o [S][R][d_v]  sum of exp(s - m) * v (v dequantised)
- *                part_o starts at the first 256-byte boundary after part_l;
- *                splitkv_workspace_bytes() gives the total.
+ *   workspace    the split partials; layout (S = total_slots, R = T*Hq):
+ *                  part_m [S][R]   fp32 max of scale*q.k over the split
+ *                                  (natural log units; -inf if the row sees
+ *                                  nothing)
+ *                  part_l [S][R]   fp32 sum of exp(s - m)
+ *                  part_o [S][R][d_v]  fp32 sum of exp(s - m) * v (v
+ *                                  dequantised), from the first 256-byte
+ *                                  boundary after part_l
+ *                For d_v = 512 (the MLA kernels) part_o is compact instead:
+ *                  part_s [S][R][2]  fp32 scale of each 256-feature half of
+ *                                  the row, right after part_l
+ *                  part_q [S][R][512]  int16 codes from the first 256-byte
+ *                                  boundary after part_s: o = code * scale
+ *                                  of its half, the scale being the half's
+ *                                  largest |o| / 32767 (codes within half a
+ *                                  step of o, i.e. 2^-16 of that largest
+ *                                  magnitude).
+ *                splitkv_workspace_bytes() gives a size that holds either.
  *   debug        optional int32 [S][Hkv][row_blocks][8] records
  *                (b, i, hk, s, e, groups, xor_phys, sum_phys mod 2^31) over
  *                the 16-token groups of the split's range; row_blocks =
@@ -145,9 +156,11 @@ typedef struct {
  *      onto num_cus identical compute units, a workgroup costing
  *      ceil(SPLITKV_AUTO_WG_OVERHEAD_BYTES / tb) + (end - start) tokens, plus
  *      the merge: ceil(Pb / (num_cus * tb)) tokens, Pb = 2 * sum over the
- *      sequences with n_b > 1 of n_b * T * Hq * (d_v + 2) * 4, the fp32
- *      partials written and read back, spread over every compute unit; the
- *      lowest estimate wins, the earlier of A, B, C, D on a tie.
+ *      sequences with n_b > 1 of n_b * T * Hq * row_bytes, the partials
+ *      written and read back, spread over every compute unit, row_bytes =
+ *      (d_v + 2) * 4, or 2 * d_v + 16 for MLA (the compact layout of the
+ *      workspace); the lowest estimate wins, the earlier of A, B, C, D on a
+ *      tie.
  *
  * Split i of n covers [16*floor(i*nblk/n), min(L, 16*floor((i+1)*nblk/n))).
  * L == 0 gives one empty split.

@@ -42,9 +42,10 @@ two are compared bit for bit.
     after another), each go to whichever of num_cus compute units is free
     first, costing ceil(AUTO_WG_OVERHEAD_BYTES / tb) + (end - start) tokens;
     to the latest finish is added ceil(Pb / (num_cus * tb)) tokens, Pb =
-    2 * sum over sequences with n_b > 1 of n_b * T * Hq * (d_v + 2) * 4, the
-    fp32 partials written and read back by the merge, spread over every
-    compute unit.  The lowest score wins; on a tie the earlier candidate in
+    2 * sum over sequences with n_b > 1 of n_b * T * Hq * row_bytes, the
+    partials written and read back by the merge, spread over every compute
+    unit; row_bytes = (d_v + 2) * 4 (fp32 m, l, o), or 2 * d_v + 16 for MLA
+    (int16 codes of o; m, l and two scales in fp32).  The lowest score wins; on a tie the earlier candidate in
     the order one round, balanced, 4/3, 2.
 * Split i of n covers [G*floor(i*nblk/n), min(L, G*floor((i+1)*nblk/n))).
   Because n <= nblk every range holds at least one token, the ranges are
@@ -104,10 +105,11 @@ def _latest_finish(L, ns, units, num_cus, overhead):
     return latest
 
 
-def _merge_tokens(ns, T, Hq, d_v, num_cus, tb):
-    """The fp32 partials a plan writes and the merge reads back, in tokens of
+def _merge_tokens(ns, T, Hq, d_v, num_cus, tb, mla):
+    """The partials a plan writes and the merge reads back, in tokens of
     streaming spread over every compute unit (single-split sequences have none)."""
-    pb = 2 * sum(n for n in ns if n > 1) * T * Hq * (d_v + 2) * 4
+    row_bytes = 2 * d_v + 16 if mla else (d_v + 2) * 4
+    pb = 2 * sum(n for n in ns if n > 1) * T * Hq * row_bytes
     return _ceil_div(pb, num_cus * tb)
 
 
@@ -130,7 +132,7 @@ def _auto_counts(L, *, T, Hq, Hkv, max_splits, num_cus, rows_per_wg, d_qk, d_v, 
     ov = _ceil_div(AUTO_WG_OVERHEAD_BYTES, tb)
     best, best_score = None, None
     for ns in (one, bal, few, half):
-        score = _latest_finish(L, ns, units, num_cus, ov) + _merge_tokens(ns, T, Hq, d_v, num_cus, tb)
+        score = _latest_finish(L, ns, units, num_cus, ov) + _merge_tokens(ns, T, Hq, d_v, num_cus, tb, mla)
         if best_score is None or score < best_score:
             best, best_score = ns, score
     return best

@@ -65,17 +65,28 @@ enum class Kind { GqaBf16, GqaFp8, Mla };
 struct Layout {
   float* m;
   float* l;
-  float* o;
+  float* o;       // fp32 o (d_v < 512)
+  float* s;       // d_v = 512: two scales per row
+  int16_t* q;     // d_v = 512: int16 codes of o
 };
 
+// The partials' layout in the workspace (documented in splitkv.h): m, l,
+// then fp32 o at the next 256-byte boundary; for d_v = 512 (the MLA kernel)
+// m, l, two scales per row, then int16 codes at the next 256-byte boundary
+// (smaller than the fp32 layout that splitkv_workspace_bytes sizes).
 Layout workspace_layout(const splitkv_args& a) {
   const size_t rows = size_t(a.total_slots) * size_t(a.T) * size_t(a.Hq);
-  size_t ml = 2 * rows * sizeof(float);
-  ml = (ml + 255) / 256 * 256;
-  Layout w;
+  Layout w = {nullptr, nullptr, nullptr, nullptr, nullptr};
+  if (!a.workspace) return w;
+  char* base = reinterpret_cast<char*>(a.workspace);
   w.m = a.workspace;
-  w.l = a.workspace ? a.workspace + rows : nullptr;
-  w.o = a.workspace ? reinterpret_cast<float*>(reinterpret_cast<char*>(a.workspace) + ml) : nullptr;
+  w.l = a.workspace + rows;
+  if (a.d_v == 512) {
+    w.s = a.workspace + 2 * rows;
+    w.q = reinterpret_cast<int16_t*>(base + (4 * rows * sizeof(float) + 255) / 256 * 256);
+  } else {
+    w.o = reinterpret_cast<float*>(base + (2 * rows * sizeof(float) + 255) / 256 * 256);
+  }
   return w;
 }
 
@@ -219,6 +230,8 @@ PartialParams make_partial_params(const splitkv_args& a, Kind kind, int row_bloc
   p.part_m = w.m;
   p.part_l = w.l;
   p.part_o = w.o;
+  p.part_s = w.s;
+  p.part_q = w.q;
   p.out = a.out;
   p.out_f32 = a.out_dtype == SPLITKV_OUT_F32;
   p.lse = a.lse;

@@ -26,20 +26,30 @@ namespace splitkv {
 
 // One thread's share of a row's splits: splits g, g+G, g+2G, ... of the n,
 // U loads in flight per pass, merged into the running (M2, lam, acc) in base 2.
-template <int U>
-__device__ __forceinline__ void merge_splits(const float* part_m, const float* part_l, const float* po,
-                                             int64_t step, int R, int rix, int base, int n, int g, int G,
-                                             float& M2, float& lam, f32x4& acc) {
+// fp32 o: po points at the thread's float4 of the row in slot 0 and step is a
+// slot's stride.  CODES (the MLA layout): po points at the thread's four int16
+// codes instead, and ps at the scale of the half of the row they lie in (a
+// slot's stride 2R floats); o = code * scale.
+template <int U, bool CODES>
+__device__ __forceinline__ void merge_splits(const float* part_m, const float* part_l, const void* po,
+                                             const float* ps, int64_t step, int R, int rix, int base,
+                                             int n, int g, int G, float& M2, float& lam, f32x4& acc) {
   for (int i0 = g; i0 < n; i0 += U * G) {
-    float mi[U], li[U];
+    float mi[U], li[U], si[U];
     f32x4 oi[U];
+    u32x2 ci[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int i = i0 + u * G;
       const int64_t sl = base + (i < n ? i : i0);   // past the end: reread a valid slot, weight 0
       mi[u] = part_m[sl * R + rix];
       li[u] = part_l[sl * R + rix];
-      oi[u] = *reinterpret_cast<const f32x4*>(po + sl * step);
+      if constexpr (CODES) {
+        si[u] = ps[sl * 2 * R];
+        ci[u] = *reinterpret_cast<const u32x2*>(static_cast<const int16_t*>(po) + sl * step);
+      } else {
+        oi[u] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(po) + sl * step);
+      }
       if (i >= n) mi[u] = -INFINITY;
     }
 #pragma unroll
@@ -50,7 +60,14 @@ __device__ __forceinline__ void merge_splits(const float* part_m, const float* p
       const float a = fast_exp2(M2 - Mn);                 // 0 while M2 is -inf
       const float w = fast_exp2(m2 - Mn);
       lam = lam * a + w * li[u];
-      acc = acc * a + w * oi[u];
+      if constexpr (CODES) {
+        const float ws = w * si[u];
+        const f32x4 o = {float(int16_t(ci[u].x & 0xffffu)), float(int16_t(ci[u].x >> 16)),
+                         float(int16_t(ci[u].y & 0xffffu)), float(int16_t(ci[u].y >> 16))};
+        acc = acc * a + ws * o;
+      } else {
+        acc = acc * a + w * oi[u];
+      }
       M2 = Mn;
     }
   }
@@ -66,10 +83,13 @@ __device__ __forceinline__ void merge_splits(const float* part_m, const float* p
 // argument is <= 0: a difference from the running max).
 // flags: d_v (bits 0-15) | skip rows of single-split sequences (bit 16) |
 // fp32 output (bit 17) | uniform split count (bits 18-26; 0: read the plan).
+// CODES: the partials are in the MLA layout (m, l, two scales per row from
+// 2 * SR floats on, int16 codes of o at the next 256-byte boundary after
+// 4 * SR floats).
 // With a uniform count the row's plan is n = that count and base = b * n, so
 // the partial loads are the first memory accesses.  The workgroup has C * G
 // threads (C = blockDim.x / G float4 columns).
-template <int G>
+template <int G, bool CODES>
 __global__ __launch_bounds__(256) void combine_kernel(const float* part_m, const int32_t* num_splits,
                                                       const int32_t* slot_offset, void* out,
                                                       float* lse, int32_t R, int32_t dsplit,
@@ -97,25 +117,33 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* part_m, const
   const int DV = flags & 0xffff;
   const int c = tid % C, g = tid / C;
   const float* part_l = part_m + SR;
-  const float* part_o = part_m + (int64_t(2) * SR * 4 + 255) / 256 * 64;
 
   // running state in base 2: M2 = max of m_i * log2(e)
   float M2 = -INFINITY, lam = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   const int f0 = 4 * (C * part + c);                  // this thread's first feature
-  const float* po = part_o + int64_t(rix) * DV + f0;
   const int64_t step = int64_t(R) * DV;
+  const void* po;
+  const float* ps = nullptr;
+  if constexpr (CODES) {
+    const int16_t* part_q = reinterpret_cast<const int16_t*>(
+        reinterpret_cast<const char*>(part_m) + (int64_t(16) * SR + 255) / 256 * 256);
+    po = part_q + int64_t(rix) * DV + f0;
+    ps = part_m + int64_t(2) * SR + int64_t(rix) * 2 + f0 / 256;
+  } else {
+    po = part_m + (int64_t(2) * SR * 4 + 255) / 256 * 64 + int64_t(rix) * DV + f0;
+  }
   // loads per thread and pass: just enough for the row's splits (uniform
   // across the workgroup), so no pass issues loads it only masks away
   const int per = (n + G - 1) / G;
   if (per <= 1)
-    merge_splits<1>(part_m, part_l, po, step, R, rix, base, n, g, G, M2, lam, acc);
+    merge_splits<1, CODES>(part_m, part_l, po, ps, step, R, rix, base, n, g, G, M2, lam, acc);
   else if (per <= 2)
-    merge_splits<2>(part_m, part_l, po, step, R, rix, base, n, g, G, M2, lam, acc);
+    merge_splits<2, CODES>(part_m, part_l, po, ps, step, R, rix, base, n, g, G, M2, lam, acc);
   else if (per <= 4)
-    merge_splits<4>(part_m, part_l, po, step, R, rix, base, n, g, G, M2, lam, acc);
+    merge_splits<4, CODES>(part_m, part_l, po, ps, step, R, rix, base, n, g, G, M2, lam, acc);
   else
-    merge_splits<8>(part_m, part_l, po, step, R, rix, base, n, g, G, M2, lam, acc);
+    merge_splits<8, CODES>(part_m, part_l, po, ps, step, R, rix, base, n, g, G, M2, lam, acc);
   if constexpr (G > 1) {
     red_m[tid] = M2;
     red_l[tid] = lam;
@@ -166,15 +194,22 @@ hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
   const int dsplit = cols / C;
   const int64_t wgs = int64_t(p.B) * p.R * dsplit;
   const int64_t SR = p.part_l - p.part_m;
-  if (wgs > INT32_MAX || SR > INT32_MAX / 8 ||
-      p.part_o != p.part_m + (2 * SR * 4 + 255) / 256 * 64)
+  const bool codes = p.d_v == 512;                  // the MLA layout
+  if (wgs > INT32_MAX || SR > INT32_MAX / 16 ||
+      (!codes && p.part_o != p.part_m + (2 * SR * 4 + 255) / 256 * 64))
     return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(wgs)), block(unsigned(C * G));
   const int32_t flags = p.d_v | (p.skip_single ? 1 << 16 : 0) | (p.out_f32 ? 1 << 17 : 0) |
                        (p.uniform_splits << 18);
-#define SPLITKV_COMBINE(GG)                                                                             \
-  hipLaunchKernelGGL(combine_kernel<GG>, grid, block, 0, stream, p.part_m, p.num_splits, p.slot_offset, \
-                     p.out, p.lse, p.R, dsplit, flags, int32_t(SR))
+#define SPLITKV_COMBINE(GG)                                                                            \
+  do {                                                                                                 \
+    if (codes)                                                                                         \
+      hipLaunchKernelGGL((combine_kernel<GG, true>), grid, block, 0, stream, p.part_m, p.num_splits,   \
+                         p.slot_offset, p.out, p.lse, p.R, dsplit, flags, int32_t(SR));                \
+    else                                                                                               \
+      hipLaunchKernelGGL((combine_kernel<GG, false>), grid, block, 0, stream, p.part_m, p.num_splits,  \
+                         p.slot_offset, p.out, p.lse, p.R, dsplit, flags, int32_t(SR));                \
+  } while (0)
   switch (G) {
     case 1: SPLITKV_COMBINE(1); break;
     case 2: SPLITKV_COMBINE(2); break;

@@ -43,7 +43,9 @@ struct PartialParams {
   float v_scale;
   float* part_m;                // [S][T*Hq]
   float* part_l;
-  float* part_o;                // [S][T*Hq][d_v]
+  float* part_o;                // [S][T*Hq][d_v] (grouped-query kernels)
+  float* part_s;                // MLA: [S][T*Hq][2] scales of the two 256-feature halves of o
+  int16_t* part_q;              // MLA: [S][T*Hq][512] codes of o (o = code * scale of its half)
   void* out;
   int32_t out_f32;
   float* lse;

@@ -74,15 +74,17 @@ static int64_t list_schedule(const int32_t* seq_lens, const std::vector<int32_t>
   return busiest;
 }
 
-// The fp32 partials a plan writes and the merge reads back, in tokens of
+// The partials a plan writes and the merge reads back, in tokens of
 // streaming spread over every compute unit (a single split writes the output
-// directly and has none).
+// directly and has none).  A partial row is (d_v + 2) fp32 values, or for the
+// MLA kernels 2 * d_v bytes of codes and four fp32 values (m, l, two scales).
 static int64_t merge_tokens(const std::vector<int32_t>& ns, int64_t T, int64_t Hq, int64_t d_v,
-                            int32_t num_cus, int64_t tb) {
+                            bool mla, int32_t num_cus, int64_t tb) {
   int64_t slots = 0;
   for (int32_t n : ns)
     if (n > 1) slots += n;
-  return ceil_div(2 * slots * T * Hq * (d_v + 2) * 4, int64_t(num_cus) * tb);
+  const int64_t row_bytes = mla ? 2 * d_v + 16 : (d_v + 2) * 4;
+  return ceil_div(2 * slots * T * Hq * row_bytes, int64_t(num_cus) * tb);
 }
 
 // Auto split counts (the rule documented at splitkv_plan).
@@ -121,7 +123,7 @@ static void auto_splits(const splitkv_plan_args& a, int32_t num_cus, const int32
   int64_t best_score = INT64_MAX;
   for (size_t k = 0; k < cand.size(); ++k) {
     const int64_t score = list_schedule(seq_lens, cand[k], units, num_cus, overhead) +
-                          merge_tokens(cand[k], a.T, a.Hq, a.d_v, num_cus, tb);
+                          merge_tokens(cand[k], a.T, a.Hq, a.d_v, mla, num_cus, tb);
     if (score < best_score) {
       best = k;
       best_score = score;

@@ -197,11 +197,18 @@ class DecodeSession:
         return self.out, self.lse
 
     def partials(self):
-        """Views (part_m [S,T,Hq], part_l [S,T,Hq], part_o [S,T,Hq,d_v]) of the workspace."""
+        """(part_m [S,T,Hq], part_l [S,T,Hq], part_o [S,T,Hq,d_v]) of the workspace:
+        views, except the MLA layout's o, which is decoded from its int16 codes
+        and half-row scales into a new fp32 tensor."""
         s = self.shape
         S, T, Hq, dv = self.total_slots, s["T"], s["Hq"], s["d_v"]
         rows = S * T * Hq
-        ml = -(-(2 * rows * 4) // 256) * 256 // 4
         w = self.workspace
-        return (w[:rows].view(S, T, Hq), w[rows:2 * rows].view(S, T, Hq),
-                w[ml:ml + rows * dv].view(S, T, Hq, dv))
+        pm, pl = w[:rows].view(S, T, Hq), w[rows:2 * rows].view(S, T, Hq)
+        if dv == 512:
+            scales = w[2 * rows:4 * rows].view(S, T, Hq, 2)
+            q0 = -(-(4 * rows * 4) // 256) * 256 // 2          # int16 offset of the codes
+            codes = w.view(self.torch.int16)[q0:q0 + rows * dv].view(S, T, Hq, 2, dv // 2)
+            return pm, pl, (codes.float() * scales[..., None]).reshape(S, T, Hq, dv)
+        ml = -(-(2 * rows * 4) // 256) * 256 // 4
+        return pm, pl, w[ml:ml + rows * dv].view(S, T, Hq, dv)

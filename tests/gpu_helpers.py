@@ -118,3 +118,21 @@ def assert_close(got, ref, atol, rtol, what):
 
 def tolerances(case):
     return (ATOL_FP8, RTOL_FP8) if case.kv_dtype == synth.KV_E4M3 else (ATOL_BF16, RTOL_BF16)
+
+
+def pack_half_rows(o):
+    """The MLA partial layout of o [..., 512]: a scale per 256-feature half
+    (its largest |o| / 32767, fp32) and int16 codes, each the nearest integer
+    to o / scale (0 where the half is all zero)."""
+    h = o.reshape(o.shape[:-1] + (2, 256)).astype(np.float32)
+    amax = np.abs(h).max(axis=-1)
+    scales = (amax * np.float32(1.0 / 32767.0)).astype(np.float32)
+    k = np.where(amax > 0, np.float32(32767.0) / np.where(amax > 0, amax, 1), 0).astype(np.float32)
+    codes = np.clip(np.rint(h * k[..., None]), -32767, 32767).astype(np.int16)
+    return scales, codes.reshape(o.shape)
+
+
+def unpack_half_rows(scales, codes):
+    """The values the MLA layout's codes stand for: code * scale of its half."""
+    h = codes.reshape(codes.shape[:-1] + (2, 256)).astype(np.float64)
+    return (h * scales[..., None].astype(np.float64)).reshape(codes.shape)

@@ -13,7 +13,7 @@ import oracle
 import synth
 from oracle import plan as oplan
 from tests.gpu_helpers import (ATOL_LSE, assert_close, check_guards, log, session_for, to_np,
-                               tolerances)
+                               tolerances, pack_half_rows, unpack_half_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -139,6 +139,32 @@ def test_few_kv_partials_match_oracle_split_emulation():
     assert_close(go / gl[..., None], po / pl[..., None], 1e-2, 2e-2, "part_o / part_l")
 
 
+@pytest.mark.parametrize("path", ["bf16", "e4m3", "e4m3-queries"])
+def test_mla_partials_match_oracle_split_emulation(path):
+    # The MLA kernels write o compactly (int16 codes, a scale per 256-feature
+    # half); decoded, each split's own softmax output o / l must meet the
+    # output bar against the oracle's fp64 split emulation, and m, l the
+    # fp32-tight bounds.
+    _need_gpu()
+    import torch
+    kv = synth.KV_BF16 if path == "bf16" else synth.KV_E4M3
+    case = synth.mla_decode(L=1500, seed=91, kv_dtype=kv, fp8_queries=path == "e4m3-queries")
+    sess, _ = session_for(case, requested_splits=5)
+    log(f"mla partials {path} L=1500 n=5")
+    sess.partial()
+    torch.cuda.synchronize()
+    pm, pl, po = oracle.split_partials(case, sess.num_splits_host, sess.slot_offset_host)
+    gm, gl, go = (to_np(x) for x in sess.partials())
+    # a score is an fp32 sum over 576 features (|s| up to ~20 here), so it is
+    # off by up to ~1e-5 * |s|; m inherits that, and l = sum exp(s - m) the
+    # same relative error, ~2e-4
+    assert_close(gm, pm, 2e-4, 1e-5, "part_m")
+    assert_close(gl, pl, 0.0, 2e-4, "part_l")
+    check_guards(sess)
+    atol, rtol = tolerances(case)
+    assert_close(go / gl[..., None], po / pl[..., None], atol, rtol, "part_o / part_l")
+
+
 def test_combine_alone_against_oracle_combine():
     _need_gpu()
     import torch
@@ -195,10 +221,19 @@ def test_combine_launch_shapes(d_v, T, Hq, splits, hint):
     o[np.isinf(m)] = 0
     nbytes = sk.splitkv_workspace_bytes(S, T, Hq, d_v)
     ws = torch.full(((nbytes + 3) // 4,), float("nan"), dtype=torch.float32, device="cuda")
-    lo = -(-(2 * S * R * 4) // 256) * 256 // 4
     ws[:S * R] = torch.from_numpy(m.reshape(-1)).cuda()
     ws[S * R:2 * S * R] = torch.from_numpy(l.reshape(-1)).cuda()
-    ws[lo:lo + S * R * d_v] = torch.from_numpy(o.reshape(-1)).cuda()
+    if d_v == 512:
+        # the MLA layout: int16 codes and a scale per 256-feature half; the
+        # merge is checked on the values the codes stand for
+        scales, codes = pack_half_rows(o)
+        ws[2 * S * R:4 * S * R] = torch.from_numpy(scales.reshape(-1)).cuda()
+        q0 = -(-(4 * S * R * 4) // 256) * 256 // 2
+        ws.view(torch.int16)[q0:q0 + S * R * d_v] = torch.from_numpy(codes.reshape(-1)).cuda()
+        o = unpack_half_rows(scales, codes)
+    else:
+        lo = -(-(2 * S * R * 4) // 256) * 256 // 4
+        ws[lo:lo + S * R * d_v] = torch.from_numpy(o.reshape(-1)).cuda()
     o = o.astype(np.float64)
     out = torch.full((B, T, Hq, d_v), float("nan"), dtype=torch.float32, device="cuda")
     lse = torch.full((B, T, Hq), float("nan"), dtype=torch.float32, device="cuda")

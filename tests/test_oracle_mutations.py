@@ -159,5 +159,13 @@ def test_unquantised_queries_are_caught(monkeypatch):
 
 def test_dropped_merge_term_is_caught(monkeypatch):
     # the auto planner's estimate without the cost of the fp32 partials
-    monkeypatch.setattr(P, "_merge_tokens", lambda ns, T, Hq, d_v, cus, tb: 0)
+    monkeypatch.setattr(P, "_merge_tokens", lambda ns, T, Hq, d_v, cus, tb, mla: 0)
+    _fails(TP.test_auto_plan_worked_examples)
+
+
+def test_fp32_row_bytes_for_mla_are_caught(monkeypatch):
+    # the MLA merge priced at the grouped-query kernels' fp32 partial row
+    orig = P._merge_tokens
+    monkeypatch.setattr(P, "_merge_tokens",
+                        lambda ns, T, Hq, d_v, cus, tb, mla: orig(ns, T, Hq, d_v, cus, tb, False))
     _fails(TP.test_auto_plan_worked_examples)

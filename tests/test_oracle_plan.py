@@ -117,18 +117,20 @@ def test_auto_plan_worked_examples():
     # units -> four each, ~4512 + 130.  4/3 and half: 5 and 4 splits, single
     # workgroups of 6400 and 8000 tokens.  One round wins.
     assert _auto([32000] * 8, Hq=32, Hkv=4, d=(128, 128), elem=1) == [8] * 8
-    # MLA decode at L=65536 (T=6, 128 heads -> units = 12, tb = 1152):
+    # MLA decode at L=65536 (T=6, 128 heads -> units = 12, tb = 1152; an MLA
+    # partial row is 2 x 512 bytes of codes and 16 of m, l and two scales):
     # c_lat = isqrt(98304) = 313; one round: c = 786432/256 = 3072 -> 21
-    # splits, 252 workgroups of up to 3136 tokens -> 3165 + merge 225 (21
-    # slots x 768 rows x 514 fp32 written and read, over 256 x 1152 B);
+    # splits, 252 workgroups of up to 3136 tokens -> 3165 + merge 114 (21
+    # slots x 768 rows x 1040 B written and read, over 256 x 1152 B);
     # balanced: c = 768 -> 86 splits, 1032 workgroups, about four per unit;
-    # 4/3: 16 splits of 4096 -> 4125 + 171.  One round wins.
+    # 4/3: 16 splits of 4096 -> 4125 + 87.  One round wins.
     assert _auto([65536], T=6, Hq=128, Hkv=1, d=(576, 512), rpw=64) == [21]
     # The same at L=2048, where the merge decides: one round, c = 96 -> 21
-    # splits of 96-112 tokens -> 141 + 225 = 366; 4/3, c = 128 -> 16 splits of
-    # 128 -> 157 + 172 = 329; half, c = 192 -> 10 splits of up to 208 -> 237 +
-    # 108 = 345; balanced, c = 55 -> 38 splits, 456 workgroups in two rounds.
-    # An e4m3 cache counts the same tb: a token costs the matrix work.
+    # splits of 96-112 tokens -> 141 + 114 = 255; 4/3, c = 128 -> 16 splits of
+    # 128 -> 157 + 87 = 244; half, c = 192 -> 10 splits of up to 208 -> 237 +
+    # 55 = 292; balanced, c = 55 -> 38 splits, 456 workgroups in two rounds:
+    # 186 + 206.  An e4m3 cache counts the same tb: a token costs the matrix
+    # work.
     assert _auto([2048], T=6, Hq=128, Hkv=1, d=(576, 512), rpw=64) == [16]
     assert _auto([2048], T=6, Hq=128, Hkv=1, d=(576, 512), rpw=64, elem=1) == [16]
     # Unequal lengths on 4 units (Hq = Hkv = 1 -> units = 1; D=128 bf16, overhead
@@ -143,9 +145,10 @@ def test_auto_plan_worked_examples():
     # 24576 / 8 = 3072 > 2048 -> 1 split, 12 workgroups of 29 + 2048 = 2077 ->
     # two rounds end at 4154.  Balanced: c = 768 -> 3 splits, 36 workgroups of
     # 701-717 tokens, four or five per unit (3553), and a merge of 3 x 768
-    # rows x 514 fp32 written and read over 8 x 1152 B: 1028 -> 4581.  No
-    # split wins; without the merge term balanced would.
-    assert _auto([2048], T=6, Hq=128, Hkv=1, d=(576, 512), rpw=64, cus=8) == [1]
+    # rows x 1040 B written and read over 8 x 1152 B: 520 -> 4073, which wins;
+    # priced at the fp32 row of the grouped-query kernels (514 x 4 B) the
+    # merge would cost 1028 and no split would win.
+    assert _auto([2048], T=6, Hq=128, Hkv=1, d=(576, 512), rpw=64, cus=8) == [3]
     # max_splits caps the count; nblk caps short sequences
     assert _auto([5900], mx=16) == [16]
     assert _auto([0, 0]) == [1, 1]
