@@ -271,14 +271,16 @@ def measured_traffic():
 
 def step_bytes(case, num_splits):
     """Bytes a step must move besides the KV (query in, output and LSE out),
-    and the method's own overhead: the fp32 partials (m, l, o) written by the
-    partial kernel and read back by the combine (sequences with one split
-    write their output directly and have none)."""
+    and the method's own overhead: the partials written by the partial kernel
+    and read back by the combine (sequences with one split write their output
+    directly and have none) -- fp32 m, l, o a row, or for MLA fp32 m, l, two
+    scales and int16 codes of o."""
     rows = case.B * case.T * case.Hq
     q = rows * case.d_qk * 2
     out = rows * case.d_v * (4 if case.out_fp32 else 2) + rows * 4
     slots = int(sum(int(n) for n in num_splits if int(n) > 1))
-    partials = slots * case.T * case.Hq * (case.d_v + 2) * 4
+    row_bytes = 2 * case.d_v + 16 if case.mla else (case.d_v + 2) * 4
+    partials = slots * case.T * case.Hq * row_bytes
     return {"algorithmic_bytes_total": case.kv_bytes() + q + out,
             "partial_bytes_written_and_read": 2 * partials}
 
