@@ -7,7 +7,9 @@
 // gives the right answer ("vLLM 0.30.0 FA4 SplitKV Bug: H100 Decode Can Be 48%
 // Slower", section "Why the result is still correct").  Its cost grows with
 // the split count ("Shipped: 484.5 tok/s on one GB300 ...", section "Why 8
-// splits lost"): it reads S * rows * (d_v + 2) * 4 bytes of partials.
+// splits lost"): it reads S * rows * (d_v + 2) * 4 bytes of partials, or
+// S * rows * (2 * d_v + 16) in the MLA kernels' compact layout (int16 codes
+// of o with a scale per 256-feature half).
 //
 // A workgroup merges one row's partials over C float4 columns (4C features)
 // with G groups of threads over the splits: thread (g, c) takes splits g,
