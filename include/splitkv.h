@@ -101,7 +101,7 @@ typedef int32_t splitkv_status;
 #define SPLITKV_AUTO_WG_OVERHEAD_BYTES 32768  /* auto: fixed cost of one workgroup, in bytes of streaming */
 #define SPLITKV_MAX_SPLITS_LIMIT 256   /* upper bound of max_splits */
 #define SPLITKV_ROWS_PER_WG_GQA 16     /* query rows (g*T) one GQA workgroup covers */
-#define SPLITKV_ROWS_PER_WG_MLA 64     /* query rows (T*Hq) one MLA workgroup covers */
+#define SPLITKV_ROWS_PER_WG_MLA 128    /* query rows (T*Hq) one MLA workgroup covers */
 #define SPLITKV_DEBUG_INTS 8
 #define SPLITKV_NOALLOC_SCRATCH_BYTES 67108864  /* library-owned partials of splitkv_decode_noalloc, per device */
 #define SPLITKV_SINGLE_LAUNCH_MAX_WORKGROUPS 64  /* splitkv_decode: one launch for grids up to this */

@@ -67,7 +67,7 @@ AUTO_BALANCE = 4
 AUTO_WG_OVERHEAD_BYTES = 32768
 MAX_SPLITS_LIMIT = 256
 ROWS_PER_WG_GQA = 16
-ROWS_PER_WG_MLA = 64
+ROWS_PER_WG_MLA = 128
 
 
 def _ceil_div(a, b):

@@ -36,7 +36,7 @@ SPLITKV_AUTO_BALANCE = 4
 SPLITKV_AUTO_WG_OVERHEAD_BYTES = 32768
 SPLITKV_MAX_SPLITS_LIMIT = 256
 SPLITKV_ROWS_PER_WG_GQA = 16
-SPLITKV_ROWS_PER_WG_MLA = 64
+SPLITKV_ROWS_PER_WG_MLA = 128
 SPLITKV_DEBUG_INTS = 8
 SPLITKV_NOALLOC_SCRATCH_BYTES = 64 << 20
 SPLITKV_SINGLE_LAUNCH_MAX_WORKGROUPS = 64

@@ -56,7 +56,6 @@ def sources():
 PER_FILE = {
     "gqa.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true", "-mllvm", "-amdgpu-kernarg-preload-count=14"],
     "combine.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=14"],
-    "mla.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
     "mla_fp8q.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
 }
 

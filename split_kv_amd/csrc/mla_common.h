@@ -11,9 +11,11 @@ namespace mla {
 
 constexpr int kDqk = 576;                        // latent row: 512 value features + 64 rope
 constexpr int kDv = 512;
-constexpr int kRows = 64;                        // query rows per workgroup
+constexpr int kBlockRows = SPLITKV_ROWS_PER_WG_MLA;   // query rows of a row block of the plan
+// The e4m3-query kernel's workgroups: 64 rows (half a row block), 8 waves.
+constexpr int kRows = 64;
 constexpr int kWaves = 8;
-static_assert(SPLITKV_ROWS_PER_WG_MLA == kRows, "rows per workgroup");
+static_assert(kBlockRows == 2 * kRows, "a row block is two e4m3-query workgroups");
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 

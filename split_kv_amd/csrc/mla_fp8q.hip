@@ -100,9 +100,10 @@ __global__ __launch_bounds__(512) void mla_fp8q_partial_kernel(PartialParams p, 
   // contiguous run of (slot, row block) work items.
   const int xcd = blockIdx.x & 7;
   const int gidx = xcd * per_xcd + int(blockIdx.x >> 3);
-  if (gidx >= p.total_wg) return;
-  const int rb = gidx % p.row_blocks;
-  const int slot = gidx / p.row_blocks;
+  // a row block of the plan (kBlockRows rows) is two workgroups of kRows
+  if (gidx >= 2 * p.total_wg) return;
+  const int rb = gidx % (2 * p.row_blocks);
+  const int slot = gidx / (2 * p.row_blocks);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -434,11 +435,12 @@ __global__ __launch_bounds__(512) void mla_fp8q_partial_kernel(PartialParams p, 
   __builtin_amdgcn_s_waitcnt(0x0F70);                      // vmcnt(0)
 
   store_rows(p, o, rowv, qg, hf, b, slot, nsplit, m_ref, m_true, l_run, ring);
-  if (p.debug && tid == 0) store_debug(p, slot, rb, b, split, s, e, dbg_groups, dbg_xor, dbg_sum);
+  if (p.debug && tid == 0 && (rb & 1) == 0)
+    store_debug(p, slot, rb >> 1, b, split, s, e, dbg_groups, dbg_xor, dbg_sum);
 }
 
 hipError_t launch_mla_fp8q_partial(const PartialParams& p, hipStream_t stream) {
-  const int per_xcd = (p.total_wg + 7) / 8;
+  const int per_xcd = (2 * p.total_wg + 7) / 8;
   const dim3 grid(unsigned(per_xcd * 8)), block(512);
   hipLaunchKernelGGL(mla_fp8q_partial_kernel, grid, block, 0, stream, p, per_xcd);
   return hipGetLastError();

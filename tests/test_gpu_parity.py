@@ -15,6 +15,8 @@ from oracle import plan as oplan
 from tests.gpu_helpers import (ATOL_LSE, assert_close, check_guards, log, session_for, to_np,
                                tolerances, pack_half_rows, unpack_half_rows)
 
+MLA_RPW = oplan.ROWS_PER_WG_MLA     # query rows of an MLA row block
+
 pytestmark = pytest.mark.gpu
 
 
@@ -320,7 +322,7 @@ def test_mla_small_full_compare(n):
     sess, _ = session_for(case, requested_splits=n, debug=True)
     sess.decode()
     _check_full(case, sess, f"mla n={n}")
-    _check_debug(case, sess, 1, 12)
+    _check_debug(case, sess, 1, -(-768 // MLA_RPW))
 
 
 def test_mla_tiles_cut_by_ranges_and_pages():
@@ -334,7 +336,7 @@ def test_mla_tiles_cut_by_ranges_and_pages():
     assert [tuple(r[2:]) for r in sess.slot_info_host] == [(0, 656), (656, 1328), (1328, 2000)]
     sess.decode()
     _check_full(case, sess, "mla L=2000 n=3")
-    _check_debug(case, sess, 1, 12)
+    _check_debug(case, sess, 1, -(-768 // MLA_RPW))
 
 
 def test_mla_short_causal_edge():
@@ -546,7 +548,7 @@ def test_mla_sequences_shorter_than_the_draft(n):
     sess, _ = session_for(case, requested_splits=n, debug=True)
     sess.decode()
     _check_full(case, sess, f"mla short n={n}")
-    _check_debug(case, sess, 1, 12)
+    _check_debug(case, sess, 1, -(-768 // MLA_RPW))
 
 
 # ---------------------------------------------------------------------------
@@ -562,7 +564,7 @@ def test_mla_fp8_small_full_compare(n):
     sess, _ = session_for(case, requested_splits=n, debug=True)
     sess.decode()
     _check_full(case, sess, f"mla e4m3 n={n}")
-    _check_debug(case, sess, 1, 12)
+    _check_debug(case, sess, 1, -(-768 // MLA_RPW))
 
 
 def test_mla_fp8_tiles_cut_by_ranges_and_pages():
@@ -572,7 +574,7 @@ def test_mla_fp8_tiles_cut_by_ranges_and_pages():
     sess, _ = session_for(case, requested_splits=3, debug=True)
     sess.decode()
     _check_full(case, sess, "mla e4m3 L=2000 n=3")
-    _check_debug(case, sess, 1, 12)
+    _check_debug(case, sess, 1, -(-768 // MLA_RPW))
 
 
 @pytest.mark.parametrize("n", [1, 4])
@@ -585,7 +587,7 @@ def test_mla_fp8_sequences_shorter_than_the_draft(n):
     sess, _ = session_for(case, requested_splits=n, debug=True)
     sess.decode()
     _check_full(case, sess, f"mla e4m3 short n={n}")
-    _check_debug(case, sess, 1, 12)
+    _check_debug(case, sess, 1, -(-768 // MLA_RPW))
 
 
 def test_mla_fp8_full_size_sampled():
@@ -616,7 +618,7 @@ def test_mla_fp8q_small_full_compare(n):
     sess, _ = session_for(case, requested_splits=n, debug=True)
     sess.decode()
     _check_full(case, sess, f"mla fp8q n={n}")
-    _check_debug(case, sess, 1, 12)
+    _check_debug(case, sess, 1, -(-768 // MLA_RPW))
 
 
 def test_mla_fp8q_tiles_cut_by_ranges_and_pages():
@@ -626,7 +628,7 @@ def test_mla_fp8q_tiles_cut_by_ranges_and_pages():
     sess, _ = session_for(case, requested_splits=3, debug=True)
     sess.decode()
     _check_full(case, sess, "mla fp8q L=2000 n=3")
-    _check_debug(case, sess, 1, 12)
+    _check_debug(case, sess, 1, -(-768 // MLA_RPW))
 
 
 @pytest.mark.parametrize("n", [1, 4])
@@ -639,7 +641,7 @@ def test_mla_fp8q_sequences_shorter_than_the_draft(n):
     sess, _ = session_for(case, requested_splits=n, debug=True)
     sess.decode()
     _check_full(case, sess, f"mla fp8q short n={n}")
-    _check_debug(case, sess, 1, 12)
+    _check_debug(case, sess, 1, -(-768 // MLA_RPW))
 
 
 @pytest.mark.parametrize("T,Hq,L,n", [(1, 128, 3000, 4), (2, 16, 777, 3), (3, 40, 1500, 0)])
@@ -650,7 +652,7 @@ def test_mla_fp8q_other_shapes(T, Hq, L, n):
     sess, _ = session_for(case, requested_splits=n, debug=True)
     sess.decode()
     _check_full(case, sess, f"mla fp8q T={T} Hq={Hq}")
-    _check_debug(case, sess, 1, -(-(T * Hq) // 64))
+    _check_debug(case, sess, 1, -(-(T * Hq) // MLA_RPW))
 
 
 def test_mla_fp8q_saturating_scale_strided_query_nhd_cache():
@@ -667,7 +669,7 @@ def test_mla_fp8q_saturating_scale_strided_query_nhd_cache():
     sess, _ = session_for(case, requested_splits=4, layout="NHD", q_pad_heads=3, debug=True)
     sess.decode()
     _check_full(case, sess, "mla fp8q saturating q_scale, NHD, strided q")
-    _check_debug(case, sess, 1, 12)
+    _check_debug(case, sess, 1, -(-768 // MLA_RPW))
 
 
 @pytest.mark.parametrize("path", ["gqa-bf16", "gqa-e4m3", "mla-bf16", "mla-e4m3", "mla-e4m3-queries"])
@@ -692,7 +694,7 @@ def test_rows_without_visible_keys_beside_visible_ones(path):
         case = synth.make_case("mixed-visibility-mla", B=2, T=3, Hq=40, Hkv=1, d_qk=576, d_v=512,
                                seq_lens=[2, 300], page_size=64, mla=True, std=0.5, seed=34, kv_dtype=kv,
                                fp8_queries=path.endswith("queries"))
-        n, blocks, hkv = 1, 2, 1
+        n, blocks, hkv = 1, -(-(3 * 40) // MLA_RPW), 1
     log(f"{path}: rows with and without visible keys in one block, n={n}")
     sess, _ = session_for(case, requested_splits=n, debug=True)
     sess.decode()
@@ -771,7 +773,7 @@ def test_mla_random_shapes(seed, mode):
     sess, _ = session_for(case, requested_splits=n, debug=True)
     sess.decode()
     _check_full(case, sess, f"mla {mode} random seed={seed}")
-    _check_debug(case, sess, 1, -(-(T * Hq) // 64))
+    _check_debug(case, sess, 1, -(-(T * Hq) // MLA_RPW))
 
 
 def test_mla_fp8q_full_size_sampled():
@@ -801,4 +803,4 @@ def test_mla_other_shapes(T, Hq, L, n, kv_dtype):
     sess, _ = session_for(case, requested_splits=n, debug=True)
     sess.decode()
     _check_full(case, sess, f"mla {kv_dtype} T={T} Hq={Hq}")
-    _check_debug(case, sess, 1, -(-(T * Hq) // 64))
+    _check_debug(case, sess, 1, -(-(T * Hq) // MLA_RPW))

@@ -76,10 +76,10 @@ def test_auto_plan_invariants():
     for _ in range(150):
         B = int(rng.integers(1, 40))
         lens = rng.integers(0, 200000, size=B).tolist()
-        for (T, Hq, Hkv, rpw, d, elem) in [(1, 32, 8, 16, (128, 128), 2), (6, 128, 1, 64, (576, 512), 2),
+        for (T, Hq, Hkv, rpw, d, elem) in [(1, 32, 8, 16, (128, 128), 2), (6, 128, 1, 128, (576, 512), 2),
                                            (1, 16, 2, 16, (256, 256), 2), (1, 32, 4, 16, (128, 128), 1)]:
             ns = _auto(lens, T=T, Hq=Hq, Hkv=Hkv, d=d, elem=elem, rpw=rpw)
-            tb = (d[0] if rpw == 64 else d[0] + d[1]) * elem
+            tb = (d[0] * 2 if rpw == P.ROWS_PER_WG_MLA else (d[0] + d[1]) * elem)
             c_lat = max(16, int(np.floor(np.sqrt(1.5 * max(lens)))) - 1)
             for n, Lb in zip(ns, lens):
                 assert 1 <= n <= max(1, min(256, -(-Lb // 16)))
@@ -117,22 +117,30 @@ def test_auto_plan_worked_examples():
     # units -> four each, ~4512 + 130.  4/3 and half: 5 and 4 splits, single
     # workgroups of 6400 and 8000 tokens.  One round wins.
     assert _auto([32000] * 8, Hq=32, Hkv=4, d=(128, 128), elem=1) == [8] * 8
-    # MLA decode at L=65536 (T=6, 128 heads -> units = 12, tb = 1152; an MLA
-    # partial row is 2 x 512 bytes of codes and 16 of m, l and two scales):
-    # c_lat = isqrt(98304) = 313; one round: c = 786432/256 = 3072 -> 21
-    # splits, 252 workgroups of up to 3136 tokens -> 3165 + merge 114 (21
-    # slots x 768 rows x 1040 B written and read, over 256 x 1152 B);
-    # balanced: c = 768 -> 86 splits, 1032 workgroups, about four per unit;
-    # 4/3: 16 splits of 4096 -> 4125 + 87.  One round wins.
-    assert _auto([65536], T=6, Hq=128, Hkv=1, d=(576, 512), rpw=64) == [21]
-    # The same at L=2048, where the merge decides: one round, c = 96 -> 21
-    # splits of 96-112 tokens -> 141 + 114 = 255; 4/3, c = 128 -> 16 splits of
-    # 128 -> 157 + 87 = 244; half, c = 192 -> 10 splits of up to 208 -> 237 +
-    # 55 = 292; balanced, c = 55 -> 38 splits, 456 workgroups in two rounds:
-    # 186 + 206.  An e4m3 cache counts the same tb: a token costs the matrix
-    # work.
-    assert _auto([2048], T=6, Hq=128, Hkv=1, d=(576, 512), rpw=64) == [16]
-    assert _auto([2048], T=6, Hq=128, Hkv=1, d=(576, 512), rpw=64, elem=1) == [16]
+    # MLA decode at L=65536 (T=6, 128 heads -> 768 rows, units = 6 row blocks
+    # of 128, tb = 1152; an MLA partial row is 2 x 512 bytes of codes and 16
+    # of m, l and two scales): c_lat = isqrt(98304) = 313, W = 393216; one
+    # round: c = 1536 -> 42 splits, 252 workgroups of up to 1568 tokens ->
+    # 1597 + merge 228 (42 slots x 768 rows x 1040 B written and read, over
+    # 256 x 1152 B) = 1825; 4/3: c = 2048 -> 32 splits of 2048 -> 2077 + 174;
+    # half: 21 splits -> 3165 + 114; balanced: c = 384 -> 171 splits, 1026
+    # workgroups, about four per unit -> 2001 + 927.  One round wins.
+    assert _auto([65536], T=6, Hq=128, Hkv=1, d=(576, 512), rpw=128) == [42]
+    # The same at L=2048, where the merge decides: c_lat = c = 55.  One round:
+    # 37 splits -> 93 + 201 = 294; balanced: 38 splits -> 93 + 206; 4/3, c =
+    # 74: 27 splits -> 109 + 147 = 256; half, c = 110: 18 splits of 112 or 128
+    # tokens -> 157 + 98 = 255, the lowest.  An e4m3 cache counts the same
+    # tb: a token costs the matrix work.
+    assert _auto([2048], T=6, Hq=128, Hkv=1, d=(576, 512), rpw=128) == [18]
+    assert _auto([2048], T=6, Hq=128, Hkv=1, d=(576, 512), rpw=128, elem=1) == [18]
+    # At L=4096 the compact partial row decides between two candidates:
+    # c_lat = 78, c = 96.  One round: 42 splits -> 141 + 228 = 369; 4/3, c =
+    # 128: 32 splits of 128 tokens -> 157 + 174 (51118080 B) = 331, the
+    # lowest; half: 21 splits of 192 -> 237 + 114 = 351; balanced: 53 splits
+    # -> 218 + 288.  Priced at the fp32 row of the grouped-query kernels (514
+    # x 4 B) the merges would double (4/3: 157 + 343 = 500; half: 237 + 225 =
+    # 462) and half would win with 21.
+    assert _auto([4096], T=6, Hq=128, Hkv=1, d=(576, 512), rpw=128) == [32]
     # Unequal lengths on 4 units (Hq = Hkv = 1 -> units = 1; D=128 bf16, overhead
     # 64): lens 4096, 3000, 200, 200, W = 7496, c_lat = 78.  One round: c = 1874
     # -> [2, 1, 1, 1]; the 3000-token workgroup alone costs 3064.  Balanced:
@@ -141,14 +149,6 @@ def test_auto_plan_worked_examples():
     # and its merge (16 partials of 130 fp32, 16640 B over 4 x 512) adds 9.
     # 4/3 and half leave every sequence whole: 4160.
     assert _auto([4096, 3000, 200, 200], Hq=1, Hkv=1, d=(128, 128), cus=4) == [9, 7, 1, 1]
-    # The merge term on 8 units: the MLA shape at 2048 tokens.  One round: c =
-    # 24576 / 8 = 3072 > 2048 -> 1 split, 12 workgroups of 29 + 2048 = 2077 ->
-    # two rounds end at 4154.  Balanced: c = 768 -> 3 splits, 36 workgroups of
-    # 701-717 tokens, four or five per unit (3553), and a merge of 3 x 768
-    # rows x 1040 B written and read over 8 x 1152 B: 520 -> 4073, which wins;
-    # priced at the fp32 row of the grouped-query kernels (514 x 4 B) the
-    # merge would cost 1028 and no split would win.
-    assert _auto([2048], T=6, Hq=128, Hkv=1, d=(576, 512), rpw=64, cus=8) == [3]
     # max_splits caps the count; nblk caps short sequences
     assert _auto([5900], mx=16) == [16]
     assert _auto([0, 0]) == [1, 1]
