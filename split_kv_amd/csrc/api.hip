@@ -15,8 +15,7 @@
 namespace splitkv {
 
 hipError_t launch_gqa_partial(const PartialParams& p, int D, bool fp8, bool fused, hipStream_t stream);
-hipError_t launch_mla_partial(const PartialParams& p, bool fp8, hipStream_t stream);
-hipError_t launch_mla_fp8q_partial(const PartialParams& p, hipStream_t stream);
+hipError_t launch_mla_partial(const PartialParams& p, int kind, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
 hipError_t launch_e4m3_to_bf16(const uint8_t* in, uint16_t* out, int64_t n, hipStream_t stream);
 
@@ -199,6 +198,10 @@ PartialParams make_partial_params(const splitkv_args& a, Kind kind, int row_bloc
   p.qsb = a.q_stride_b;
   p.qst = a.q_stride_t;
   p.qsh = a.q_stride_h;
+  // rows (t, h) of a sequence evenly spaced: the MLA kernel reads them with
+  // 32-bit byte offsets from the sequence's query
+  p.q_rows_linear = kind == Kind::Mla && a.q_stride_h >= 0 && a.q_stride_t == int64_t(a.Hq) * a.q_stride_h &&
+                    (int64_t(a.T) * a.Hq - 1) * a.q_stride_h * 2 + 2 * 576 < (int64_t(1) << 31);
   p.k = static_cast<const uint8_t*>(a.k_cache);
   p.v = kind == Kind::Mla ? p.k : static_cast<const uint8_t*>(a.v_cache);
   p.ksp = a.k_stride_page * elem;
@@ -224,6 +227,7 @@ PartialParams make_partial_params(const splitkv_args& a, Kind kind, int row_bloc
   p.page_shift = (a.page_size & (a.page_size - 1)) == 0 ? __builtin_ctz(unsigned(a.page_size)) : -1;
   const bool q8 = a.q_dtype == SPLITKV_Q_E4M3;
   p.q_scale = q8 ? a.q_scale : 1.f;
+  p.q_rcp = p.q_scale >= 0x1p-64f && p.q_scale <= 0x1p64f ? 1.f / p.q_scale : 0.f;
   p.scale_log2 = a.scale * a.k_scale * p.q_scale * kLog2e;
   p.v_scale = a.v_scale;
   const Layout w = workspace_layout(a);
@@ -257,10 +261,8 @@ splitkv_status run_partial(const splitkv_args* a, Kind kind, bool direct, void* 
   hipError_t err;
   if (kind != Kind::Mla)
     err = launch_gqa_partial(p, a->d_qk, kind == Kind::GqaFp8, fused, s);
-  else if (a->q_dtype == SPLITKV_Q_E4M3)
-    err = launch_mla_fp8q_partial(p, s);
   else
-    err = launch_mla_partial(p, a->kv_dtype == SPLITKV_KV_E4M3, s);
+    err = launch_mla_partial(p, a->q_dtype == SPLITKV_Q_E4M3 ? 2 : a->kv_dtype == SPLITKV_KV_E4M3 ? 1 : 0, s);
   if (err != hipSuccess) return fail(SPLITKV_ERR_LAUNCH, "%s: launch failed: %s", fn, hipGetErrorString(err));
   return SPLITKV_OK;
 }

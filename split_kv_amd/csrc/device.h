@@ -26,6 +26,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 struct PartialParams {
   const uint16_t* q;            // bf16 codes
   int64_t qsb, qst, qsh;        // element strides
+  int32_t q_rows_linear;        // MLA: row r = t * Hq + h at r * qsh (qst == Hq * qsh), byte offsets < 2^31
   const uint8_t* k;             // cache base, as bytes
   const uint8_t* v;
   int64_t ksp, ksh, kst;        // byte strides
@@ -40,6 +41,7 @@ struct PartialParams {
   int32_t page_shift;           // log2(page_size) when it is a power of two, else -1
   float scale_log2;             // scale * k_scale * log2(e) (times q_scale for e4m3 queries)
   float q_scale;                // e4m3 queries: codes of q / q_scale
+  float q_rcp;                  // RN(1 / q_scale) when 2^-64 <= q_scale <= 2^64, else 0
   float v_scale;
   float* part_m;                // [S][T*Hq]
   float* part_l;
@@ -138,6 +140,40 @@ __device__ __forceinline__ u32x2 quantise8(u32x4 w, float s) {
     if (h) r.y = uint32_t(c); else r.x = uint32_t(c);
   }
   return r;
+}
+
+// The same codes without a division per value, given r = RN(1 / s) and
+// 2^-64 <= s <= 2^64.  For x = |value| the quotient estimate q0 = RN(x r)
+// is corrected once by the exact remainder: q1 = RN(q0 + RN(x - s q0) r),
+// both steps fused multiply-adds.  For a numerator with at most 8 significant
+// bits (every bf16 value) q1 is the correctly rounded fp32 quotient x / s:
+// the check runs every fp32 significand of s against every bf16 significand
+// of x (2^30 pairs, none differs), and the rounding steps scale with the
+// exponents as long as the values that decide a code (quotients from 2^-12
+// to 448, whose remainders are near x 2^-24) stay normal, which the bounds on
+// s guarantee.  Quotient estimates above 448 (the exact quotient then rounds
+// to the 448 code too; infinite x gives one) saturate; NaN stays NaN; the
+// sign bit of each value is copied onto its code, so -0 keeps its own code.
+__device__ __forceinline__ u32x2 quantise8_rcp(u32x4 w, float s, float r) {
+  u32x2 res;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t a = h ? w.z : w.x, b = h ? w.w : w.y;
+    float f[4] = {__uint_as_float((a << 16) & 0x7fffffffu), __uint_as_float(a & 0x7fff0000u),
+                  __uint_as_float((b << 16) & 0x7fffffffu), __uint_as_float(b & 0x7fff0000u)};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float q0 = f[i] * r;
+      const float q1 = __builtin_fmaf(__builtin_fmaf(-s, q0, f[i]), r, q0);
+      f[i] = q0 > kE4m3Max ? kE4m3Max : q1;
+    }
+    int c = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+    c = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], c, true);
+    // sign bits: bit 7 of bytes 1 and 3 of a and of b, to bytes 0 .. 3
+    const uint32_t sg = __builtin_amdgcn_perm(b, a, 0x07050301u) & 0x80808080u;
+    if (h) res.y = uint32_t(c) | sg; else res.x = uint32_t(c) | sg;
+  }
+  return res;
 }
 
 // Lane-exchange helpers within a 64-wide wavefront.

@@ -2,41 +2,54 @@
 // by every query head; the value is the first 512 columns of the same row
 // ("Shipped: 484.5 tok/s on one GB300 ...", table "What shipped": split-KV
 // MLA decode of one request at six speculative tokens, causal within them).
+// One kernel body, three cache/query kinds (KIND):
+//   0: bf16 latent cache, bf16 queries;
+//   1: e4m3 latent cache (one per-tensor scale, "Xqa decode kernels", section
+//      "Purpose"), bf16 queries;
+//   2: e4m3 latent cache and e4m3 queries, quantised here to codes of
+//      q / q_scale, so the scores run on the FP8 matrix instruction (the
+//      pages' FP8-Q path, "Xqa decode kernels", timeline: the FP8-Q selection).
 //
-// Unlike the grouped-query kernel this one is bound by matrix throughput:
-// every cached token meets all T*Hq query rows (768 in the six-token,
-// 128-head shape), 1,671,168 FLOPs per 1152-byte row.  What limits such a
-// kernel is how many FLOPs each byte moved into and out of LDS buys, so a
-// workgroup keeps 128 query rows -- each cache tile is brought on chip once
-// for twice as many rows as with 64 -- and each of its four waves (one per
-// SIMD) owns 32 whole rows: the query's 576 features (144 VGPRs) and the
-// output's 512 (256 accumulation registers).  A 32-row wave multiplies on the
-// 32x32x16 bf16 matrix instruction, whose operands are twice as wide as the
-// 16x16 form's, so one 16-byte read from LDS feeds twice the work, and no
-// wave shares a row with another: no partial-score exchange, one workgroup
-// barrier per tile.
+// Every cached token meets all T*Hq query rows (768 in the six-token,
+// 128-head shape), 1,671,168 FLOPs per latent row.  What bounds such a kernel
+// on gfx950 is the bytes it reads out of LDS per FLOP (an LDS read returns
+// ~100 bytes a clock per CU for 16-byte reads, ~80 for transposing ones,
+// against 4096 FLOPs a clock of bf16 matrix work), so a workgroup keeps 128
+// query rows -- each cache tile is brought on chip once for all of them --
+// and each of its four waves (one per SIMD) owns 32 whole rows: the query in
+// registers (the bf16 query's 64 rope features in LDS) and O's 32 rows x 512
+// features in all 256 accumulation registers.  The products are the 32x32
+// forms (v_mfma_f32_32x32x16_bf16, and v_mfma_f32_32x32x64_f8f6f4 for the
+// e4m3-query scores), whose operands feed twice the work of the 16x16 forms
+// per byte read.  No wave shares a row: no partial-score exchange, one
+// workgroup barrier per tile.
 //   * Tiles of 32 tokens arrive by direct global->LDS loads (16 bytes per
-//     lane, no register staging) into a ring of four, three tiles ahead of
-//     the one being computed.
-//   * A token's 72 16-byte chunks are stored unpadded, chunk c of tile token
-//     t at position c ^ swz(t) (a permutation inside each aligned group of
-//     eight), which keeps both operand reads free of bank conflicts: the
-//     key reads (one chunk of 32 tokens per 32 lanes) and the transposing
-//     value reads (4 tokens x 64 bytes per 32 lanes).
-//   * Per tile: S^T[token][row] = K Q^T (36 products over 16 features each,
-//     the K operand read from LDS a few products ahead), the online softmax
-//     in base 2 (lazily moved reference max) over the tile's 32 tokens, then
-//     O^T[d][row] += V^T P^T (32 products, 16 tokens each), the V^T operand
-//     read straight from the token-major tile with the gfx950 transposing
-//     LDS read (ds_read_b64_tr_b16: a 16-lane group that points at 4 tokens
-//     x 16 consecutive features receives, in lane x, feature x of the 4
-//     tokens).  P needs no data movement: the inner dimension of the second
-//     product may list the tokens in any order shared by both operands, and
-//     the order chosen is the one the scores come out in.
-// An e4m3 latent cache (bf16 queries, "Xqa decode kernels", section
-// "Purpose") runs the same tile code: its codes, half the bytes, arrive the
-// same way into a four-deep code ring and are widened exactly to bf16 at the
-// start of each step into a two-deep ring of bf16 tiles laid out as above.
+//     lane, no register staging) into a ring, several tiles ahead of the one
+//     being computed.  An e4m3 tile holds the codes themselves, half the
+//     bytes of bf16: the operands are read as codes and widened exactly to
+//     bf16 in registers (v_cvt_scalef32_pk_bf16_fp8), which halves the LDS
+//     reads; with e4m3 queries the score operands are the codes.
+//   * Token rows are stored unpadded, 16-byte chunk c of tile token t at a
+//     swizzled position inside an aligned group of chunks, which keeps every
+//     operand read free of bank conflicts.
+//   * Per tile: S^T[token][row] = K Q^T (the K operand read from LDS a few
+//     products ahead), the online softmax in base 2 (lazily moved reference
+//     max) over the tile's 32 tokens, then O^T[d][row] += V^T P^T (32
+//     products of 16 tokens), the V^T operand read straight from the
+//     token-major tile with the gfx950 transposing LDS reads
+//     (ds_read_b64_tr_b16 for bf16: a 16-lane group that points at 4 tokens
+//     x 16 features receives, in lane x, feature x of the 4 tokens;
+//     ds_read_b64_tr_b8 for codes: lane x receives byte x & 7 of the 8-byte
+//     vectors read by lanes 2j + (x >> 3), j = 0..7, i.e. one feature of 8
+//     tokens).  P needs no data movement: the inner dimension of the value
+//     product lists the tile's tokens in the order the scores come out in.
+//     P enters it as bf16 in every kind: with e4m3 queries the FP8
+//     instruction serves the scores, and the value product runs on bf16
+//     operands like the others' (V widened from its codes).
+//   * The bf16 query is staged through LDS in a bf16 tile's layout by loads
+//     of 1 KiB of consecutive rows (loaded straight into the operand layout,
+//     every load would touch 32 rows); e4m3 queries are quantised in
+//     registers with an exact division-free quotient.
 // Workgroups of one split are placed on one XCD (dispatch is round-robin over
 // the eight XCDs), so the row blocks' reads of a tile share that XCD's L2.
 // The block-table entries a tile fill needs are read one step ahead, so the
@@ -48,102 +61,98 @@ namespace splitkv {
 namespace {
 
 using namespace mla;
-constexpr int kWRows = SPLITKV_ROWS_PER_WG_MLA;  // 128 query rows per workgroup
-constexpr int kWWaves = 4;                       // one per SIMD, 32 rows each
-static_assert(kWRows == 32 * kWWaves, "32 rows per wave");
-constexpr int kTile = 32;                        // tokens per LDS tile
-constexpr int kPitch = kDqk * 2 / 16;            // 72 16-byte chunks per token row, unpadded
-constexpr int kTileLoads = kTile * kPitch / 64;  // 36 wave-level 1 KiB loads
-constexpr int kLoadsPerWave = kTileLoads / kWWaves;   // 9
-static_assert(kLoadsPerWave * kWWaves == kTileLoads, "every wave issues the same loads per tile");
-constexpr int kSlotBytes = kTileLoads * 1024;    // 36864
-constexpr int kRing = 4;
-// e4m3 cache: a tile's codes (32 x 576 bytes) are 18 wave-level loads; waves
-// 0-1 issue five, waves 2-3 four plus a repeat of their fourth, so every wave
-// issues five.  The codes land in a four-deep staging ring and are widened
-// into a two-deep ring of bf16 tiles laid out as above.
-constexpr int kF8Pitch = kDqk / 16;                   // 36 16-byte chunks per code row
-constexpr int kF8TileLoads = kTile * kDqk / 1024;     // 18
-constexpr int kF8LoadsPerWave = 5;
-constexpr int kF8StageBytes = kF8TileLoads * 1024;    // 18432
-constexpr int kPoolBytes = kRing * kSlotBytes;        // 147456 either way
-static_assert(2 * kSlotBytes + 4 * kF8StageBytes == kPoolBytes, "e4m3 rings fill the pool");
-static_assert((kF8LoadsPerWave - 1) * kWWaves < kF8TileLoads && kF8LoadsPerWave * kWWaves >= kF8TileLoads,
-              "five loads per wave cover an e4m3 tile");
-constexpr int kQk = kDqk / 16;                   // 36 products of 16 key features
-constexpr int kQkReg = kDv / 16;                 // 32 of them take the query from registers; the
-                                                 // rope features' 4 take it from LDS
-constexpr int kVb = kDv / 32;                    // 16 blocks of 32 value features
-constexpr int kKAhead = 4;                       // K operand reads in flight ahead of their product
-constexpr int kVAhead = 4;                       // products whose V operands are in flight
-// Epilogue staging of the compact partial: 128 rows of 512 int16 codes, row
-// pitch 1040 bytes.
-constexpr int kCodeRowBytes = 1040;
-static_assert(kWRows * kCodeRowBytes <= kPoolBytes, "the code staging fits the tile pool");
-constexpr int kQRopeBytes = kWWaves * (kQk - kQkReg) * 1024;   // 16384
-static_assert(kPoolBytes + kQRopeBytes <= 160 * 1024, "tile pool and rope query fit the LDS");
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
-__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+// Tile geometry of each kind.
+template <int KIND>
+struct Geo {
+  static constexpr bool kCodes = KIND != 0;                            // the tile holds e4m3 codes
+  static constexpr int kChunks = kCodes ? kDqk / 16 : kDqk * 2 / 16;   // 36 or 72 16-byte chunks a row
+  static constexpr int kRowBytes = 16 * kChunks;                       // 576 or 1152
+  static constexpr int kLoads = kTile * kChunks / 64;                  // 18 or 36 wave-level 1 KiB loads
+  static constexpr int kLPW = (kLoads + kWWaves - 1) / kWWaves;        // 5 or 9 loads per wave and tile
+  static constexpr int kSlotBytes = kLoads * 1024;                     // 18432 or 36864
+  static constexpr int kRing = kCodes ? 8 : 4;                         // tile slots
+  static constexpr int kAhead = kCodes ? 6 : 3;                        // tiles filled ahead of the one computed
+  static constexpr int kPoolBytes = kRing * kSlotBytes;                // 147456 either way
+  static_assert(kAhead < kRing && kAhead * kLPW < 64, "fills in flight fit the ring and the counter");
+  static_assert(kStageBytes <= kPoolBytes, "the epilogue's staging fits the tile pool");
+};
+
+// bf16 tiles: chunk c of token t at position c ^ swz_bf16(t) (3 bits, inside
+// each aligned group of eight).  The eight tokens of one residue mod 4 (whose
+// rows start on the same bank at the 1152-byte pitch) take eight different
+// values, so the 32 lanes of a key read (one chunk of 32 tokens) hit 32
+// different 16-byte bank groups; tokens t and t + 2 of an aligned group of
+// four differ in bit 2, so the four 64-byte pieces of a transposing read
+// land in the four different quarters of the 256 bytes of banks it is served
+// from.
+__device__ __forceinline__ uint32_t swz_bf16(uint32_t t) { return ((t >> 2) ^ ((t & 2u) << 1)) & 7u; }
+// e4m3 tiles: chunk c of token t at position 4 (c >> 2) + ((c & 3) ^
+// swz_e4m3(t)) (2 bits, inside each aligned group of four).  At the 576-byte
+// pitch tokens t and t + 8 start on the same bank: tokens t, t + 8, t + 16,
+// t + 24 take four different values, so a key read's 32 lanes (one chunk of
+// 32 tokens) hit 32 bank groups; and tokens t and t + 8 differ in bit 1, so
+// the eight 32-byte pieces of a transposing byte read (8 tokens x 32
+// features) fill its 256 bytes of banks.
+__device__ __forceinline__ uint32_t swz_e4m3(uint32_t t) { return (((t >> 3) & 1u) << 1) | ((t >> 4) & 1u); }
+
+// D += A B over 64 e4m3 inner elements (both operands e4m3: format codes 0;
+// with both scale operands zero the compiler emits the unscaled instruction).
+__device__ __forceinline__ f32x16 mma64(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
-// Position swizzle of tile token t's chunks (t in 0..31, 3 bits): the eight
-// tokens of one residue mod 4 (whose rows start on the same bank, the row
-// pitch being 1152 bytes) take eight different values, so the 32 lanes of a
-// key read hit 32 different 16-byte bank groups; and tokens t and t + 2 of
-// an aligned group of four differ in bit 2, so the four 64-byte pieces of a
-// transposing read land in the four different quarters of the 256 bytes of
-// banks it is served from.
-__device__ __forceinline__ uint32_t swz(uint32_t t) { return ((t >> 2) ^ ((t & 2u) << 1)) & 7u; }
-
-// Max and sum over the two lanes l and l ^ 32 (one row of the 32x32 result).
-__device__ __forceinline__ float pair_max(float v) {
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-}
-__device__ __forceinline__ float pair_sum(float v) {
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+// Eight e4m3 codes (two dwords) to eight bf16 values, exactly.
+__device__ __forceinline__ bf16x8 widen8(uint32_t lo, uint32_t hi) {
+  const u32x2 a = e4m3x4_to_bf16x4(lo), b = e4m3x4_to_bf16x4(hi);
+  return __builtin_bit_cast(bf16x8, u32x4{a.x, a.y, b.x, b.y});
 }
 
-// acc *= a for an accumulator held in the accumulation registers, one
-// register at a time (read, multiply, write back): written as whole-vector
-// arithmetic, the compiler copies every accumulator out at once, which does
-// not fit beside the query.
-__device__ __forceinline__ void scale_acc(f32x16& acc, float a) {
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    float tmp;
-    asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
-                 : "+a"(acc[v]), "=&v"(tmp)
-                 : "v"(a));
+// s_waitcnt vmcnt(kLPW * n) for a uniform n in 0..6.
+template <int kLPW>
+__device__ __forceinline__ void wait_tiles(int n) {
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); break;
+    case 1: __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLPW)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kLPW)); break;
+    case 3: __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * kLPW < 64 ? 3 * kLPW : 63)); break;
+    case 4: __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * kLPW < 64 ? 4 * kLPW : 63)); break;
+    case 5: __builtin_amdgcn_s_waitcnt(vmcnt_imm(5 * kLPW < 64 ? 5 * kLPW : 63)); break;
+    default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(6 * kLPW < 64 ? 6 * kLPW : 63)); break;
   }
 }
 
-// s_waitcnt immediate for vmcnt(n) alone (n < 64).
-constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+constexpr int kVAhead = 4;                       // value products whose operands are in flight
+constexpr int kQRopeBytes = 16384;               // bf16 queries: 64 rope features x 32 rows x 4 waves
 
 }  // namespace
 
-template <bool FP8>
+template <int KIND>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_partial_kernel(PartialParams p, int per_xcd) {
-  // bf16: four tile slots.  e4m3: two bf16 tile slots, then four code slots.
-  __shared__ __attribute__((aligned(1024))) uint8_t pool[kPoolBytes];
-  // the query's 64 rope features, in the operand layout: wave w, product
-  // it - 32, lane j at qrope + 1024 (4 w + it - 32) + 16 j
-  __shared__ __attribute__((aligned(1024))) uint8_t qrope[kQRopeBytes];
-  constexpr int kLPW = FP8 ? kF8LoadsPerWave : kLoadsPerWave;   // loads per wave and tile
+  using G = Geo<KIND>;
+  constexpr bool kCodes = G::kCodes;
+  constexpr bool kQ8 = KIND == 2;
+  constexpr int kLPW = G::kLPW;
+  constexpr int kAhead = G::kAhead;
+  constexpr int kRowBytes = G::kRowBytes;
+  // the tile ring; the epilogue's staging once the tile loop is done
+  __shared__ __attribute__((aligned(1024))) uint8_t pool[G::kPoolBytes];
+  // bf16 queries: the query's 64 rope features, in the score operand layout
+  // (kept out of the registers, which bound this layout): wave w, operand
+  // block i (0..3), lane j at qrope + 4096 w + 1024 i + 16 j
+  __shared__ __attribute__((aligned(1024))) uint8_t qrope[kQ8 ? 16 : kQRopeBytes];
+  static_assert(G::kPoolBytes + kQRopeBytes <= 160 * 1024, "tile pool and rope query fit the LDS");
   auto tile_slot = [&](int k) __attribute__((always_inline)) {
-    return pool + (FP8 ? (k & 1) : (k & 3)) * kSlotBytes;
-  };
-  auto fill_slot = [&](int k) __attribute__((always_inline)) {
-    return FP8 ? pool + 2 * kSlotBytes + (k & 3) * kF8StageBytes : pool + (k & 3) * kSlotBytes;
+    return pool + (k & (G::kRing - 1)) * G::kSlotBytes;
   };
 
   // XCD-aware placement: block id i runs on XCD i % 8; give each XCD a
@@ -164,27 +173,11 @@ void mla_partial_kernel(PartialParams p, int per_xcd) {
   const int L = ((cint32*)p.seq_lens)[b];
 
   // This lane's query row (column of the S^T tiles); rows past the last one
-  // read row rows-1 and are never stored.  Lane (r32, h) holds features
-  // 16 it + 8 h .. +7 of the row for the product it: in registers for the
-  // 512 latent features, in LDS for the 64 rope features (the registers are
-  // what bounds this layout).
+  // read row rows-1 and are never stored.
   const int rowv = rb * kWRows + wave * 32 + r32;
-  int limit;
-  bf16x8 q[kQkReg];
-  const lds_u8* qr = (const lds_u8*)qrope + wave * ((kQk - kQkReg) * 1024) + 16 * lane;
-  {
-    const int rc = min(rowv, p.rows - 1);
-    const int t = rc / p.Hq, hq = rc % p.Hq;
-    limit = L - p.T + t;      // last key position this row sees
-    const uint16_t* qrow = p.q + b * p.qsb + t * p.qst + hq * p.qsh + 8 * h;
-#pragma unroll
-    for (int it = 0; it < kQkReg; ++it) q[it] = *reinterpret_cast<const bf16x8*>(qrow + 16 * it);
-    // the rope part goes straight to LDS, so nothing waits for it here
-#pragma unroll
-    for (int it = kQkReg; it < kQk; ++it)
-      dma16(reinterpret_cast<const uint8_t*>(qrow + 16 * it),
-            uint32_t(size_t(qrope + wave * ((kQk - kQkReg) * 1024) + 1024 * (it - kQkReg))));
-  }
+  const int rc = min(rowv, p.rows - 1);
+  const int limit = L - p.T + rc / p.Hq;           // last key position this row sees
+  const uint16_t* qrow = p.q + b * p.qsb + (rc / p.Hq) * p.qst + (rc % p.Hq) * p.qsh;
 
   // Tiles that end at or before full_end need no mask: every token is in the
   // range and visible to every row of the wave (its first row has the
@@ -197,37 +190,33 @@ void mla_partial_kernel(PartialParams p, int per_xcd) {
   cint32* cbt = (cint32*)(p.bt + b * p.bt_stride);
   const uint32_t ksp = uint32_t(p.ksp), kst = uint32_t(p.kst);   // < 2^31, checked on the host
 
-  // Tile fill: wave w issues the wave-level loads w, w+4, ..., w+32 of the 36
-  // a tile needs.  Lane j of load i fills the 16-byte position q = 64*i + j of
-  // the slot: token q / 72, holding chunk (q % 72) ^ swz(token) of that
-  // token's row.  Tokens past the range end load the range's last token
-  // (finite, masked later).  Loads 0-17 hold tokens 0-15 and loads 18-35
-  // tokens 16-31 (16 x 72 = 18 x 64 chunks), and a 16-token half of a tile
-  // lies in one page (tiles start on multiples of 16, pages hold a power of
-  // two >= 16 tokens), so for a tile inside the range a load reads one page:
-  // its address is a uniform page base plus the lane's offset inside the
-  // half, lo[u].
-  // For an e4m3 cache, lane j of load i fills 16-byte position q = 64*i + j
-  // of the code slot in plain order: token q / 36, code bytes 16*(q % 36)
-  // .. +15 of its row; loads 0-8 hold tokens 0-15, loads 9-17 tokens 16-31;
-  // a wave with only four loads repeats its fourth (same lanes, same
-  // addresses, same bytes), so every wave's completion counts are the same.
+  // Tile fill: wave w issues the wave-level loads w, w+4, w+8, ... of those a
+  // tile needs; a wave with one fewer repeats its last (same lanes, same
+  // addresses, same bytes), so every wave issues kLPW and all waves' counts
+  // agree.  Lane j of load i fills the 16-byte position q = 64*i + j of the
+  // slot: token q / kChunks, position q % kChunks, which holds the chunk the
+  // swizzle maps there.  Tokens past the range end load the range's last
+  // token (finite, masked later).  The first half of the loads holds tokens
+  // 0-15, the second tokens 16-31 (16 rows are a whole number of 1 KiB
+  // loads), and a 16-token half of a tile lies in one page (tiles start on
+  // multiples of 16, pages hold a power of two >= 16 tokens), so for a tile
+  // inside the range a load reads one page: its address is a uniform page
+  // base plus the lane's offset inside the half, lo[u].
   const int nt = (e - s + kTile - 1) / kTile;      // tiles of the range
   auto load_index = [&](int u) __attribute__((always_inline)) {
     int i = wave + kWWaves * u;
-    if (FP8 && i >= kF8TileLoads) i -= kWWaves;
+    if (i >= G::kLoads) i -= kWWaves;
     return i;
   };
   // (token, byte offset in its row) of the chunk lane fills in load u
   auto chunk_of = [&](int u, uint32_t& tk, uint32_t& c16) __attribute__((always_inline)) {
     const uint32_t qc = uint32_t(64 * load_index(u) + lane);
-    if constexpr (FP8) {
-      tk = qc / uint32_t(kF8Pitch);
-      c16 = 16u * (qc - tk * kF8Pitch);
-    } else {
-      tk = qc / uint32_t(kPitch);
-      c16 = 16u * ((qc - tk * kPitch) ^ swz(tk));
-    }
+    tk = qc / uint32_t(G::kChunks);
+    const uint32_t pos = qc - tk * G::kChunks;
+    if constexpr (kCodes)
+      c16 = 16u * ((pos & ~3u) | ((pos & 3u) ^ swz_e4m3(tk)));
+    else
+      c16 = 16u * (pos ^ swz_bf16(tk));
   };
   uint32_t lo[kLPW];
 #pragma unroll
@@ -255,7 +244,7 @@ void mla_partial_kernel(PartialParams p, int per_xcd) {
     dbg_xor ^= pa ^ (has1 ? pb : 0);
     dbg_sum += uint32_t(pa) + (has1 ? uint32_t(pb) : 0u);
   };
-  constexpr int kHalf = (FP8 ? kF8TileLoads : kTileLoads) / 2;
+  constexpr int kHalf = G::kLoads / 2;
   // A tile inside the range: half 0 in page pa, half 1 in page pb; load u of
   // this wave is a uniform page base plus lo[u].  Split into single loads so
   // that the steps can spread them over their products.
@@ -300,6 +289,94 @@ void mla_partial_kernel(PartialParams p, int per_xcd) {
     }
   };
 
+  // The query, loaded before any tile.  bf16 (kinds 0, 1): lane (r32, h)
+  // holds 8 features of the row for each 16-feature score product, in
+  // registers for the 512 latent features and in LDS for the 64 rope features
+  // -- kind 0: features 16 i + 8 h .. +7 for product i; kind 1 (a chunk of 16
+  // codes feeds two products): features 32 m + 16 h .. +7 for product 2 m and
+  // +8 .. +15 for product 2 m + 1.  e4m3 (kind 2): codes of features 64 p +
+  // 32 h .. +31 for the 64-feature product p, all in registers.
+  constexpr int kQOps = kQ8 ? 9 : 32;              // register operands
+  bf16x8 qb[kQ8 ? 1 : kQOps];
+  i32x8 qc8[kQ8 ? kQOps : 1];
+  const lds_u8* qr = (const lds_u8*)qrope + wave * 4096 + 16 * lane;
+  if constexpr (kQ8) {
+    auto quantise_q = [&](auto FAST) __attribute__((always_inline)) {
+      constexpr bool fast = decltype(FAST)::value;
+#pragma unroll
+      for (int pp = 0; pp < kQOps; ++pp) {
+        const uint16_t* src = qrow + 64 * pp + 32 * h;
+        u32x2 c[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const u32x4 w = *reinterpret_cast<const u32x4*>(src + 8 * j);
+          c[j] = fast ? quantise8_rcp(w, p.q_scale, p.q_rcp) : quantise8(w, p.q_scale);
+        }
+        qc8[pp] = i32x8{int(c[0].x), int(c[0].y), int(c[1].x), int(c[1].y),
+                        int(c[2].x), int(c[2].y), int(c[3].x), int(c[3].y)};
+      }
+    };
+    // a division per value only for scales outside the fast path's bounds
+    if (p.q_rcp != 0.f)
+      quantise_q(std::true_type{});
+    else
+      quantise_q(std::false_type{});
+  } else {
+    // 16-byte chunk (8 features) of operand i
+    auto qchunk = [&](int i) __attribute__((always_inline)) {
+      return KIND == 0 ? 2 * i + h : 4 * (i >> 1) + 2 * h + (i & 1);
+    };
+    if (p.q_rows_linear) {
+      // Row r of the sequence's query at r * qsh: the wave's 32 rows go
+      // through its own 36 KiB of the tile pool, laid out as a bf16 key tile
+      // (chunk c of row t at position c ^ swz_bf16(t)), with loads that read
+      // 1 KiB of consecutive rows each -- loaded straight into the operand
+      // layout, every load would touch 32 rows.  The operand reads then
+      // follow the key reads' conflict-free pattern.
+      const uint8_t* qbase = reinterpret_cast<const uint8_t*>(p.q + b * p.qsb);
+      const uint32_t r0 = uint32_t(rb * kWRows + wave * 32), rlast = uint32_t(p.rows - 1);
+      const uint32_t qrb = 2u * uint32_t(p.qsh);
+      uint8_t* qs = pool + wave * (32 * 1152);
+#pragma unroll
+      for (int i = 0; i < 36; ++i) {
+        const uint32_t qpos = 64u * i + lane;
+        const uint32_t tk = qpos / 72u, c = (qpos - 72u * tk) ^ swz_bf16(tk);
+        dma16_sbase(qbase, min(r0 + tk, rlast) * qrb + 16u * c, uint32_t(size_t((lds_u8*)(qs + 1024 * i))));
+      }
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      const lds_u8* qsl = (const lds_u8*)qs + r32 * 1152;
+#pragma unroll
+      for (int i = 0; i < kQOps; ++i) qb[i] = *(const lds_bf16x8*)(qsl + 16 * (qchunk(i) ^ swz_bf16(r32)));
+#pragma unroll
+      for (int i = kQOps; i < kQOps + 4; ++i)
+        *(lds_u32x4*)(qrope + wave * 4096 + 1024 * (i - kQOps) + 16 * lane) =
+            *(const lds_u32x4*)(qsl + 16 * (qchunk(i) ^ swz_bf16(r32)));
+      // every wave has its query before the fills below reuse the pool
+      lds_barrier();
+    } else {
+#pragma unroll
+      for (int i = 0; i < kQOps; ++i) qb[i] = *reinterpret_cast<const bf16x8*>(qrow + 8 * qchunk(i));
+      // the rope operands 32..35 go straight to LDS, so nothing waits for them
+#pragma unroll
+      for (int i = kQOps; i < kQOps + 4; ++i)
+        dma16(reinterpret_cast<const uint8_t*>(qrow + 8 * qchunk(i)), uint32_t(size_t(qrope + wave * 4096 + 1024 * (i - kQOps))));
+      // the wait for the query (and with it everything issued before it) here
+#pragma unroll
+      for (int i = 0; i < kQOps; ++i) asm volatile("" ::"v"(qb[i]));
+    }
+  }
+  // the first kAhead tiles go out once the query has landed (a wait for it
+  // issued after them would wait for them too)
+  int pa = 0, pb = 0;      // pages of the tile the next fill loads
+#pragma unroll
+  for (int k = 0; k < kAhead; ++k) {
+    tile_pages(k, pa, pb);
+    if (k < nt) fill(k, tile_slot(k), pa, pb);
+  }
+  tile_pages(kAhead, pa, pb);
+
   // O^T accumulators: lane (r32, h) holds O[row r32][32 blk + 8 (v / 4) +
   // 4 h + v % 4] in o[blk][v].
   f32x16 o[kVb];
@@ -310,119 +387,188 @@ void mla_partial_kernel(PartialParams p, int per_xcd) {
   constexpr float kRescaleMargin = 8.f;
   float m_ref = -INFINITY, m_true = -INFINITY, l_run = 0.f;
 
-  // Byte offsets of this lane's K operand reads: product it reads chunk
-  // 2 it + h of token r32, at kofs[it & 3] + 128 (it >> 2).
-  uint32_t kofs[4];
+  // Byte offsets of this lane's K operand reads (token r32).  Kind 0: product
+  // it reads chunk 2 it + h at kofs[it & 3] + 128 (it >> 2).  Kind 1: read m
+  // takes chunk 2 m + h (16 codes: products 2 m and 2 m + 1) at
+  // kofs[m & 1] + 64 (m >> 1).  Kind 2: product p takes chunks 4 p + 2 h + c
+  // (c = 0, 1) at kofs[c] + 64 p.
+  uint32_t kofs[KIND == 0 ? 4 : 2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) kofs[j] = uint32_t(r32) * (kPitch * 16) + 16u * ((2u * j + h) ^ swz(r32));
+  for (int j = 0; j < (KIND == 0 ? 4 : 2); ++j) {
+    if constexpr (KIND == 0)
+      kofs[j] = uint32_t(r32) * kRowBytes + 16u * ((2u * j + h) ^ swz_bf16(r32));
+    else if constexpr (KIND == 1)
+      kofs[j] = uint32_t(r32) * kRowBytes + 16u * ((2u * j + h) ^ swz_e4m3(r32));
+    else
+      kofs[j] = uint32_t(r32) * kRowBytes + 16u * ((2u * h + j) ^ swz_e4m3(r32));
+  }
   // Byte offsets of this lane's transposing V reads.  The score result leaves
   // lane (r32, h) the tokens 8 (v / 4) + 4 h + v % 4 of row r32 in item v, so
-  // the second product's inner index 8 h + u of 16-token step kb is token
-  // 16 kb + 8 (u / 4) + 4 h + u % 4.  Its V^T operand: lane (x, g1, h)
-  // (x = lane & 15, g1 = bit 4) holds feature 32 blk + 16 g1 + x of those
-  // tokens; read r (u / 4) of step kb points the lane at token tv = 16 kb +
-  // 8 r + 4 h + x / 4, features 32 blk + 16 g1 + 4 (x & 3) .. +3: chunk
-  // c = 4 blk + 2 g1 + (x & 3) / 2, half x & 1, at position c ^ swz(tv).
-  // With swz(tv) = (4 kb + 2 r + h) ^ 4 (x >> 3), the position's offset
-  // inside the 128 bytes of blk >> 1 is 64 ((blk & 1) ^ kb ^ (x >> 3)) +
-  // 16 ((2 g1 + (x & 3) / 2) ^ (2 r + h)): four per-lane offsets
-  // vofs[(blk & 1) ^ kb][r], the rest (16 kb + 8 r tokens, 128 (blk >> 1)
-  // bytes) a constant.
+  // the value product's inner index 8 h + u of 16-token step kb is token
+  // 16 kb + 8 (u / 4) + 4 h + u % 4, and its V^T operand gives lane (x, g1, h)
+  // (x = lane & 15, g1 = bit 4) feature 32 blk + 16 g1 + x of those tokens.
+  // Kind 0, two 16-bit transposing reads: read r (u / 4) of step kb points
+  // the lane at token tv = 16 kb + 8 r + 4 h + x / 4, features 32 blk + 16 g1
+  // + 4 (x & 3) .. +3: chunk c = 4 blk + 2 g1 + (x & 3) / 2, half x & 1, at
+  // position c ^ swz_bf16(tv); with swz_bf16(tv) = (4 kb + 2 r + h) ^ 4 (x >> 3)
+  // the offset inside the 128 bytes of blk >> 1 is 64 ((blk & 1) ^ kb ^ (x >> 3))
+  // + 16 ((2 g1 + (x & 3) / 2) ^ (2 r + h)): vofs[(blk & 1) ^ kb][r], the rest
+  // (16 kb + 8 r tokens, 128 (blk >> 1) bytes) a constant.
+  // Codes, one byte transposing read: source lane x = 2 j + sh points at
+  // token tv = 16 kb + 8 (j / 4) + 4 h + j % 4, codes 32 blk + 16 g1 + 8 sh
+  // .. +7: chunk c = 2 blk + g1, half sh, at position 4 (c >> 2) + ((c & 3) ^
+  // swz_e4m3(tv)); swz_e4m3(tv) = 2 (j / 4) + kb, so the offset is 576 tv +
+  // 64 (blk >> 1) + 32 ((blk & 1) ^ (j / 4)) + 16 (g1 ^ kb) + 8 sh:
+  // vofs[kb][blk & 1] plus 64 (blk >> 1).
   uint32_t vofs[2][2];
   {
     const uint32_t x = lane & 15, g1 = (lane >> 4) & 1;
 #pragma unroll
-    for (int bk = 0; bk < 2; ++bk)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int r = 0; r < 2; ++r)
-        vofs[bk][r] = (4u * h + (x >> 2)) * (kPitch * 16) + 64u * (bk ^ (x >> 3)) +
-                      16u * ((2u * g1 + ((x & 3u) >> 1)) ^ (2u * r + h)) + 8u * (x & 1u);
+      for (int j2 = 0; j2 < 2; ++j2) {
+        if constexpr (KIND == 0) {
+          vofs[i][j2] = (4u * h + (x >> 2)) * kRowBytes + 64u * (i ^ (x >> 3)) +
+                        16u * ((2u * g1 + ((x & 3u) >> 1)) ^ (2u * j2 + h)) + 8u * (x & 1u);
+        } else {
+          const uint32_t j = x >> 1, sh = x & 1;
+          const uint32_t tv = 16u * i + 8u * (j >> 2) + 4u * h + (j & 3u);
+          vofs[i][j2] = tv * kRowBytes + 32u * (j2 ^ (j >> 2)) + 16u * (g1 ^ i) + 8u * sh;
+        }
+      }
   }
 
-  // e4m3: widen tile k's codes (exactly; the scales are applied to the scores
-  // and the output) into its bf16 slot, 16-byte chunk c of token t at
-  // position c ^ swz(t) as the bf16 fills place it.  Thread tid widens token
-  // tid / 8, chunks tid % 8 + 8 j (j = 0..8): 8 code bytes at wsrc + 64 j,
-  // 16 bf16 bytes at wdst + 128 j (the swizzle stays inside the aligned
-  // group of eight).
-  constexpr int kWiden = kPitch / 8;               // 9
-  static_assert(kWWaves * 64 == 8 * kTile, "eight threads per tile token");
-  uint32_t wsrc = 0, wdst = 0;
-  if constexpr (FP8) {
-    const uint32_t t = uint32_t(tid) >> 3, c = uint32_t(tid) & 7u;
-    wsrc = t * kDqk + 8u * c;
-    wdst = t * (kPitch * 16) + 16u * (c ^ swz(t));
-  }
-  // All nine reads go out before the first conversion (one wave per SIMD:
-  // nothing else would hide their latency), and a scheduling barrier keeps
-  // them and the writes out of the score products' read pattern.
-  auto widen_tile = [&](int k) __attribute__((always_inline)) {
-    const lds_u8* src = (const lds_u8*)fill_slot(k) + wsrc;
-    lds_u8* dst = (lds_u8*)tile_slot(k) + wdst;
-    u32x2 w[FP8 ? kWiden : 1];
-#pragma unroll
-    for (int j = 0; j < (FP8 ? kWiden : 0); ++j) w[j] = *(const __attribute__((address_space(3))) u32x2*)(src + 64 * j);
-#pragma unroll
-    for (int j = 0; j < (FP8 ? kWiden : 0); ++j) {
-      const u32x2 a = e4m3x4_to_bf16x4(w[j].x), b2 = e4m3x4_to_bf16x4(w[j].y);
-      const u32x4 r = {a.x, a.y, b2.x, b2.y};
-      *(__attribute__((address_space(3))) u32x4*)(dst + 128 * j) = r;
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
-  // One 32-token tile in slotp, tokens t0 .. t0+31 of the range; load u of
-  // the next tile's fill (fill_u, which may do nothing) goes out after
-  // product 4 u + 2 of the scores.
+  // One 32-token tile in slotp, tokens t0 .. t0+31 of the range; fill_u(u)
+  // issues load u of a later tile's fill (or nothing), spread over the score
+  // products.
   auto tile = [&](const uint8_t* slotp, int t0, auto&& fill_u) __attribute__((always_inline)) {
     const lds_u8* ls = (const lds_u8*)slotp;
-    // ---- S^T = K Q^T: 36 products into one accumulator, each K operand
-    // read kKAhead products ahead
     f32x16 sacc;
 #pragma unroll
     for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
-    bf16x8 kr[kQk], qrr[kQk];
-    auto kread = [&](int it) __attribute__((always_inline)) {
-      kr[it] = *(const lds_bf16x8*)(ls + kofs[it & 3] + 128 * (it >> 2));
-      if (it >= kQkReg) qrr[it] = *(const lds_bf16x8*)(qr + 1024 * (it - kQkReg));
-    };
+    if constexpr (KIND == 0) {
+      // ---- S^T = K Q^T: 36 products into one accumulator, each K operand
+      // read four products ahead
+      constexpr int kN = 36, kAh = 4;
+      bf16x8 kr[kN], qrr[kN];
+      auto kread = [&](int it) __attribute__((always_inline)) {
+        kr[it] = *(const lds_bf16x8*)(ls + kofs[it & 3] + 128 * (it >> 2));
+        if (it >= 32) qrr[it] = *(const lds_bf16x8*)(qr + 1024 * (it - 32));
+      };
 #pragma unroll
-    for (int it = 0; it < kKAhead; ++it) kread(it);
+      for (int it = 0; it < kAh; ++it) kread(it);
 #pragma unroll
-    for (int it = 0; it < kQk; ++it) {
-      if (it + kKAhead < kQk) kread(it + kKAhead);
-      if (it % 4 == 2 && it / 4 < kLPW) fill_u(it / 4);
-      sacc = mfma32(kr[it], it < kQkReg ? q[it] : qrr[it], sacc);
+      for (int it = 0; it < kN; ++it) {
+        if (it + kAh < kN) kread(it + kAh);
+        if (it % 4 == 2 && it / 4 < kLPW) fill_u(it / 4);
+        sacc = mfma32(kr[it], it < 32 ? qb[it] : qrr[it], sacc);
+      }
+      // Hold the scheduler to that order (left alone it issues each read just
+      // before its product, which then waits out the LDS latency): the first
+      // reads, then product, read (two for a rope product), ...
+      __builtin_amdgcn_sched_group_barrier(0x100, kAh, 0);
+#pragma unroll
+      for (int it = 0; it < 32 - kAh; ++it) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+#pragma unroll
+      for (int it = 32 - kAh; it < kN - kAh; ++it) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+#pragma unroll
+      for (int it = kN - kAh; it < kN; ++it) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    } else if constexpr (KIND == 1) {
+      // ---- 18 reads of 16 codes, each widened into the operands of two
+      // products; the reads run three ahead (with the rope query's two
+      // operand reads for the last two)
+      constexpr int kN = 18, kAh = 3;
+      u32x4 kr[kN], qlo[kN], qhi[kN];
+      auto kread = [&](int m) __attribute__((always_inline)) {
+        kr[m] = *(const lds_u32x4*)(ls + kofs[m & 1] + 64 * (m >> 1));
+        if (m >= 16) {
+          qlo[m] = *(const lds_u32x4*)(qr + 1024 * (2 * (m - 16)));
+          qhi[m] = *(const lds_u32x4*)(qr + 1024 * (2 * (m - 16) + 1));
+        }
+      };
+#pragma unroll
+      for (int m = 0; m < kAh; ++m) kread(m);
+#pragma unroll
+      for (int m = 0; m < kN; ++m) {
+        if (m + kAh < kN) kread(m + kAh);
+        if (m % 2 == 1 && m / 2 < kLPW) fill_u(m / 2);
+        const bf16x8 qa = m < 16 ? qb[2 * m] : __builtin_bit_cast(bf16x8, qlo[m]);
+        const bf16x8 qz = m < 16 ? qb[2 * m + 1] : __builtin_bit_cast(bf16x8, qhi[m]);
+        sacc = mfma32(widen8(kr[m].x, kr[m].y), qa, sacc);
+        sacc = mfma32(widen8(kr[m].z, kr[m].w), qz, sacc);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, kAh, 0);
+#pragma unroll
+      for (int m = 0; m < 16 - kAh; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+#pragma unroll
+      for (int m = 16 - kAh; m < kN - kAh; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+      }
+#pragma unroll
+      for (int m = kN - kAh; m < kN; ++m) __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    } else {
+      // ---- e4m3 queries: nine 64-feature products on the codes, two
+      // 16-byte reads each, two products ahead
+      constexpr int kN = 9, kAh = 2;
+      u32x4 kr[kN][2];
+      auto kread = [&](int pp) __attribute__((always_inline)) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) kr[pp][c] = *(const lds_u32x4*)(ls + kofs[c] + 64 * pp);
+      };
+#pragma unroll
+      for (int pp = 0; pp < kAh; ++pp) kread(pp);
+#pragma unroll
+      for (int pp = 0; pp < kN; ++pp) {
+        if (pp + kAh < kN) kread(pp + kAh);
+        if (pp < kLPW) fill_u(pp);
+        const i32x8 ka = {int(kr[pp][0].x), int(kr[pp][0].y), int(kr[pp][0].z), int(kr[pp][0].w),
+                          int(kr[pp][1].x), int(kr[pp][1].y), int(kr[pp][1].z), int(kr[pp][1].w)};
+        sacc = mma64(ka, qc8[pp], sacc);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAh, 0);
+#pragma unroll
+      for (int pp = 0; pp < kN - kAh; ++pp) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+#pragma unroll
+      for (int pp = kN - kAh; pp < kN; ++pp) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
-    // Hold the scheduler to that order (left alone it issues each read just
-    // before its product, which then waits out the LDS latency): the first
-    // kKAhead reads, then read (two for a rope product), product, ...
-    __builtin_amdgcn_sched_group_barrier(0x100, kKAhead, 0);
-#pragma unroll
-    for (int it = 0; it < kQkReg - kKAhead; ++it) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-#pragma unroll
-    for (int it = kQkReg - kKAhead; it < kQk - kKAhead; ++it) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-#pragma unroll
-    for (int it = kQk - kKAhead; it < kQk; ++it) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     // the first value products' operands do not depend on the scores: their
     // reads overlap the softmax
-    auto vread = [&](int n, v4i16& a0, v4i16& a1) __attribute__((always_inline)) {
-      const int kb = n / kVb, blk = n % kVb;
-      const lds_u8* base = ls + 16 * kb * (kPitch * 16) + 128 * (blk >> 1);
-      a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(base + vofs[(blk & 1) ^ kb][0]));
-      a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_v4i16*)(base + 8 * (kPitch * 16) + vofs[(blk & 1) ^ kb][1]));
-    };
     v4i16 va[2 * kVb], vb[2 * kVb];
+    i32x2 vc[2 * kVb];
+    auto vread = [&](int n) __attribute__((always_inline)) {
+      const int kb = n / kVb, blk = n % kVb;
+      if constexpr (KIND == 0) {
+        const lds_u8* base = ls + 16 * kb * kRowBytes + 128 * (blk >> 1);
+        va[n] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(base + vofs[(blk & 1) ^ kb][0]));
+        vb[n] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(base + 8 * kRowBytes + vofs[(blk & 1) ^ kb][1]));
+      } else {
+        vc[n] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(ls + 64 * (blk >> 1) + vofs[kb][blk & 1]));
+      }
+    };
+    auto vop = [&](int n) __attribute__((always_inline)) {
+      if constexpr (KIND == 0)
+        return __builtin_bit_cast(bf16x8, u32x4{__builtin_bit_cast(u32x2, va[n]).x, __builtin_bit_cast(u32x2, va[n]).y,
+                                                __builtin_bit_cast(u32x2, vb[n]).x, __builtin_bit_cast(u32x2, vb[n]).y});
+      else
+        return widen8(uint32_t(vc[n].x), uint32_t(vc[n].y));
+    };
+    constexpr int kVReads = KIND == 0 ? 2 : 1;     // reads per value product
 #pragma unroll
-    for (int n = 0; n < kVAhead; ++n) vread(n, va[n], vb[n]);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kVAhead, 0);
+    for (int n = 0; n < kVAhead; ++n) vread(n);
+    __builtin_amdgcn_sched_group_barrier(0x100, kVReads * kVAhead, 0);
     // ---- online softmax over the tile: lane (r32, h) holds tokens
     // 8 (v / 4) + 4 h + v % 4 of row r32
     float sv[16];
@@ -479,65 +625,42 @@ void mla_partial_kernel(PartialParams p, int per_xcd) {
     // ahead
 #pragma unroll
     for (int n = 0; n < 2 * kVb; ++n) {
-      if (n + kVAhead < 2 * kVb) vread(n + kVAhead, va[n + kVAhead], vb[n + kVAhead]);
-      const u32x4 w = {__builtin_bit_cast(u32x2, va[n]).x, __builtin_bit_cast(u32x2, va[n]).y,
-                       __builtin_bit_cast(u32x2, vb[n]).x, __builtin_bit_cast(u32x2, vb[n]).y};
-      o[n % kVb] = mfma32(__builtin_bit_cast(bf16x8, w), pk[n / kVb], o[n % kVb]);
+      if (n + kVAhead < 2 * kVb) vread(n + kVAhead);
+      o[n % kVb] = mfma32(vop(n), pk[n / kVb], o[n % kVb]);
     }
-    // as for the scores: read two ahead, product, ...
+    // as for the scores: read ahead, product, ...
 #pragma unroll
     for (int n = 0; n < 2 * kVb - kVAhead; ++n) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, kVReads, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
 #pragma unroll
     for (int n = 2 * kVb - kVAhead; n < 2 * kVb; ++n) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
   };
 
-  int pa = 0, pb = 0;      // pages of the tile the next fill loads
-  // Step k: wait until this wave's loads of tile k are done (those of tiles
-  // k+1 and k+2, where the range has them, may still be in flight), then a
-  // barrier so every wave's part of the tile has landed -- which also means
-  // every wave has finished tile k-1, so its slot can be refilled with tile
-  // k+3.  Tiles past the range are never loaded: the wait allows as many
-  // loads in flight as the range has tiles after k, up to two.
-  // e4m3: the same three-ahead fills into the code ring; tile k+1 is widened
-  // at the start of step k, so at step k this wave waits for its loads of
-  // tile k+1 (those of tile k+2 may still be in flight) and the barrier makes
-  // tile k's widened slot and tile k+1's codes visible.
-  // The steps of the loop's last three tiles (TAIL) take these counts from
-  // the range; the others have two tiles in flight behind theirs and a tile
-  // to fill.
-  // Steps whose fill is a tile before the range's last (all but the last
-  // four) spread its loads over the score products; the last four (TAIL)
-  // fill the range's last tile, which may be cut by the range end, up front,
-  // or nothing.
+  // Step k: wait until this wave's loads of tile k are done (those of the
+  // next kAhead - 1 tiles, where the range has them, may still be in
+  // flight), then a barrier so every wave's part of the tile has landed --
+  // which also means every wave has finished tile k-1, whose slot (the ring
+  // holds kAhead + 1 tiles or more) takes tile k + kAhead.  Tiles past the
+  // range are never loaded: the wait allows as many loads in flight as the
+  // range has tiles after k.
+  // Steps whose fill is a tile before the range's last spread its loads over
+  // the score products; the others (TAIL) fill the range's last tile, which
+  // may be cut by the range end, up front, or nothing.
   auto step = [&](int k, auto TAIL) __attribute__((always_inline)) {
     constexpr bool tail = decltype(TAIL)::value;
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    if constexpr (FP8) {
-      if (!tail || k + 2 < nt)
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLPW));
-      else
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    } else {
-      if (!tail || k + 2 < nt)
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kLPW));
-      else if (k + 1 < nt)
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLPW));
-      else
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    }
+    if constexpr (!tail)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm((kAhead - 1) * kLPW));
+    else
+      wait_tiles<kLPW>(min(kAhead - 1, nt - 1 - k));
     lds_barrier();
-    if (tail && k + 3 < nt) fill(k + 3, fill_slot(k + 3), pa, pb);
-    // e4m3: widen tile k+1 (its codes have landed) into the slot tile k-1 left
-    if constexpr (FP8) {
-      if (!tail || k + 1 < nt) widen_tile(k + 1);
-    }
+    if (tail && k + kAhead < nt) fill(k + kAhead, tile_slot(k + kAhead), pa, pb);
     const uint8_t* cur = tile_slot(k);
     const int t0 = s + kTile * k;
     if constexpr (!tail) {
-      const WholeFill f = whole_fill(k + 3, fill_slot(k + 3), pa, pb);
+      const WholeFill f = whole_fill(k + kAhead, tile_slot(k + kAhead), pa, pb);
       tile(cur, t0, [&](int u) __attribute__((always_inline)) { whole_load(f, u); });
     } else {
       tile(cur, t0, [](int) {});
@@ -547,39 +670,13 @@ void mla_partial_kernel(PartialParams p, int per_xcd) {
     // of the tile: while one is in flight the compiler can only wait for LDS
     // reads with lgkmcnt(0), which would drain the reads in flight.
     __builtin_amdgcn_sched_barrier(0);
-    tile_pages(k + 4, pa, pb);
+    tile_pages(k + kAhead + 1, pa, pb);
   };
 
   if (nt > 0) {
-    tile_pages(0, pa, pb);
-    fill(0, fill_slot(0), pa, pb);
-    tile_pages(1, pa, pb);
-    if (nt > 1) fill(1, fill_slot(1), pa, pb);
-    tile_pages(2, pa, pb);
-    if (nt > 2) fill(2, fill_slot(2), pa, pb);
-    tile_pages(3, pa, pb);
-    // Wait here for the query and tile 0 (loads complete in order; tiles 1
-    // and 2 may still be in flight): the compiler does not see the fills, and
-    // a wait for the query placed inside the tile loop would drain the fills
-    // in flight there.
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    if (nt > 2)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kLPW));
-    else if (nt > 1)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLPW));
-    else
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-#pragma unroll
-    for (int it = 0; it < kQkReg; ++it) asm volatile("" ::"v"(q[it]));
-    if constexpr (FP8) {
-      // tile 0 (landed with the wait above) widened before the loop; tile
-      // k+1 is widened in step k
-      lds_barrier();
-      widen_tile(0);
-    }
-    // tiles k + 3 < nt - 1 are inside the range; tile nt - 1 may be cut
+    // tiles k + kAhead < nt - 1 are inside the range; tile nt - 1 may be cut
     int k = 0;
-    for (; k + 4 < nt; ++k) step(k, std::false_type());
+    for (; k + kAhead + 1 < nt; ++k) step(k, std::false_type());
     for (; k < nt; ++k) step(k, std::true_type());
   }
   // no wave leaves while loads it issued may still write LDS
@@ -678,13 +775,16 @@ void mla_partial_kernel(PartialParams p, int per_xcd) {
   if (p.debug && tid == 0) store_debug(p, slot, rb, b, split, s, e, dbg_groups, dbg_xor, dbg_sum);
 }
 
-hipError_t launch_mla_partial(const PartialParams& p, bool fp8, hipStream_t stream) {
+// kind: 0 bf16 cache, 1 e4m3 cache with bf16 queries, 2 e4m3 cache and queries.
+hipError_t launch_mla_partial(const PartialParams& p, int kind, hipStream_t stream) {
   const int per_xcd = (p.total_wg + 7) / 8;
   const dim3 grid(unsigned(per_xcd * 8)), block(256);
-  if (fp8)
-    hipLaunchKernelGGL(mla_partial_kernel<true>, grid, block, 0, stream, p, per_xcd);
+  if (kind == 2)
+    hipLaunchKernelGGL(mla_partial_kernel<2>, grid, block, 0, stream, p, per_xcd);
+  else if (kind == 1)
+    hipLaunchKernelGGL(mla_partial_kernel<1>, grid, block, 0, stream, p, per_xcd);
   else
-    hipLaunchKernelGGL(mla_partial_kernel<false>, grid, block, 0, stream, p, per_xcd);
+    hipLaunchKernelGGL(mla_partial_kernel<0>, grid, block, 0, stream, p, per_xcd);
   return hipGetLastError();
 }
 

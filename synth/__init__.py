@@ -315,13 +315,14 @@ def random_queries(rng, shape, std=1.0) -> np.ndarray:
 # device upload (array conversion only)
 # --------------------------------------------------------------------------
 
-def to_torch(case: Case, device, layout: str = "HND", q_pad_heads: int = 0):
+def to_torch(case: Case, device, layout: str = "HND", q_pad_heads: int = 0, q_pad_dim: int = 0):
     """Copy a case's arrays to ``device`` as torch tensors.
 
     layout "HND" keeps [page][head][slot][d] contiguous; "NHD" stores
     [page][slot][head][d] and returns the [page][head][slot][d] strided view.
     ``q_pad_heads`` > 0 embeds q in a wider head dimension so that the query
-    tensor the kernels see is not contiguous.
+    tensor the kernels see is not contiguous; ``q_pad_dim`` > 0 pads each
+    query row instead (rows evenly spaced, wider than the row).
     """
     torch = _torch()
 
@@ -339,11 +340,11 @@ def to_torch(case: Case, device, layout: str = "HND", q_pad_heads: int = 0):
         return t.view(torch.bfloat16) if dt == torch.int16 else t
 
     q = torch.from_numpy(case.q.view(np.int16))
-    if q_pad_heads:
+    if q_pad_heads or q_pad_dim:
         B, T, Hq, D = q.shape
-        big = torch.zeros((B, T, Hq + q_pad_heads, D), dtype=torch.int16)
-        big[:, :, :Hq] = q
-        qd = big.to(device)[:, :, :Hq]
+        big = torch.zeros((B, T, Hq + q_pad_heads, D + q_pad_dim), dtype=torch.int16)
+        big[:, :, :Hq, :D] = q
+        qd = big.to(device)[:, :, :Hq, :D]
     else:
         qd = q.to(device)
     return dict(q=qd.view(torch.bfloat16), k_cache=cache(case.k_cache), v_cache=cache(case.v_cache),

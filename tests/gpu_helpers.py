@@ -65,10 +65,10 @@ def check_guards(sess):
 
 
 def session_for(case, requested_splits=0, max_splits=64, layout="HND", q_pad_heads=0, debug=False,
-                num_cus=0, guard=True):
+                num_cus=0, guard=True, q_pad_dim=0):
     import torch
     from split_kv_amd.session import DecodeSession
-    t = synth.to_torch(case, "cuda", layout=layout, q_pad_heads=q_pad_heads)
+    t = synth.to_torch(case, "cuda", layout=layout, q_pad_heads=q_pad_heads, q_pad_dim=q_pad_dim)
     k = t["k_cache"]
     v = t["v_cache"]
     sess = DecodeSession(q=t["q"], k_cache=k, v_cache=v, block_table=t["block_table"],

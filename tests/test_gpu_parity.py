@@ -672,6 +672,26 @@ def test_mla_fp8q_saturating_scale_strided_query_nhd_cache():
     _check_debug(case, sess, 1, -(-768 // MLA_RPW))
 
 
+@pytest.mark.parametrize("kv_dtype", [synth.KV_BF16, synth.KV_E4M3])
+@pytest.mark.parametrize("pad", ["heads", "dim"])
+def test_mla_query_row_layouts(kv_dtype, pad):
+    # The query rows (t, h) of a sequence are read either as evenly spaced
+    # rows (a padded row: stride 600 elements, 600 * Hq per token) or, when
+    # the token stride is not Hq row strides (padded heads), one row at a time;
+    # 3 x 40 rows leave a partial last block of 128.
+    _need_gpu()
+    case = synth.mla_decode(L=1500, seed=83, T=3, Hq=40, kv_dtype=kv_dtype)
+    log(f"mla {kv_dtype} query padded along {pad}")
+    sess, t = session_for(case, requested_splits=5, q_pad_heads=3 if pad == "heads" else 0,
+                          q_pad_dim=24 if pad == "dim" else 0, debug=True)
+    q = t["q"]
+    assert q.stride(2) == (600 if pad == "dim" else 576)
+    assert (q.stride(1) == 40 * q.stride(2)) == (pad == "dim")
+    sess.decode()
+    _check_full(case, sess, f"mla {kv_dtype} query padded along {pad}")
+    _check_debug(case, sess, 1, -(-(3 * 40) // MLA_RPW))
+
+
 @pytest.mark.parametrize("path", ["gqa-bf16", "gqa-e4m3", "mla-bf16", "mla-e4m3", "mla-e4m3-queries"])
 def test_rows_without_visible_keys_beside_visible_ones(path):
     # The lazy rescale moves the rows of a 16-row block whose maximum jumped
