@@ -11,47 +11,39 @@
 // S * rows * (2 * d_v + 16) in the MLA kernels' compact layout (int16 codes
 // of o with a scale per 256-feature half).
 //
-// A workgroup merges one row's partials over C float4 columns (4C features)
-// with G groups of threads over the splits: thread (g, c) takes splits g,
-// g + G, g + 2G, ... of the row for column c, issuing the loads of up to U
-// splits (m, l and a float4 of o each) before merging any, and the G groups
-// meet in LDS (the same rescaling as across splits).  The host picks G for
-// the plan's largest split count so that a thread has at most eight splits
-// (G = 1 needs no LDS step at all); C is 256 / G columns, or the whole row
-// when that is narrower, so a row of the six-token MLA shape (512 features,
-// ~21 splits) is two workgroups of 4 x 64 threads and a row of the few-KV
-// shape (256 features, ~62 splits) two of 8 x 32.  Every load of a row is
-// in flight at once: at decode sizes the merge is latency-bound.
+// fp32 partials: a workgroup merges one row's partials over C float4 columns
+// (4C features) with G groups of threads over the splits: thread (g, c) takes
+// splits g, g + G, g + 2G, ... of the row for column c, issuing the loads of
+// up to U splits (m, l and a float4 of o each) before merging any, and the G
+// groups meet in LDS (the same rescaling as across splits).  The host picks G
+// for the plan's largest split count so that a thread has at most eight
+// splits (G = 1 needs no LDS step at all); C is 256 / G columns, or the whole
+// row when that is narrower, so a row of the few-KV shape (256 features, ~62
+// splits) is two workgroups of 8 x 32.  Every load of a row is in flight at
+// once: at decode sizes the merge is latency-bound.  The MLA layout has a
+// kernel of its own (combine_codes_kernel, below).
 #include "device.h"
 
 namespace splitkv {
 
 // One thread's share of a row's splits: splits g, g+G, g+2G, ... of the n,
 // U loads in flight per pass, merged into the running (M2, lam, acc) in base 2.
-// fp32 o: po points at the thread's float4 of the row in slot 0 and step is a
-// slot's stride.  CODES (the MLA layout): po points at the thread's four int16
-// codes instead, and ps at the scale of the half of the row they lie in (a
-// slot's stride 2R floats); o = code * scale.
-template <int U, bool CODES>
-__device__ __forceinline__ void merge_splits(const float* part_m, const float* part_l, const void* po,
-                                             const float* ps, int64_t step, int R, int rix, int base,
-                                             int n, int g, int G, float& M2, float& lam, f32x4& acc) {
+// po points at the thread's float4 of the row in slot 0 and step is a slot's
+// stride.
+template <int U>
+__device__ __forceinline__ void merge_splits(const float* part_m, const float* part_l, const float* po,
+                                             int64_t step, int R, int rix, int base, int n, int g, int G,
+                                             float& M2, float& lam, f32x4& acc) {
   for (int i0 = g; i0 < n; i0 += U * G) {
-    float mi[U], li[U], si[U];
+    float mi[U], li[U];
     f32x4 oi[U];
-    u32x2 ci[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int i = i0 + u * G;
       const int64_t sl = base + (i < n ? i : i0);   // past the end: reread a valid slot, weight 0
       mi[u] = part_m[sl * R + rix];
       li[u] = part_l[sl * R + rix];
-      if constexpr (CODES) {
-        si[u] = ps[sl * 2 * R];
-        ci[u] = *reinterpret_cast<const u32x2*>(static_cast<const int16_t*>(po) + sl * step);
-      } else {
-        oi[u] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(po) + sl * step);
-      }
+      oi[u] = *reinterpret_cast<const f32x4*>(po + sl * step);
       if (i >= n) mi[u] = -INFINITY;
     }
 #pragma unroll
@@ -62,14 +54,7 @@ __device__ __forceinline__ void merge_splits(const float* part_m, const float* p
       const float a = fast_exp2(M2 - Mn);                 // 0 while M2 is -inf
       const float w = fast_exp2(m2 - Mn);
       lam = lam * a + w * li[u];
-      if constexpr (CODES) {
-        const float ws = w * si[u];
-        const f32x4 o = {float(int16_t(ci[u].x & 0xffffu)), float(int16_t(ci[u].x >> 16)),
-                         float(int16_t(ci[u].y & 0xffffu)), float(int16_t(ci[u].y >> 16))};
-        acc = acc * a + ws * o;
-      } else {
-        acc = acc * a + w * oi[u];
-      }
+      acc = acc * a + w * oi[u];
       M2 = Mn;
     }
   }
@@ -85,13 +70,10 @@ __device__ __forceinline__ void merge_splits(const float* part_m, const float* p
 // argument is <= 0: a difference from the running max).
 // flags: d_v (bits 0-15) | skip rows of single-split sequences (bit 16) |
 // fp32 output (bit 17) | uniform split count (bits 18-26; 0: read the plan).
-// CODES: the partials are in the MLA layout (m, l, two scales per row from
-// 2 * SR floats on, int16 codes of o at the next 256-byte boundary after
-// 4 * SR floats).
 // With a uniform count the row's plan is n = that count and base = b * n, so
 // the partial loads are the first memory accesses.  The workgroup has C * G
 // threads (C = blockDim.x / G float4 columns).
-template <int G, bool CODES>
+template <int G>
 __global__ __launch_bounds__(256) void combine_kernel(const float* part_m, const int32_t* num_splits,
                                                       const int32_t* slot_offset, void* out,
                                                       float* lse, int32_t R, int32_t dsplit,
@@ -125,27 +107,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* part_m, const
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   const int f0 = 4 * (C * part + c);                  // this thread's first feature
   const int64_t step = int64_t(R) * DV;
-  const void* po;
-  const float* ps = nullptr;
-  if constexpr (CODES) {
-    const int16_t* part_q = reinterpret_cast<const int16_t*>(
-        reinterpret_cast<const char*>(part_m) + (int64_t(16) * SR + 255) / 256 * 256);
-    po = part_q + int64_t(rix) * DV + f0;
-    ps = part_m + int64_t(2) * SR + int64_t(rix) * 2 + f0 / 256;
-  } else {
-    po = part_m + (int64_t(2) * SR * 4 + 255) / 256 * 64 + int64_t(rix) * DV + f0;
-  }
+  const float* po = part_m + (int64_t(2) * SR * 4 + 255) / 256 * 64 + int64_t(rix) * DV + f0;
   // loads per thread and pass: just enough for the row's splits (uniform
   // across the workgroup), so no pass issues loads it only masks away
   const int per = (n + G - 1) / G;
   if (per <= 1)
-    merge_splits<1, CODES>(part_m, part_l, po, ps, step, R, rix, base, n, g, G, M2, lam, acc);
+    merge_splits<1>(part_m, part_l, po, step, R, rix, base, n, g, G, M2, lam, acc);
   else if (per <= 2)
-    merge_splits<2, CODES>(part_m, part_l, po, ps, step, R, rix, base, n, g, G, M2, lam, acc);
+    merge_splits<2>(part_m, part_l, po, step, R, rix, base, n, g, G, M2, lam, acc);
   else if (per <= 4)
-    merge_splits<4, CODES>(part_m, part_l, po, ps, step, R, rix, base, n, g, G, M2, lam, acc);
+    merge_splits<4>(part_m, part_l, po, step, R, rix, base, n, g, G, M2, lam, acc);
   else
-    merge_splits<8, CODES>(part_m, part_l, po, ps, step, R, rix, base, n, g, G, M2, lam, acc);
+    merge_splits<8>(part_m, part_l, po, step, R, rix, base, n, g, G, M2, lam, acc);
   if constexpr (G > 1) {
     red_m[tid] = M2;
     red_l[tid] = lam;
@@ -180,6 +153,146 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* part_m, const
   if (lse && part == 0 && c == 0) lse[row] = ok ? (M2 + log2f(lam)) * kLn2 : -INFINITY;
 }
 
+// The MLA layout (512 features: int16 codes of o, a scale per 256-feature
+// half): one workgroup of four waves per row.  Wave w merges splits w, w + 4,
+// w + 8, ...; lane j keeps features 8 j .. 8 j + 7, whose codes are one
+// 16-byte load per split (the wave reads a split's row of codes in one 1 KiB
+// load); a split's m, l and two scales are the same for the whole wave (one
+// address per load; as scalar loads they measured slower).  Up to U splits'
+// loads are in flight before any is merged; the four waves meet in LDS, and
+// wave 0 writes the row.
+template <int U>
+__device__ __forceinline__ void merge_code_splits(const float* part_m, const float* part_l, const float* part_s,
+                                                  const int16_t* pq, int64_t R, int rix, int base, int n,
+                                                  int w, int hf, float& M2, float& lam, float (&acc)[8]) {
+  for (int i0 = w; i0 < n; i0 += 4 * U) {
+    float mi[U], li[U], si[U], s2[U][2];
+    u32x4 ci[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + 4 * u;
+      const int64_t ix = int64_t(base + (i < n ? i : i0)) * R + rix;   // past the end: a valid slot, weight 0
+      mi[u] = part_m[ix];
+      li[u] = part_l[ix];
+      const float s0 = part_s[2 * ix], s1 = part_s[2 * ix + 1];
+      ci[u] = *reinterpret_cast<const u32x4*>(pq + ix * 512);
+      s2[u][0] = s0;
+      s2[u][1] = s1;
+    }
+    // every load of the pass is in flight before the first wait
+#pragma unroll
+    for (int u = 0; u < U; ++u) asm volatile("" :: "v"(mi[u]), "v"(li[u]), "v"(s2[u][0]), "v"(s2[u][1]));
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      si[u] = hf ? s2[u][1] : s2[u][0];
+      if (i0 + 4 * u >= n) mi[u] = -INFINITY;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (mi[u] == -INFINITY) continue;                  // empty split: zero weight
+      const float m2 = mi[u] * kLog2e;
+      const float Mn = fmaxf(M2, m2);
+      const float a = fast_exp2(M2 - Mn);                 // 0 while M2 is -inf
+      const float wt = fast_exp2(m2 - Mn);
+      lam = lam * a + wt * li[u];
+      const float ws = wt * si[u];
+      const uint32_t c4[4] = {ci[u].x, ci[u].y, ci[u].z, ci[u].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        acc[2 * k] = acc[2 * k] * a + ws * float(int16_t(c4[k] & 0xffffu));
+        acc[2 * k + 1] = acc[2 * k + 1] * a + ws * float(int16_t(c4[k] >> 16));
+      }
+      M2 = Mn;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void combine_codes_kernel(const float* part_m, const int32_t* num_splits,
+                                                            const int32_t* slot_offset, void* out, float* lse,
+                                                            int32_t R, int32_t flags, int32_t SR) {
+  __shared__ float red_ml[4][2];
+  __shared__ f32x4 red_o[3][2][64];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = uniform(tid >> 6);
+  const int row = blockIdx.x;
+  const int b = row / R;
+  const int rix = row - b * R;
+  const int un = (flags >> 18) & 0x1ff;
+  int n, base;
+  if (un > 0) {
+    n = un;
+    base = b * un;
+  } else {
+    n = ((cint32*)num_splits)[b];
+    base = ((cint32*)slot_offset)[b];
+    asm volatile("" :: "s"(n), "s"(base));   // both reads in flight before either is used
+  }
+  if ((flags & (1 << 16)) && n == 1) return;
+  const float* part_l = part_m + SR;
+  const float* part_s = part_m + 2 * int64_t(SR);
+  const int16_t* pq = reinterpret_cast<const int16_t*>(reinterpret_cast<const char*>(part_m) +
+                                                       (int64_t(16) * SR + 255) / 256 * 256) + 8 * lane;
+  float M2 = -INFINITY, lam = 0.f;
+  float acc[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc[k] = 0.f;
+  const int hf = lane >> 5;                            // features 8 lane .. +7 lie in half lane / 32
+  // loads per wave and pass: just enough for the row's splits
+  const int per = (n + 3) / 4;
+  if (per <= 1)
+    merge_code_splits<1>(part_m, part_l, part_s, pq, R, rix, base, n, w, hf, M2, lam, acc);
+  else if (per <= 2)
+    merge_code_splits<2>(part_m, part_l, part_s, pq, R, rix, base, n, w, hf, M2, lam, acc);
+  else if (per <= 4)
+    merge_code_splits<4>(part_m, part_l, part_s, pq, R, rix, base, n, w, hf, M2, lam, acc);
+  else
+    merge_code_splits<8>(part_m, part_l, part_s, pq, R, rix, base, n, w, hf, M2, lam, acc);
+  if (w > 0) {
+    if (lane == 0) {
+      red_ml[w][0] = M2;
+      red_ml[w][1] = lam;
+    }
+    red_o[w - 1][0][lane] = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    red_o[w - 1][1][lane] = f32x4{acc[4], acc[5], acc[6], acc[7]};
+  }
+  __syncthreads();
+  if (w > 0) return;
+  float Mt = M2;
+#pragma unroll
+  for (int k = 1; k < 4; ++k) Mt = fmaxf(Mt, red_ml[k][0]);
+  const float a0 = M2 == -INFINITY ? 0.f : fast_exp2(M2 - Mt);
+  float lt = lam * a0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc[k] *= a0;
+#pragma unroll
+  for (int k = 1; k < 4; ++k) {
+    const float mk = red_ml[k][0];
+    const float wk = mk == -INFINITY ? 0.f : fast_exp2(mk - Mt);
+    lt += wk * red_ml[k][1];
+    const f32x4 lo = red_o[k - 1][0][lane], hi = red_o[k - 1][1][lane];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc[j] += wk * lo[j];
+      acc[4 + j] += wk * hi[j];
+    }
+  }
+  const bool ok = Mt != -INFINITY && lt > 0.f;
+  const float inv = ok ? 1.f / lt : 0.f;
+  const int64_t o = int64_t(row) * 512 + 8 * lane;
+  if (flags & (1 << 17)) {
+    float* of = static_cast<float*>(out) + o;
+    *reinterpret_cast<f32x4*>(of) = f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+    *reinterpret_cast<f32x4*>(of + 4) = f32x4{acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
+  } else {
+    const u32x4 pk = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
+                      pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
+    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + o) = pk;
+  }
+  if (lse && lane == 0) lse[row] = ok ? (Mt + log2f(lt)) * kLn2 : -INFINITY;
+}
+
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
   if (p.d_v % 4 != 0 || p.d_v > 0xffff || p.uniform_splits < 0 || p.uniform_splits > 0x1ff)
     return hipErrorInvalidValue;
@@ -200,18 +313,19 @@ hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
   if (wgs > INT32_MAX || SR > INT32_MAX / 16 ||
       (!codes && p.part_o != p.part_m + (2 * SR * 4 + 255) / 256 * 64))
     return hipErrorInvalidValue;
+  const int32_t flags0 = p.d_v | (p.skip_single ? 1 << 16 : 0) | (p.out_f32 ? 1 << 17 : 0) |
+                         (p.uniform_splits << 18);
+  if (codes) {
+    const int64_t rows = int64_t(p.B) * p.R;
+    if (rows > INT32_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(combine_codes_kernel, dim3(unsigned(rows)), dim3(256), 0, stream, p.part_m, p.num_splits,
+                       p.slot_offset, p.out, p.lse, p.R, flags0, int32_t(SR));
+    return hipGetLastError();
+  }
   const dim3 grid(static_cast<unsigned>(wgs)), block(unsigned(C * G));
-  const int32_t flags = p.d_v | (p.skip_single ? 1 << 16 : 0) | (p.out_f32 ? 1 << 17 : 0) |
-                       (p.uniform_splits << 18);
 #define SPLITKV_COMBINE(GG)                                                                            \
-  do {                                                                                                 \
-    if (codes)                                                                                         \
-      hipLaunchKernelGGL((combine_kernel<GG, true>), grid, block, 0, stream, p.part_m, p.num_splits,   \
-                         p.slot_offset, p.out, p.lse, p.R, dsplit, flags, int32_t(SR));                \
-    else                                                                                               \
-      hipLaunchKernelGGL((combine_kernel<GG, false>), grid, block, 0, stream, p.part_m, p.num_splits,  \
-                         p.slot_offset, p.out, p.lse, p.R, dsplit, flags, int32_t(SR));                \
-  } while (0)
+  hipLaunchKernelGGL((combine_kernel<GG>), grid, block, 0, stream, p.part_m, p.num_splits,             \
+                     p.slot_offset, p.out, p.lse, p.R, dsplit, flags0, int32_t(SR))
   switch (G) {
     case 1: SPLITKV_COMBINE(1); break;
     case 2: SPLITKV_COMBINE(2); break;

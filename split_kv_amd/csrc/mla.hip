@@ -289,6 +289,12 @@ void mla_partial_kernel(PartialParams p, int per_xcd) {
     }
   };
 
+  // Pages of the first kAhead + 1 tiles: their scalar loads go out before
+  // the query's loads and have landed when the first fills need them.
+  int pg[2 * (kAhead + 1)];
+#pragma unroll
+  for (int k = 0; k <= kAhead; ++k) tile_pages(k, pg[2 * k], pg[2 * k + 1]);
+
   // The query, loaded before any tile.  bf16 (kinds 0, 1): lane (r32, h)
   // holds 8 features of the row for each 16-feature score product, in
   // registers for the 512 latent features and in LDS for the 64 rope features
@@ -369,13 +375,10 @@ void mla_partial_kernel(PartialParams p, int per_xcd) {
   }
   // the first kAhead tiles go out once the query has landed (a wait for it
   // issued after them would wait for them too)
-  int pa = 0, pb = 0;      // pages of the tile the next fill loads
 #pragma unroll
-  for (int k = 0; k < kAhead; ++k) {
-    tile_pages(k, pa, pb);
-    if (k < nt) fill(k, tile_slot(k), pa, pb);
-  }
-  tile_pages(kAhead, pa, pb);
+  for (int k = 0; k < kAhead; ++k)
+    if (k < nt) fill(k, tile_slot(k), pg[2 * k], pg[2 * k + 1]);
+  int pa = pg[2 * kAhead], pb = pg[2 * kAhead + 1];     // pages of the tile the next fill loads
 
   // O^T accumulators: lane (r32, h) holds O[row r32][32 blk + 8 (v / 4) +
   // 4 h + v % 4] in o[blk][v].
@@ -722,46 +725,65 @@ void mla_partial_kernel(PartialParams p, int per_xcd) {
     // the patterns is the largest positive value, the unsigned maximum the
     // negative value of largest magnitude (or, with none, the largest
     // positive), so the larger of their magnitudes is the answer -- two
-    // three-operand integer maxima per pair of values.
-    float amax[2], kq[2];
+    // three-operand integer maxima per pair of values.  A half's 128 values
+    // per lane are copied out of the accumulation registers once and serve
+    // both its maximum and its codes.
+    float amax[2];
+    lds_u8* st = (lds_u8*)pool + (wave * 32) * kCodeRowBytes;
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
+      float xv[128];
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) xv[16 * c + v] = o[8 * hf + c][v];
       int32_t smax = INT32_MIN;
       uint32_t umax = 0;
 #pragma unroll
-      for (int c = 8 * hf; c < 8 * hf + 8; ++c)
-#pragma unroll
-        for (int v = 0; v < 16; v += 2) {
-          const int32_t x = __float_as_int(o[c][v]), y = __float_as_int(o[c][v + 1]);
-          smax = max(smax, max(x, y));
-          umax = max(umax, max(uint32_t(x), uint32_t(y)));
-        }
+      for (int v = 0; v < 128; v += 2) {
+        const int32_t x = __float_as_int(xv[v]), y = __float_as_int(xv[v + 1]);
+        smax = max(smax, max(x, y));
+        umax = max(umax, max(uint32_t(x), uint32_t(y)));
+      }
       const float a = pair_max(fmaxf(fabsf(__int_as_float(smax)), fabsf(__uint_as_float(umax))));
       amax[hf] = a * fabsf(mul);
       // o * kq lies in [-1, 1]; its code is the nearest integer to 32767 times it
-      kq[hf] = amax[hf] > 0.f ? mul / amax[hf] : 0.f;
+      const float kq = amax[hf] > 0.f ? mul / amax[hf] : 0.f;
+      if (hf == 0) __syncthreads();        // every wave is done with the tile pool
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          // v_cvt_pknorm_i16_f32: two values in [-1, 1] to the nearest
+          // multiples of 1/32767, as int16 codes
+          const float* x4 = xv + 16 * c + 4 * j;
+          const u32x2 w = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pknorm_i16(x4[0] * kq, x4[1] * kq)),
+                           __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pknorm_i16(x4[2] * kq, x4[3] * kq))};
+          *(__attribute__((address_space(3))) u32x2*)(st + r32 * kCodeRowBytes +
+                                                      2 * (32 * (8 * hf + c) + 8 * j + 4 * h)) = w;
+        }
     }
-    lds_u8* st = (lds_u8*)pool + (wave * 32) * kCodeRowBytes;
-    __syncthreads();                       // every wave is done with the tile pool
-#pragma unroll
-    for (int c = 0; c < kVb; ++c)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        // v_cvt_pknorm_i16_f32: two values in [-1, 1] to the nearest multiples
-        // of 1/32767, as int16 codes
-        const float kk = kq[c / 8];
-        const u32x2 w = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pknorm_i16(o[c][4 * j] * kk, o[c][4 * j + 1] * kk)),
-                         __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pknorm_i16(o[c][4 * j + 2] * kk, o[c][4 * j + 3] * kk))};
-        *(__attribute__((address_space(3))) u32x2*)(st + r32 * kCodeRowBytes + 2 * (32 * c + 8 * j + 4 * h)) = w;
-      }
     // each wave reads back only what it wrote (no barrier; the LDS waits
-    // suffice); rows are in (t, h) order, so a row's index within the
-    // sequence is the row number itself
+    // suffice), eight rows in flight at a time; rows are in (t, h) order, so
+    // a row's index within the sequence is the row number itself
     const int row0 = rb * kWRows + wave * 32;
+    int16_t* qdst = p.part_q + (int64_t(slot) * R + row0) * kDv + 8 * lane;
+    const lds_u8* qsrc = st + 16 * lane;
+    if (row0 + 32 <= p.rows) {
 #pragma unroll
-    for (int r = 0; r < 32; ++r) {
-      const u32x4 w = *(const __attribute__((address_space(3))) u32x4*)(st + r * kCodeRowBytes + 16 * lane);
-      if (row0 + r < p.rows) *reinterpret_cast<u32x4*>(p.part_q + (int64_t(slot) * R + row0 + r) * kDv + 8 * lane) = w;
+      for (int r0 = 0; r0 < 32; r0 += 8) {
+        u32x4 w[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) w[j] = *(const lds_u32x4*)(qsrc + (r0 + j) * kCodeRowBytes);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) *reinterpret_cast<u32x4*>(qdst + (r0 + j) * kDv) = w[j];
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 32; ++r) {
+        const u32x4 w = *(const lds_u32x4*)(qsrc + r * kCodeRowBytes);
+        if (row0 + r < p.rows) *reinterpret_cast<u32x4*>(qdst + r * kDv) = w;
+      }
     }
     if (real && h == 0) {
       const int64_t ix = int64_t(slot) * R + rowv;
