@@ -299,25 +299,33 @@ def monotonic(sweep, band=1.03):
 
 def partial_kernel_name(case):
     if case.mla:
-        if case.q_scale:
-            return "mla_fp8q_partial_kernel"
-        return "mla_partial_kernel<%s>" % ("e4m3" if case.kv_dtype == "e4m3" else "bf16")
+        # kinds: 0 bf16 cache, 1 e4m3 cache with bf16 queries, 2 e4m3 cache and queries
+        return "mla_partial_kernel<%d>" % (2 if case.q_scale else (1 if case.kv_dtype == "e4m3" else 0))
     return "gqa_partial_kernel<%d,%s>" % (case.d_qk, "e4m3" if case.kv_dtype == "e4m3" else "bf16")
 
 
 def partial_grid(case, sess):
     """Workgroups of one partial-kernel launch."""
     if case.mla:
+        import split_kv_amd
         rows = case.T * case.Hq
-        return sess.total_slots * -(-rows // 64)
+        return sess.total_slots * -(-rows // split_kv_amd.SPLITKV_ROWS_PER_WG_MLA)
     return sess.total_slots * case.Hkv * -(-(case.g * case.T) // 16)
 
 
 def roofline(case, part_us):
     if case.mla:
-        flops = 2 * case.T * case.Hq * (case.d_qk + case.d_v) * int(case.seq_lens.sum())
-        # e4m3 queries put the products on the FP8 matrix path: its own peak
-        peak = MFMA_FP8_PEAK_TFLOPS if case.q_scale else MFMA_BF16_PEAK_TFLOPS
+        tokens = int(case.seq_lens.sum())
+        flops_qk = 2 * case.T * case.Hq * case.d_qk * tokens
+        flops_pv = 2 * case.T * case.Hq * case.d_v * tokens
+        flops = flops_qk + flops_pv
+        if case.q_scale:
+            # e4m3 queries put the scores on the FP8 matrix path and keep the
+            # value product on bf16: the peak is the rate of that mix, each
+            # part at its own dtype's peak
+            peak = round(flops / (flops_qk / MFMA_FP8_PEAK_TFLOPS + flops_pv / MFMA_BF16_PEAK_TFLOPS), 1)
+        else:
+            peak = MFMA_BF16_PEAK_TFLOPS
         return {"bound": "mfma", "kernel": partial_kernel_name(case),
                 "achieved": round(flops / part_us / 1e6, 1), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(flops / part_us / 1e6 / peak, 4),
