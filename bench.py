@@ -465,8 +465,49 @@ def floor_measurement(kv_bytes, grids, steps, stream):
     us = graph_time(read_all, 4)
     reads.append({"workgroups": 4096, "bytes": gib, "us": round(us, 3), "GBps": round(gib / us / 1e3, 1)})
     out["stream_read"] = reads
-    del buf, sink
+    del buf
+    out.update(unit_rates(sink, stream))
+    del sink
     torch.cuda.empty_cache()
+    return out
+
+
+def unit_rates(sink, stream):
+    """What the compute-bound (MLA) kernels' two inner resources deliver on
+    this GPU, measured with the library's calibration kernels: the bf16
+    32x32x16 matrix product issued back to back on every SIMD (one
+    workgroup of four waves per CU), and conflict-free LDS reads (16-byte and
+    transposing 8-byte) by four waves per CU.  Rates are per launch (events)
+    and per core clock (the kernels' own s_memtime cycle counts)."""
+    import numpy as np
+    import torch
+    import split_kv_amd as sk
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    st = torch.cuda.current_stream().cuda_stream
+
+    def run(launch):
+        launch()                                   # warm-up
+        torch.cuda.synchronize()
+        e0, e1 = _events()
+        e0.record()
+        launch()
+        e1.record()
+        torch.cuda.synchronize()
+        cyc = sink[:8 * cus].view(-1, 2)[:, 1].cpu().numpy().astype(np.uint32).astype(np.float64)
+        return e0.elapsed_time(e1) * 1e3, float(np.median(cyc))
+
+    iters = 20000
+    us, cyc = run(lambda: sk.splitkv_calib_mfma(cus, iters, sink.data_ptr(), st))
+    flops = cus * 4 * iters * 4 * 2 * 32 * 32 * 16
+    out = {"mfma_bf16_32x32x16": {"tflops": round(flops / us / 1e6, 1),
+                                  "cycles_per_product": round(cyc / (iters * 4), 2),
+                                  "clock_ghz": round(cyc / us / 1e3, 3), "us": round(us, 1)}}
+    lds = {}
+    for mode, name, per_read in ((0, "ds_read_b128", 1024), (1, "ds_read_b64_tr_b16", 512)):
+        it = 4000
+        us, cyc = run(lambda: sk.splitkv_calib_lds_read(cus, it, mode, sink.data_ptr(), st))
+        lds[name] = {"bytes_per_clock_per_cu": round(4 * it * 16 * per_read / cyc, 1), "us": round(us, 1)}
+    out["lds_read"] = lds
     return out
 
 

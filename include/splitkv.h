@@ -397,10 +397,32 @@ splitkv_status splitkv_e4m3_to_bf16(const uint8_t* in, uint16_t* out, int64_t n,
  * in flight per thread; workgroup w stores the XOR of what it read to sink[w]
  * (`sink` holds `workgroups` uint32 values).  Bad arguments give
  * SPLITKV_ERR_INVALID_ARG.
+ *
+ * The compute-bound kernels (MLA) are judged against what their two inner
+ * resources deliver on this GPU, measured the same way:
+ *
+ * splitkv_calib_mfma -- `workgroups` workgroups of four waves; every wave
+ * runs `iters` (1 .. 2^24) rounds of four independent
+ * v_mfma_f32_32x32x16_bf16 chains on register operands (131,072 FLOPs a
+ * round).  Wave w of workgroup g writes sink[2 (4 g + w)] (a checksum of its
+ * results) and sink[2 (4 g + w) + 1] (the core-clock cycles of its loop, from
+ * s_memtime); `sink` holds 8 * workgroups uint32 values.
+ *
+ * splitkv_calib_lds_read -- `workgroups` workgroups of four waves, each
+ * filling 64 KiB of LDS; every wave then runs `iters` (1 .. 2^24) rounds of
+ * sixteen conflict-free reads of 1 KiB a wave -- `mode` 0: ds_read_b128 (16
+ * bytes a lane), 1: ds_read_b64_tr_b16 (8 bytes a lane, 512 bytes a wave).
+ * sink as for splitkv_calib_mfma (a checksum, then the read loop's cycles).
+ *
+ * Both give SPLITKV_ERR_INVALID_ARG for a null or misaligned sink or counts
+ * out of range; the caller owns `sink` (device memory).
  */
 splitkv_status splitkv_calib_empty(void* stream);
 splitkv_status splitkv_calib_stream_read(const void* src, size_t bytes, int32_t workgroups, uint32_t* sink,
                                          void* stream);
+splitkv_status splitkv_calib_mfma(int32_t workgroups, int32_t iters, uint32_t* sink, void* stream);
+splitkv_status splitkv_calib_lds_read(int32_t workgroups, int32_t iters, int32_t mode, uint32_t* sink,
+                                      void* stream);
 
 const char* splitkv_last_error(void);   /* thread-local message of the last failure */
 const char* splitkv_version(void);      /* source revision the library was built from */

@@ -133,6 +133,8 @@ def load():
             "splitkv_append_args_size": (c_sz, []),
             "splitkv_calib_empty": (c_i32, [c_vp]),
             "splitkv_calib_stream_read": (c_i32, [c_vp, c_sz, c_i32, c_vp, c_vp]),
+            "splitkv_calib_mfma": (c_i32, [c_i32, c_i32, c_vp, c_vp]),
+            "splitkv_calib_lds_read": (c_i32, [c_i32, c_i32, c_i32, c_vp, c_vp]),
             "splitkv_last_error": (ctypes.c_char_p, []),
             "splitkv_version": (ctypes.c_char_p, []),
             "splitkv_args_size": (c_sz, []),
@@ -156,7 +158,7 @@ EXPORTED = ("splitkv_plan", "splitkv_split_range", "splitkv_workspace_bytes",
             "splitkv_validate_block_table",
             "splitkv_e4m3_to_bf16", "splitkv_append_kv", "splitkv_last_error", "splitkv_version",
             "splitkv_args_size", "splitkv_plan_args_size", "splitkv_append_args_size",
-            "splitkv_calib_empty", "splitkv_calib_stream_read")
+            "splitkv_calib_empty", "splitkv_calib_stream_read", "splitkv_calib_mfma", "splitkv_calib_lds_read")
 
 
 def _check(fn, status):
@@ -256,3 +258,11 @@ def splitkv_calib_empty(stream: int = 0):
 
 def splitkv_calib_stream_read(src: int, nbytes: int, workgroups: int, sink: int, stream: int = 0):
     _check("splitkv_calib_stream_read", load().splitkv_calib_stream_read(src, nbytes, workgroups, sink, stream))
+
+
+def splitkv_calib_mfma(workgroups: int, iters: int, sink: int, stream: int = 0):
+    _check("splitkv_calib_mfma", load().splitkv_calib_mfma(workgroups, iters, sink, stream))
+
+
+def splitkv_calib_lds_read(workgroups: int, iters: int, mode: int, sink: int, stream: int = 0):
+    _check("splitkv_calib_lds_read", load().splitkv_calib_lds_read(workgroups, iters, mode, sink, stream))

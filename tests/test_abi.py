@@ -294,3 +294,16 @@ def test_noalloc_refuses_an_oversized_plan_without_a_device():
     st = lib.splitkv_decode_noalloc(ctypes.byref(a), sk.SPLITKV_KERNEL_MLA, None)
     assert st == sk.SPLITKV_ERR_WORKSPACE
     assert "library buffer" in sk.splitkv_last_error()
+
+
+def test_calibration_argument_errors_without_device():
+    # the probes check their arguments before touching a device
+    lib = sk.load()
+    ok_sink = ctypes.c_void_p(256)
+    assert lib.splitkv_calib_mfma(1, 1, None, None) == sk.SPLITKV_ERR_INVALID_ARG
+    assert lib.splitkv_calib_mfma(0, 1, ok_sink, None) == sk.SPLITKV_ERR_INVALID_ARG
+    assert lib.splitkv_calib_mfma(1, 0, ok_sink, None) == sk.SPLITKV_ERR_INVALID_ARG
+    assert lib.splitkv_calib_mfma(1, 1, ctypes.c_void_p(258), None) == sk.SPLITKV_ERR_INVALID_ARG
+    assert lib.splitkv_calib_lds_read(1, 1, 2, ok_sink, None) == sk.SPLITKV_ERR_INVALID_ARG
+    assert lib.splitkv_calib_lds_read(1, (1 << 24) + 1, 0, ok_sink, None) == sk.SPLITKV_ERR_INVALID_ARG
+    assert "splitkv_calib_lds_read" in sk.splitkv_last_error()
