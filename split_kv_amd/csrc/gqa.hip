@@ -98,12 +98,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t group_rsrc(const uint8_t* base
 
 // 8 consecutive V features of one token: 4 dwords of bf16 pairs (bf16 cache)
 // or 2 dwords of e4m3 codes (FP8 cache, widened later).
-template <bool FP8>
+// Cache policy of the K/V loads: 0, or 2 (non-temporal, `nt`) for launches
+// with a workgroup per compute unit or more.
+template <bool FP8, int AUX>
 __device__ __forceinline__ u32x4 load_v8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   if constexpr (!FP8) {
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX));
   } else {
-    const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+    const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, AUX));
     u32x4 v = {w.x, w.y, 0u, 0u};
     return v;
   }
@@ -150,7 +152,7 @@ struct GroupRegs {
 
 // Launch geometry packed into one preloaded dword: Hkv (bits 0-15), row
 // blocks (16-23), log2(page size) + 1 (24-31; 0 when not a power of two).
-template <int D, bool FP8, bool FUSED>
+template <int D, bool FP8, bool FUSED, bool NT>
 __global__ __launch_bounds__(256) void gqa_partial_kernel(
     const int32_t* bt, const int32_t* slot_info, const uint16_t* q, const uint8_t* kc,
     const uint8_t* vc, int32_t bt_stride, int32_t geom, GqaRest a) {
@@ -240,6 +242,11 @@ __global__ __launch_bounds__(256) void gqa_partial_kernel(
   for (int jt = 0; jt < 4; ++jt) voff[jt] = uint32_t((4 * qg + jt) * a.vst) + uint32_t(ELEM * 8 * vl);
 
   // Group j of this wave (j < ngw loads; later j only keep the counts static).
+  // Non-temporal loads (NT) stream faster once the grid fills the chip (a
+  // 1 GiB read: 6.7-6.8 against 5.8-6.0 TB/s) but slow a partly filled one
+  // (few-KV L=5900, 124 workgroups: 6.8 -> 7.2 us), so the host picks them
+  // by the grid size.
+  constexpr int kAux = NT ? 2 : 0;
   auto load = [&](int j, int64_t pg, GroupRegs<D, FP8>& r) {
     const bool valid = j < ngw;
     const int tok = s + 16 * (wave + 4 * j);
@@ -249,17 +256,17 @@ __global__ __launch_bounds__(256) void gqa_partial_kernel(
     if constexpr (!FP8) {
 #pragma unroll
       for (int it = 0; it < NIT; ++it)
-        r.k[it] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, koff + 64 * it, 0, 0));
+        r.k[it] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, koff + 64 * it, 0, kAux));
     } else {
 #pragma unroll
       for (int kk = 0; kk < D / 64; ++kk)
-        r.k[2 * kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, koff + 64 * kk, 0, 0));
+        r.k[2 * kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, koff + 64 * kk, 0, kAux));
     }
 #pragma unroll
     for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
       for (int c = 0; c < NC; ++c)
-        r.v[c][jt] = load_v8<FP8>(rv, voff[jt] + ELEM * 128 * c);
+        r.v[c][jt] = load_v8<FP8, kAux>(rv, voff[jt] + ELEM * 128 * c);
   };
 
   auto compute = [&](int j, GroupRegs<D, FP8>& r) {
@@ -573,6 +580,20 @@ __global__ __launch_bounds__(256) void gqa_partial_kernel(
   }
 }
 
+// Compute units of the current device, queried once per device.
+static int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1 << 30;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+      return 1 << 30;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 // Host launcher: grid = slots x KV heads x row blocks, 256 threads.
 hipError_t launch_gqa_partial(const PartialParams& p, int D, bool fp8, bool fused, hipStream_t stream) {
   GqaRest a;
@@ -606,15 +627,24 @@ hipError_t launch_gqa_partial(const PartialParams& p, int D, bool fp8, bool fuse
   const int32_t geom = (p.Hkv & 0xffff) | ((p.row_blocks & 0xff) << 16) | ((p.page_shift + 1) << 24);
   const int32_t bt_stride = int32_t(p.bt_stride);
   const dim3 grid(p.total_wg), block(256);
-#define SPLITKV_LAUNCH(DD, F8, FU)                                                                       \
-  hipLaunchKernelGGL((gqa_partial_kernel<DD, F8, FU>), grid, block, 0, stream, p.bt, p.slot_info, p.q, \
+  // non-temporal K/V loads for a grid with a workgroup per compute unit or
+  // more (the single launch runs only small grids)
+  const bool nt = !fused && p.total_wg >= device_cus();
+#define SPLITKV_LAUNCH(DD, F8, FU, NTV)                                                                       \
+  hipLaunchKernelGGL((gqa_partial_kernel<DD, F8, FU, NTV>), grid, block, 0, stream, p.bt, p.slot_info, p.q, \
                      p.k, p.v, bt_stride, geom, a)
-#define SPLITKV_LAUNCH_D(DD)                      \
-  do {                                            \
-    if (!fp8 && !fused) SPLITKV_LAUNCH(DD, false, false); \
-    else if (fp8 && !fused) SPLITKV_LAUNCH(DD, true, false); \
-    else if (!fp8) SPLITKV_LAUNCH(DD, false, true); \
-    else SPLITKV_LAUNCH(DD, true, true);          \
+#define SPLITKV_LAUNCH_D(DD)                                       \
+  do {                                                             \
+    if (fused) {                                                   \
+      if (fp8) SPLITKV_LAUNCH(DD, true, true, false);              \
+      else SPLITKV_LAUNCH(DD, false, true, false);                 \
+    } else if (nt) {                                               \
+      if (fp8) SPLITKV_LAUNCH(DD, true, false, true);              \
+      else SPLITKV_LAUNCH(DD, false, false, true);                 \
+    } else {                                                       \
+      if (fp8) SPLITKV_LAUNCH(DD, true, false, false);             \
+      else SPLITKV_LAUNCH(DD, false, false, false);                \
+    }                                                              \
   } while (0)
   if (D == 64) SPLITKV_LAUNCH_D(64);
   else if (D == 128) SPLITKV_LAUNCH_D(128);

@@ -28,13 +28,17 @@ def _need_gpu():
 
 
 # The oracle's output for the full-size cases, computed once per case (the
-# tests of one case at several split counts share it).
+# tests of one full-size case at several split counts share it; only those
+# tests use the cache, and their cases are built unmodified from the
+# generators).
 _ORACLE = {}
 
 
-def _oracle_attend(case):
-    key = (case.name, case.seed, case.T, case.Hq, case.Hkv, case.kv_dtype, case.q_scale,
-           tuple(int(x) for x in case.seq_lens))
+def _oracle_attend(case, cache):
+    if not cache:
+        return oracle.attend(case)
+    key = (case.name, case.seed, case.B, case.T, case.Hq, case.Hkv, case.d_qk, case.d_v, case.page_size,
+           case.kv_dtype, case.q_scale, case.k_scale, case.v_scale, tuple(int(x) for x in case.seq_lens))
     if key not in _ORACLE:
         if len(_ORACLE) > 4:
             _ORACLE.clear()
@@ -42,10 +46,10 @@ def _oracle_attend(case):
     return _ORACLE[key]
 
 
-def _check_full(case, sess, tag):
+def _check_full(case, sess, tag, cache=False):
     import torch
     torch.cuda.synchronize()
-    O, L = _oracle_attend(case)
+    O, L = _oracle_attend(case, cache)
     atol, rtol = tolerances(case)
     e1 = assert_close(to_np(sess.out), O, atol, rtol, f"{tag} out")
     e2 = assert_close(to_np(sess.lse), L, ATOL_LSE, 0.0, f"{tag} lse")
@@ -425,7 +429,7 @@ def test_fp8_full_size():
     sess, _ = session_for(case, requested_splits=0)
     log(f"  plan: splits {sess.num_splits_host.tolist()}")
     sess.decode()
-    _check_full(case, sess, "fp8 full")
+    _check_full(case, sess, "fp8 full", cache=True)
 
 
 @pytest.mark.parametrize("n", [1, 4, 8, 0])
@@ -435,7 +439,7 @@ def test_mla_full_size(n):
     log(f"mla full L=65536 n={n}, every row")
     sess, _ = session_for(case, requested_splits=n, max_splits=256)
     sess.decode()
-    _check_full(case, sess, f"mla full n={n}")
+    _check_full(case, sess, f"mla full n={n}", cache=True)
 
 
 def test_ragged_full_size():
@@ -446,7 +450,7 @@ def test_ragged_full_size():
     log(f"  plan total slots {sess.total_slots}")
     sess.decode()
     _check_debug(case, sess, case.Hkv, 1)
-    _check_full(case, sess, "ragged full")
+    _check_full(case, sess, "ragged full", cache=True)
 
 
 # ---------------------------------------------------------------------------
@@ -583,7 +587,7 @@ def test_mla_fp8_full_size():
     log("mla e4m3 L=65536 auto plan, every row")
     sess, _ = session_for(case, requested_splits=0, max_splits=256)
     sess.decode()
-    _check_full(case, sess, "mla e4m3 L=65536")
+    _check_full(case, sess, "mla e4m3 L=65536", cache=True)
 
 
 # ---------------------------------------------------------------------------
@@ -783,7 +787,7 @@ def test_mla_fp8q_full_size():
     log("mla e4m3 queries L=65536 auto plan, every row")
     sess, _ = session_for(case, requested_splits=0, max_splits=256)
     sess.decode()
-    _check_full(case, sess, "mla fp8q L=65536")
+    _check_full(case, sess, "mla fp8q L=65536", cache=True)
 
 
 # ---------------------------------------------------------------------------
