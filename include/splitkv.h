@@ -394,7 +394,9 @@ splitkv_status splitkv_e4m3_to_bf16(const uint8_t* in, uint16_t* out, int64_t n,
  * splitkv_calib_stream_read -- read `bytes` (a multiple of 16) of device
  * memory at `src` (16-byte aligned) with `workgroups` workgroups of 256
  * threads, each reading one contiguous share with 16-byte loads, thirty-two
- * in flight per thread; workgroup w stores the XOR of what it read to sink[w]
+ * in flight per thread (non-temporal loads when `workgroups` is at least the
+ * device's compute-unit count, as the grouped-query kernel chooses them);
+ * workgroup w stores the XOR of what it read to sink[w]
  * (`sink` holds `workgroups` uint32 values).  Bad arguments give
  * SPLITKV_ERR_INVALID_ARG.
  *

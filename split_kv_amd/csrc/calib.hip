@@ -16,10 +16,13 @@ __global__ void calib_empty_kernel() {}
 // Workgroup w reads 16-byte words [w * per_wg, min(n16, (w + 1) * per_wg)),
 // thirty-two loads in flight per thread (128 KiB per workgroup, as many bytes
 // as a grouped-query decode workgroup keeps in flight), and stores the XOR of
-// everything it read to sink[w] so that no load can be dropped.
+// everything it read to sink[w] so that no load can be dropped.  Like the
+// grouped-query kernel, a grid with a workgroup per compute unit or more
+// reads with non-temporal loads (NT), a smaller one with default ones.
 constexpr int kCalibThreads = 256;
 constexpr int kCalibUnroll = 32;
 
+template <bool NT>
 __global__ __launch_bounds__(kCalibThreads) void calib_stream_read_kernel(const u32x4* src, int64_t n16,
                                                                          int64_t per_wg, uint32_t* sink) {
   __shared__ uint32_t red[kCalibThreads / 64];
@@ -34,7 +37,10 @@ __global__ __launch_bounds__(kCalibThreads) void calib_stream_read_kernel(const 
 #pragma unroll
     for (int u = 0; u < kCalibUnroll; ++u) {
       const int64_t j = base + int64_t(u) * kCalibThreads;
-      v[u] = j < hi ? src[j] : zero;
+      if constexpr (NT)
+        v[u] = j < hi ? __builtin_nontemporal_load(src + j) : zero;
+      else
+        v[u] = j < hi ? src[j] : zero;
     }
 #pragma unroll
     for (int u = 0; u < kCalibUnroll; ++u) acc ^= v[u];
@@ -169,8 +175,16 @@ splitkv_status splitkv_calib_stream_read(const void* src, size_t bytes, int32_t 
     return fail(SPLITKV_ERR_INVALID_ARG, "%s: bad arguments (bytes %zu, workgroups %d)", fn, bytes, workgroups);
   const int64_t n16 = int64_t(bytes / 16);
   const int64_t per_wg = (n16 + workgroups - 1) / workgroups;
-  hipLaunchKernelGGL(calib_stream_read_kernel, dim3(unsigned(workgroups)), dim3(kCalibThreads), 0,
-                     static_cast<hipStream_t>(stream), static_cast<const u32x4*>(src), n16, per_wg, sink);
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return fail(SPLITKV_ERR_DEVICE, "%s: cannot query the compute-unit count", fn);
+  if (workgroups >= cus)
+    hipLaunchKernelGGL(calib_stream_read_kernel<true>, dim3(unsigned(workgroups)), dim3(kCalibThreads), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const u32x4*>(src), n16, per_wg, sink);
+  else
+    hipLaunchKernelGGL(calib_stream_read_kernel<false>, dim3(unsigned(workgroups)), dim3(kCalibThreads), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const u32x4*>(src), n16, per_wg, sink);
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return fail(SPLITKV_ERR_LAUNCH, "%s: %s", fn, hipGetErrorString(err));
   return SPLITKV_OK;
