@@ -250,8 +250,8 @@ splitkv_status splitkv_decode_partial_fp8(const splitkv_args* args, void* stream
 /*
  * splitkv_mla_decode_partial -- MLA partial kernel: one latent KV head
  * (Hkv == 1) of width d_qk == 576 serves as key, its first d_v == 512
- * columns as value; one workgroup per (slot, block of 64 query rows in
- * (t, h) order).  Causal within the T query tokens ("Shipped: 484.5 tok/s on
+ * columns as value; one workgroup per (slot, block of 128 query rows in
+ * (t, h) order, SPLITKV_ROWS_PER_WG_MLA).  Causal within the T query tokens ("Shipped: 484.5 tok/s on
  * one GB300 ...", table "What shipped": split-KV MLA decode of one request
  * at six tokens).  The latent cache is bf16 or e4m3 (kv_dtype); e4m3 codes
  * widen exactly to bf16 and k_scale / v_scale (the same value for a latent
@@ -261,13 +261,12 @@ splitkv_status splitkv_decode_partial_fp8(const splitkv_args* args, void* stream
  *
  * With q_dtype == SPLITKV_Q_E4M3 (e4m3 cache only) the queries go FP8 as well
  * ("Xqa decode kernels", timeline: FP8-Q, used only where the cache is FP8):
- * each bf16 query value is quantised to the e4m3 code of q / q_scale (fp32
- * division, saturated to +-448, nearest code, ties to even -- the encoding of
- * splitkv_append_kv) and the scores and P V run on the FP8 matrix path with
- * each softmax weight entered as two e4m3 terms (hi + lo, within 2^-8 of
- * the weight plus 2^-10; the weight sum adds the weights themselves).  The
- * result approximates attention over the dequantised queries, keys and
- * values.  q_scale must be positive and finite.
+ * each bf16 query value is quantised to the e4m3 code of q / q_scale (the
+ * correctly rounded fp32 quotient, saturated to +-448, nearest code, ties to
+ * even -- the encoding of splitkv_append_kv) and the scores run on the FP8
+ * matrix path over the codes; P V runs on bf16 operands as in the other
+ * modes.  The result approximates attention over the dequantised queries,
+ * keys and values.  q_scale must be positive and finite.
  */
 splitkv_status splitkv_mla_decode_partial(const splitkv_args* args, void* stream);
 
