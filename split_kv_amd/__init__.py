@@ -76,6 +76,7 @@ class splitkv_args(ctypes.Structure):
         ("uniform_splits", c_i32),
         ("q_dtype", c_i32), ("q_scale", c_f32),
         ("max_seq_splits", c_i32),
+        ("max_range_tokens", c_i32),
         ("tickets", c_vp),
     ]
 

@@ -46,15 +46,18 @@ def sources():
                   if f.endswith(".hip") or f.endswith(".cpp"))
 
 
-# Per-source code-generation options.  The grouped-query kernel rescales its
-# MFMA accumulators with vector ALU code; keeping them in VGPRs (instead of the
-# accumulation registers) avoids copying them across on every group.  The
+# Per-source code-generation options.  The grouped-query and short-range MLA
+# kernels rescale their MFMA accumulators with vector ALU code; keeping them
+# in VGPRs (instead of the accumulation registers) avoids copying them across
+# on every group or tile.  The
 # grouped-query and combine kernels take their first fourteen argument dwords
 # preloaded into scalar registers at wave launch, so their first memory access
 # does not wait for an argument load.
 PER_FILE = {
     "gqa.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true", "-mllvm", "-amdgpu-kernarg-preload-count=14"],
     "combine.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=14"],
+    "mla_short.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
+    "mla_short_q8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
 }
 
 

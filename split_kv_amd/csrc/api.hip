@@ -2,6 +2,7 @@
 // dispatch to the kernels.  Every entry point returns a status and records a
 // message instead of asserting; the library allocates nothing.
 #include <algorithm>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 
@@ -16,6 +17,8 @@ namespace splitkv {
 
 hipError_t launch_gqa_partial(const PartialParams& p, int D, bool fp8, bool fused, hipStream_t stream);
 hipError_t launch_mla_partial(const PartialParams& p, int kind, hipStream_t stream);
+hipError_t launch_mla_short_partial(const PartialParams& p, bool fp8, hipStream_t stream);
+hipError_t launch_mla_short_q8_partial(const PartialParams& p, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
 hipError_t launch_e4m3_to_bf16(const uint8_t* in, uint16_t* out, int64_t n, hipStream_t stream);
 
@@ -245,6 +248,33 @@ PartialParams make_partial_params(const splitkv_args& a, Kind kind, int row_bloc
   return p;
 }
 
+// Compute units of the current device, queried once per device (0 if unknown).
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+// The MLA kernel of a step: the short-range one (64 rows, eight waves a
+// workgroup) when the caller says every split range is at most eight 32-token
+// tiles and its 64-row workgroups all fit on the compute units at once; the
+// 128-row one otherwise.  SPLITKV_MLA_KERNEL=short or =long in the
+// environment forces either (for tests and measurements).
+bool use_short_mla(const splitkv_args& a) {
+  if (const char* env = getenv("SPLITKV_MLA_KERNEL")) {
+    if (!strcmp(env, "short")) return true;
+    if (!strcmp(env, "long")) return false;
+  }
+  const int64_t wgs = int64_t(a.total_slots) * ceil_div(int64_t(a.T) * a.Hq, int64_t(64));
+  return a.max_range_tokens > 0 && a.max_range_tokens <= 8 * 32 && wgs <= device_cus();
+}
+
 splitkv_status run_partial(const splitkv_args* a, Kind kind, bool direct, void* stream,
                            const char* fn, bool fused = false) {
   int row_blocks = 0;
@@ -261,8 +291,15 @@ splitkv_status run_partial(const splitkv_args* a, Kind kind, bool direct, void* 
   hipError_t err;
   if (kind != Kind::Mla)
     err = launch_gqa_partial(p, a->d_qk, kind == Kind::GqaFp8, fused, s);
-  else
+  else if (!use_short_mla(*a))
     err = launch_mla_partial(p, a->q_dtype == SPLITKV_Q_E4M3 ? 2 : a->kv_dtype == SPLITKV_KV_E4M3 ? 1 : 0, s);
+  else {
+    // the same plan in 64-row blocks (two to a plan row block)
+    const PartialParams ps =
+        make_partial_params(*a, kind, int(ceil_div(int64_t(a->T) * a->Hq, int64_t(64))), direct);
+    err = a->q_dtype == SPLITKV_Q_E4M3 ? launch_mla_short_q8_partial(ps, s)
+                                       : launch_mla_short_partial(ps, a->kv_dtype == SPLITKV_KV_E4M3, s);
+  }
   if (err != hipSuccess) return fail(SPLITKV_ERR_LAUNCH, "%s: launch failed: %s", fn, hipGetErrorString(err));
   return SPLITKV_OK;
 }

@@ -145,6 +145,8 @@ class DecodeSession:
         ns = self.num_splits_host
         a.uniform_splits = int(ns[0]) if len(ns) and (ns == ns[0]).all() else 0
         a.max_seq_splits = int(ns.max()) if len(ns) else 0
+        info = self.slot_info_host
+        a.max_range_tokens = max(1, int((info[:, 3] - info[:, 2]).max())) if len(info) else 0
         a.tickets = self.tickets.data_ptr() if self.tickets is not None else None
         self.args = a
 
