@@ -297,8 +297,14 @@ def monotonic(sweep, band=1.03):
             "worst_request": worst["num_splits_requested"]}
 
 
-def partial_kernel_name(case):
+def partial_kernel_name(case, sess=None):
     if case.mla:
+        import split_kv_amd as sk
+        if sess is not None and sk.splitkv_mla_short_range(sess.args):
+            # the short-range kernels (64 rows, eight waves a workgroup)
+            if case.q_scale:
+                return "mla_short_q8_partial_kernel"
+            return "mla_short_partial_kernel<%s>" % ("true" if case.kv_dtype == "e4m3" else "false")
         # kinds: 0 bf16 cache, 1 e4m3 cache with bf16 queries, 2 e4m3 cache and queries
         return "mla_partial_kernel<%d>" % (2 if case.q_scale else (1 if case.kv_dtype == "e4m3" else 0))
     return "gqa_partial_kernel<%d,%s>" % (case.d_qk, "e4m3" if case.kv_dtype == "e4m3" else "bf16")
@@ -307,13 +313,14 @@ def partial_kernel_name(case):
 def partial_grid(case, sess):
     """Workgroups of one partial-kernel launch."""
     if case.mla:
-        import split_kv_amd
+        import split_kv_amd as sk
         rows = case.T * case.Hq
-        return sess.total_slots * -(-rows // split_kv_amd.SPLITKV_ROWS_PER_WG_MLA)
+        rpw = 64 if sk.splitkv_mla_short_range(sess.args) else sk.SPLITKV_ROWS_PER_WG_MLA
+        return sess.total_slots * -(-rows // rpw)
     return sess.total_slots * case.Hkv * -(-(case.g * case.T) // 16)
 
 
-def roofline(case, part_us):
+def roofline(case, part_us, kernel=None):
     if case.mla:
         tokens = int(case.seq_lens.sum())
         flops_qk = 2 * case.T * case.Hq * case.d_qk * tokens
@@ -326,13 +333,13 @@ def roofline(case, part_us):
             peak = round(flops / (flops_qk / MFMA_FP8_PEAK_TFLOPS + flops_pv / MFMA_BF16_PEAK_TFLOPS), 1)
         else:
             peak = MFMA_BF16_PEAK_TFLOPS
-        return {"bound": "mfma", "kernel": partial_kernel_name(case),
+        return {"bound": "mfma", "kernel": kernel or partial_kernel_name(case),
                 "achieved": round(flops / part_us / 1e6, 1), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(flops / part_us / 1e6 / peak, 4),
                 "traffic": None, "kernel_us": round(part_us, 3), "flops_per_launch": flops}
     kv = case.kv_bytes()
     achieved = kv / part_us / 1e3
-    return {"bound": "hbm", "kernel": partial_kernel_name(case), "achieved": round(achieved, 1),
+    return {"bound": "hbm", "kernel": kernel or partial_kernel_name(case), "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": None, "kernel_us": round(part_us, 3), "bytes_per_launch": kv}
 
@@ -382,6 +389,7 @@ def measure(case, pool, counts, steps, stream, eager=True, log_prefix=""):
             head = dict(rec, plan_host_us=round(plan_us, 1), partial_kernel_us=round(part_us, 3),
                         partial_batches_us=[round(x, 3) for x in part_batches],
                         partial_workgroups=partial_grid(case, sess),
+                        partial_kernel=partial_kernel_name(case, sess),
                         num_splits_host=sess.num_splits_host.copy())
             if not case.mla:
                 # the whole step as one launch (ticketed last-arriver merge), for comparison;
@@ -537,7 +545,7 @@ def extra_record(name, L, counts, steps, stream, dev):
     case = make_workload(name, L)
     pool = Pool(case, dev, False)
     sweep, head = measure(case, pool, counts, steps, stream, eager=False, log_prefix=f"{name} L={L} ")
-    roof = roofline(case, head["partial_kernel_us"])
+    roof = roofline(case, head["partial_kernel_us"], head.get("partial_kernel"))
     rec = {"workload": describe(case, name),
            "kv_bytes_per_step": case.kv_bytes(),
            "cold_copies": pool.R,
@@ -693,7 +701,7 @@ def main():
     sweep, head = measure(case, pool, counts, args.steps, stream)
 
     us = head["us_per_step"]
-    roof = roofline(case, head["partial_kernel_us"])
+    roof = roofline(case, head["partial_kernel_us"], head.get("partial_kernel"))
     if headline and head["num_splits_requested"] == 0 and not args.warm_cache:
         traffic, detail = measured_traffic()
         roof["traffic"] = traffic

@@ -275,6 +275,17 @@ splitkv_status splitkv_decode_partial_fp8(const splitkv_args* args, void* stream
 splitkv_status splitkv_mla_decode_partial(const splitkv_args* args, void* stream);
 
 /*
+ * splitkv_mla_short_range -- 1 if an MLA step with these arguments runs the
+ * short-range partial kernel (64 query rows and eight waves a workgroup:
+ * chosen when args->max_range_tokens is 1 .. 256 and the plan's 64-row
+ * workgroups, total_slots * ceil(T*Hq / 64), fit on the device's compute
+ * units at once, or forced by SPLITKV_MLA_KERNEL=short in the environment),
+ * 0 if it runs the 128-row kernel (also for a null args).  Host only; the
+ * device is the current one.
+ */
+int32_t splitkv_mla_short_range(const splitkv_args* args);
+
+/*
  * splitkv_combine -- log-sum-exp merge of the partials of every sequence into
  * out and lse: M = max_i m_i, w_i = exp(m_i - M) (0 for an empty split),
  * out = sum_i w_i o_i / sum_i w_i l_i, lse = M + ln(sum_i w_i l_i); a row

@@ -135,6 +135,7 @@ def load():
             "splitkv_calib_empty": (c_i32, [c_vp]),
             "splitkv_calib_stream_read": (c_i32, [c_vp, c_sz, c_i32, c_vp, c_vp]),
             "splitkv_calib_mfma": (c_i32, [c_i32, c_i32, c_vp, c_vp]),
+            "splitkv_mla_short_range": (c_i32, [c_vp]),
             "splitkv_calib_lds_read": (c_i32, [c_i32, c_i32, c_i32, c_vp, c_vp]),
             "splitkv_last_error": (ctypes.c_char_p, []),
             "splitkv_version": (ctypes.c_char_p, []),
@@ -159,7 +160,8 @@ EXPORTED = ("splitkv_plan", "splitkv_split_range", "splitkv_workspace_bytes",
             "splitkv_validate_block_table",
             "splitkv_e4m3_to_bf16", "splitkv_append_kv", "splitkv_last_error", "splitkv_version",
             "splitkv_args_size", "splitkv_plan_args_size", "splitkv_append_args_size",
-            "splitkv_calib_empty", "splitkv_calib_stream_read", "splitkv_calib_mfma", "splitkv_calib_lds_read")
+            "splitkv_calib_empty", "splitkv_calib_stream_read", "splitkv_calib_mfma", "splitkv_calib_lds_read",
+            "splitkv_mla_short_range")
 
 
 def _check(fn, status):
@@ -217,6 +219,10 @@ def splitkv_decode_partial_fp8(args: splitkv_args, stream: int = 0):
 
 def splitkv_mla_decode_partial(args: splitkv_args, stream: int = 0):
     _check("splitkv_mla_decode_partial", load().splitkv_mla_decode_partial(ctypes.byref(args), stream))
+
+
+def splitkv_mla_short_range(args: splitkv_args) -> bool:
+    return bool(load().splitkv_mla_short_range(ctypes.byref(args)))
 
 
 def splitkv_combine(args: splitkv_args, stream: int = 0):

@@ -402,6 +402,10 @@ splitkv_status splitkv_decode_partial_fp8(const splitkv_args* args, void* stream
   return run_partial(args, Kind::GqaFp8, false, stream, "splitkv_decode_partial_fp8");
 }
 
+int32_t splitkv_mla_short_range(const splitkv_args* args) {
+  return args && use_short_mla(*args) ? 1 : 0;
+}
+
 splitkv_status splitkv_mla_decode_partial(const splitkv_args* args, void* stream) {
   return run_partial(args, Kind::Mla, false, stream, "splitkv_mla_decode_partial");
 }

@@ -307,3 +307,19 @@ def test_calibration_argument_errors_without_device():
     assert lib.splitkv_calib_lds_read(1, 1, 2, ok_sink, None) == sk.SPLITKV_ERR_INVALID_ARG
     assert lib.splitkv_calib_lds_read(1, (1 << 24) + 1, 0, ok_sink, None) == sk.SPLITKV_ERR_INVALID_ARG
     assert "splitkv_calib_lds_read" in sk.splitkv_last_error()
+
+
+def test_mla_kernel_choice_query(monkeypatch):
+    # no hint: the 128-row kernel; the environment switch forces either;
+    # a null args is the 128-row kernel too
+    lib = sk.load()
+    assert lib.splitkv_mla_short_range(None) == 0
+    a = sk.splitkv_args()
+    a.B, a.T, a.Hq, a.Hkv, a.total_slots, a.max_range_tokens = 1, 6, 128, 1, 18, 0
+    monkeypatch.delenv("SPLITKV_MLA_KERNEL", raising=False)
+    assert not sk.splitkv_mla_short_range(a)
+    monkeypatch.setenv("SPLITKV_MLA_KERNEL", "short")
+    assert sk.splitkv_mla_short_range(a)
+    monkeypatch.setenv("SPLITKV_MLA_KERNEL", "long")
+    a.max_range_tokens = 114
+    assert not sk.splitkv_mla_short_range(a)
