@@ -326,7 +326,10 @@ def roofline(case, part_us, kernel=None):
         flops_qk = 2 * case.T * case.Hq * case.d_qk * tokens
         flops_pv = 2 * case.T * case.Hq * case.d_v * tokens
         flops = flops_qk + flops_pv
-        if case.q_scale:
+        if case.q_scale and (kernel or "").startswith("mla_short_q8"):
+            # the short-range e4m3-query kernel runs both products on FP8
+            peak = MFMA_FP8_PEAK_TFLOPS
+        elif case.q_scale:
             # e4m3 queries put the scores on the FP8 matrix path and keep the
             # value product on bf16: the peak is the rate of that mix, each
             # part at its own dtype's peak
