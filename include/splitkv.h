@@ -224,7 +224,9 @@ typedef struct {
   int32_t max_range_tokens;        /* > 0: no split range of the plan holds more tokens (a hint:
                                       MLA steps whose ranges are all short and whose 64-row
                                       workgroups fit on the compute units at once run the
-                                      short-range kernel); 0: not given */
+                                      short-range kernel, which is correct for ranges of any
+                                      length, so a wrong hint is slower, never wrong); 0: not
+                                      given */
   int32_t* tickets;                /* splitkv_decode_single_launch only: int32 [B][Hkv][row_blocks]
                                       arrival counters (row_blocks = ceil(g*T / 16)), all zero
                                       before the first call; every completed call leaves them
