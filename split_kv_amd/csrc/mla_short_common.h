@@ -105,16 +105,15 @@ __device__ __forceinline__ void store_rows(const PartialParams& p, const f32x4 (
 #pragma unroll
     for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(o[e][i]));
   amax = column_max4(amax) * fabsf(mul);
-  const float k = amax > 0.f ? mul * (32767.f / amax) : 0.f;   // code = nearest integer to o * k
+  // o * kq lies in [-1, 1]; v_cvt_pknorm_i16_f32 takes two such values to
+  // the nearest multiples of 1/32767, as int16 codes
+  const float kq = amax > 0.f ? mul / amax : 0.f;
   int16_t* st = reinterpret_cast<int16_t*>(stage) + wave * 16 * kCodePitch;
   __syncthreads();                       // every wave is done with the tile pool
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
-    int c[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) c[i] = int(fminf(fmaxf(rintf(o[e][i] * k), -32767.f), 32767.f));
-    const u32x2 w = {(uint32_t(c[0]) & 0xffffu) | (uint32_t(c[1]) << 16),
-                     (uint32_t(c[2]) & 0xffffu) | (uint32_t(c[3]) << 16)};
+    const u32x2 w = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pknorm_i16(o[e][0] * kq, o[e][1] * kq)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pknorm_i16(o[e][2] * kq, o[e][3] * kq))};
     *reinterpret_cast<u32x2*>(st + n16 * kCodePitch + 16 * e + 4 * qg) = w;
   }
   u32x2 rc[16];
