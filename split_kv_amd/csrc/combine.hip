@@ -160,8 +160,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* part_m, const
 // 16-byte load per split (the wave reads a split's row of codes in one 1 KiB
 // load); a split's m, l and two scales are the same for the whole wave (one
 // address per load; as scalar loads they measured slower).  Up to U splits'
-// loads are in flight before any is merged; the four waves meet in LDS, and
-// wave 0 writes the row.
+// loads are in flight before any is merged (U up to 12: the 42 splits of a
+// long context in one pass, one memory trip); the four waves meet in LDS,
+// and wave 0 writes the row.
 template <int U>
 __device__ __forceinline__ void merge_code_splits(const float* part_m, const float* part_l, const float* part_s,
                                                   const int16_t* pq, int64_t R, int rix, int base, int n,
@@ -248,8 +249,10 @@ __global__ __launch_bounds__(256) void combine_codes_kernel(const float* part_m,
     merge_code_splits<2>(part_m, part_l, part_s, pq, R, rix, base, n, w, hf, M2, lam, acc);
   else if (per <= 4)
     merge_code_splits<4>(part_m, part_l, part_s, pq, R, rix, base, n, w, hf, M2, lam, acc);
-  else
+  else if (per <= 8)
     merge_code_splits<8>(part_m, part_l, part_s, pq, R, rix, base, n, w, hf, M2, lam, acc);
+  else
+    merge_code_splits<12>(part_m, part_l, part_s, pq, R, rix, base, n, w, hf, M2, lam, acc);
   if (w > 0) {
     if (lane == 0) {
       red_ml[w][0] = M2;
