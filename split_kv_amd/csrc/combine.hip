@@ -159,8 +159,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* part_m, const
 // w + 8, ...; lane j keeps features 8 j .. 8 j + 7, whose codes are one
 // 16-byte load per split (the wave reads a split's row of codes in one 1 KiB
 // load); a split's m, l and two scales are the same for the whole wave (one
-// address per load; as scalar loads they measured slower).  Up to U splits'
-// loads are in flight before any is merged (U up to 12: the 42 splits of a
+// address per load; as scalar loads they measured slower).  U splits' loads
+// per wave are in flight before any is merged, U the fewest of 1, 2, 4, 6, 8
+// and 12 that hold the wave's share of the row's splits (the 42 splits of a
 // long context in one pass, one memory trip); the four waves meet in LDS,
 // and wave 0 writes the row.
 template <int U>
@@ -249,6 +250,8 @@ __global__ __launch_bounds__(256) void combine_codes_kernel(const float* part_m,
     merge_code_splits<2>(part_m, part_l, part_s, pq, R, rix, base, n, w, hf, M2, lam, acc);
   else if (per <= 4)
     merge_code_splits<4>(part_m, part_l, part_s, pq, R, rix, base, n, w, hf, M2, lam, acc);
+  else if (per <= 6)
+    merge_code_splits<6>(part_m, part_l, part_s, pq, R, rix, base, n, w, hf, M2, lam, acc);
   else if (per <= 8)
     merge_code_splits<8>(part_m, part_l, part_s, pq, R, rix, base, n, w, hf, M2, lam, acc);
   else

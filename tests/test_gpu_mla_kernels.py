@@ -32,7 +32,7 @@ def kernel(request, monkeypatch):
 
 
 @pytest.mark.parametrize("kind", list(KINDS))
-@pytest.mark.parametrize("L,n", [(2048, 16), (2000, 3), (21, 2), (700, 0)])
+@pytest.mark.parametrize("L,n", [(2048, 16), (2048, 0), (2000, 3), (21, 2), (700, 0)])
 def test_mla_kernels_agree_with_oracle(kernel, kind, L, n):
     _need_gpu()
     case = synth.mla_decode(L=L, seed=97 + L, **KINDS[kind])
