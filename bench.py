@@ -347,6 +347,9 @@ def roofline(case, part_us, kernel=None):
             "traffic": None, "kernel_us": round(part_us, 3), "bytes_per_launch": kv}
 
 
+KERNEL_LAUNCHES = 100
+
+
 def measure(case, pool, counts, steps, stream, eager=True, log_prefix=""):
     """Sweep the split counts: us/step from graph replays (median of BATCHES),
     plus the partial kernel alone at the first count.  Returns (sweep, head)."""
@@ -388,9 +391,13 @@ def measure(case, pool, counts, steps, stream, eager=True, log_prefix=""):
         if eager_us is not None:
             rec["eager_us_per_step"] = round(eager_us, 3)
         if n == counts[0]:
-            part_us, part_batches = timed_graphs(sess, pool, sess.partial, steps, stream)
+            # the kernel alone: graphs of at least KERNEL_LAUNCHES launches, so that a
+            # graph's own launch cost is a small share of each launch at any --steps
+            part_n = max(steps, KERNEL_LAUNCHES)
+            part_us, part_batches = timed_graphs(sess, pool, sess.partial, part_n, stream)
             head = dict(rec, plan_host_us=round(plan_us, 1), partial_kernel_us=round(part_us, 3),
                         partial_batches_us=[round(x, 3) for x in part_batches],
+                        partial_launches_per_graph=part_n,
                         partial_workgroups=partial_grid(case, sess),
                         partial_kernel=partial_kernel_name(case, sess),
                         num_splits_host=sess.num_splits_host.copy())
